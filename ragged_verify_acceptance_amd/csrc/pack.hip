@@ -1,0 +1,135 @@
+// Stage 2: ragged packing of the scheduled verify rows and tier rounding.
+//
+// Source: "DFlash 到 DSpark in SGLang：解码提速 4.3×，以及 DeepSeek-V4 支持"
+// (yichizhang.dev, AI-Infra-Visualized), section "Ragged verify under full CUDA graphs":
+// the scheduled tokens of all requests sit back to back in one [total_tokens, hidden]
+// buffer with cu_seqlens offsets, and the total is rounded up to the nearest captured
+// tier so that a smaller graph is replayed when the budget shrinks.
+//
+// One launch, destination-row oriented: every workgroup rebuilds cu_seqlens for the whole
+// batch in LDS (a 256-lane scan of at most a few hundred ints, cheaper than a second
+// launch), picks the tier, and then handles kRowsPerBlock destination rows: a binary
+// search in LDS finds the owning request, the row is copied with 16-byte vector accesses
+// when alignment allows, rows [M, tier) are zero-filled.  Workgroup 0 publishes
+// cu_seqlens and {M, tier}.
+#include "rva_common.h"
+
+namespace rva {
+namespace {
+
+constexpr int kPackThreads = 256;
+constexpr int kRowsPerBlock = 4;
+constexpr int kMaxPackB = 4096;
+
+__global__ __launch_bounds__(kPackThreads) void pack_kernel(
+    int B, int gamma, const int32_t* __restrict__ windows,
+    const int32_t* __restrict__ context_lens, TierTable tiers, const uint8_t* __restrict__ src,
+    size_t row_bytes, uint8_t* __restrict__ dst, int max_rows, int32_t* __restrict__ cu_out,
+    int32_t* __restrict__ row_req, int32_t* __restrict__ row_pos,
+    int32_t* __restrict__ total_tier, int32_t* status) {
+  __shared__ int cu[kMaxPackB + 1];
+  __shared__ int part[kPackThreads];
+  __shared__ int s_M, s_tier;
+  const int tid = threadIdx.x;
+
+  // per-thread run of consecutive requests, then a scan over the 256 run totals
+  const int per = (B + kPackThreads - 1) / kPackThreads;
+  const int b0 = tid * per;
+  int run = 0;
+  for (int i = 0; i < per; ++i) {
+    const int b = b0 + i;
+    if (b < B) {
+      int w = windows[b];
+      if (w < 1 || w > gamma) {
+        if (blockIdx.x == 0) flag(status, RVA_DEV_BAD_WINDOW);
+        w = w < 1 ? 1 : gamma;
+      }
+      run += w;
+      cu[b + 1] = w;  // temporarily the window
+    }
+  }
+  part[tid] = run;
+  __syncthreads();
+  for (int o = 1; o < kPackThreads; o <<= 1) {
+    const int v = tid >= o ? part[tid - o] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int acc = tid > 0 ? part[tid - 1] : 0;
+  for (int i = 0; i < per; ++i) {
+    const int b = b0 + i;
+    if (b < B) {
+      acc += cu[b + 1];
+      cu[b + 1] = acc;
+    }
+  }
+  if (tid == 0) {
+    cu[0] = 0;
+    const int M = part[kPackThreads - 1];
+    int tier = tiers.t[tiers.n - 1];
+    for (int t = 0; t < tiers.n; ++t)
+      if (tiers.t[t] >= M) {
+        tier = tiers.t[t];
+        break;
+      }
+    s_M = M;
+    s_tier = tier;
+  }
+  __syncthreads();
+  const int M = s_M, tier = s_tier;
+  if (blockIdx.x == 0) {
+    for (int b = tid; b <= B; b += kPackThreads) cu_out[b] = cu[b];
+    if (tid == 0) {
+      total_tier[0] = M;
+      total_tier[1] = tier;
+    }
+  }
+
+  for (int rr = 0; rr < kRowsPerBlock; ++rr) {
+    const int r = blockIdx.x * kRowsPerBlock + rr;
+    if (r >= max_rows) break;
+    int b = -1, i = 0;
+    if (r < M) {
+      int lo = 0, hi = B - 1;  // largest b with cu[b] <= r
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (cu[mid] <= r) lo = mid; else hi = mid - 1;
+      }
+      b = lo;
+      i = r - cu[b];
+    }
+    if (tid == 0) {
+      row_req[r] = b;
+      row_pos[r] = b >= 0 ? context_lens[b] + i : -1;
+    }
+    if (!src || r >= tier) continue;
+    uint8_t* d = dst + size_t(r) * row_bytes;
+    const uint8_t* s = b >= 0 ? src + (size_t(b) * gamma + i) * row_bytes : nullptr;
+    const bool vec16 = (row_bytes % 16 == 0) && ((reinterpret_cast<uintptr_t>(src) |
+                                                  reinterpret_cast<uintptr_t>(dst)) % 16 == 0);
+    if (vec16) {
+      const size_t n = row_bytes / 16;
+      for (size_t k = tid; k < n; k += kPackThreads)
+        reinterpret_cast<uint4*>(d)[k] = s ? reinterpret_cast<const uint4*>(s)[k] : make_uint4(0, 0, 0, 0);
+    } else {
+      for (size_t k = tid; k < row_bytes; k += kPackThreads) d[k] = s ? s[k] : uint8_t(0);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_pack(int B, int gamma, const int32_t* windows, const int32_t* context_lens,
+                       const TierTable& tiers, const void* src, size_t row_bytes, void* dst,
+                       int max_rows, int32_t* cu, int32_t* row_req, int32_t* row_pos,
+                       int32_t* total_tier, int32_t* status, hipStream_t stream) {
+  const int blocks = (max_rows + kRowsPerBlock - 1) / kRowsPerBlock;
+  hipLaunchKernelGGL(pack_kernel, dim3(blocks), dim3(kPackThreads), 0, stream, B, gamma, windows,
+                     context_lens, tiers, static_cast<const uint8_t*>(src), row_bytes,
+                     static_cast<uint8_t*>(dst), max_rows, cu, row_req, row_pos, total_tier,
+                     status);
+  return hipGetLastError();
+}
+
+}  // namespace rva

@@ -1,0 +1,118 @@
+// Shared device helpers and launcher declarations of librva (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/rva.h"
+
+namespace rva {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- bf16 <-> f32
+// bf16 is carried as its 16 raw bits; widening is exact (shift into the high half).
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// Round-to-nearest-even narrowing (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  __device__ __forceinline__ static float load(const float* p, size_t i) { return p[i]; }
+  __device__ __forceinline__ static void store(float* p, size_t i, float v) { p[i] = v; }
+};
+template <> struct Elem<uint16_t> {
+  __device__ __forceinline__ static float load(const uint16_t* p, size_t i) { return bf16_to_f32(p[i]); }
+  __device__ __forceinline__ static void store(uint16_t* p, size_t i, float v) { p[i] = f32_to_bf16(v); }
+};
+
+// ---------------------------------------------------------------- wave reductions
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+__device__ __forceinline__ void flag(int32_t* status, int bits) {
+  if (status) atomicOr(status, bits);
+}
+
+// ---------------------------------------------------------------- launchers
+// Each returns hipSuccess or the launch error; arguments are validated by the caller.
+
+struct TierTable {
+  int n;
+  int t[512];
+};
+
+hipError_t launch_schedule(int B, int gamma, int mode, const void* hidden, int hidden_dtype,
+                           int H, const float* head_w, float head_b, const float* conf_in,
+                           const float* sts_T, float bias, const float* alpha,
+                           const float* theta, float* conf_out, float* surv_out,
+                           int32_t* windows, int32_t* K_out, double* ratio_out,
+                           int32_t* status, hipStream_t stream);
+
+hipError_t launch_pack(int B, int gamma, const int32_t* windows, const int32_t* context_lens,
+                       const TierTable& tiers, const void* src, size_t row_bytes, void* dst,
+                       int max_rows, int32_t* cu, int32_t* row_req, int32_t* row_pos,
+                       int32_t* total_tier, int32_t* status, hipStream_t stream);
+
+struct AttnArgs {
+  int B, max_window, max_rows, Hq, Hkv, D, page_size, num_pages, max_pages;
+  const void* q;
+  const void* k_new;
+  const void* v_new;
+  void* k_cache;
+  void* v_cache;
+  const int32_t* block_table;
+  const int32_t* context_lens;
+  const int32_t* cu;
+  const int32_t* total_tier;
+  float scale;
+  void* out;
+  int32_t* status;
+  void* ws;
+};
+size_t attention_workspace_bytes(int B, int max_window, int Hq, int Hkv, int D, int page_size,
+                                 int max_pages, int kv_dtype);
+hipError_t launch_attention(const AttnArgs& a, int kv_dtype, hipStream_t stream);
+
+struct AcceptArgs {
+  int B, gamma, V, max_rows;
+  const void* target;
+  const void* draft;
+  const int32_t* tokens;
+  const float* u_acc;
+  const float* u_res;
+  const int32_t* cu;
+  int32_t* accept_len;
+  int32_t* committed;
+  int32_t* context_lens;
+  float* pt_at;
+  float* pd_at;
+  float* labels;
+  int32_t* status;
+  void* ws;
+};
+size_t accept_workspace_bytes(int B, int gamma, int V, int max_rows);
+hipError_t launch_accept(const AcceptArgs& a, int logit_dtype, bool commit, hipStream_t stream);
+
+}  // namespace rva

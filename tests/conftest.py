@@ -27,3 +27,13 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+@pytest.fixture(scope="session", autouse=True)
+def _library_built():
+    """Build librva.so once if it is missing (hipcc cross-compiles without a GPU)."""
+    from ragged_verify_acceptance_amd import build as _build
+
+    if not os.path.exists(_build.LIB_PATH):
+        _build.build(verbose=True)
+    yield

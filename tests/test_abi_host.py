@@ -1,0 +1,128 @@
+"""Host-side checks of the C ABI (CPU only, no GPU compute).
+
+The library loads, exports every entry point the header declares, and rejects invalid
+arguments on the host before anything is enqueued (these calls return before any HIP
+call is made, so they are safe without a GPU).
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from ragged_verify_acceptance_amd import rva
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rva.h")
+
+OK, INVALID, UNSUPPORTED, WS_SMALL = 0, 1, 2, 3
+FAKE = ctypes.c_void_p(0x100000)  # non-null, 256-aligned; never dereferenced on these paths
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rva_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = rva.lib()
+    names = declared_functions()
+    assert "rva_verify_attention" in names and len(names) == 9
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in rva.h but not exported"
+    assert set(names) == set(rva.EXPORTED)
+
+
+def test_version():
+    assert rva.version() == 100
+
+
+def _sched(**kw):
+    args = dict(B=4, gamma=6, mode=0, hidden=None, hd=1, H=0, head_w=None, head_b=0.0,
+                conf_in=FAKE, sts_T=None, bias=20.0, alpha=FAKE, alpha_len=5, theta=FAKE,
+                theta_len=25, out=FAKE)
+    args.update(kw)
+    a = args
+    return rva.lib().rva_schedule_windows(a["B"], a["gamma"], a["mode"], a["hidden"], a["hd"], a["H"],
+                                          a["head_w"], a["head_b"], a["conf_in"], a["sts_T"], a["bias"],
+                                          a["alpha"], a["alpha_len"], a["theta"], a["theta_len"],
+                                          a["out"], a["out"], a["out"], a["out"], a["out"], None, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), INVALID),
+    (dict(gamma=1), INVALID),
+    (dict(gamma=65), INVALID),
+    (dict(B=1000, gamma=6), INVALID),          # B*(gamma-1) > 4096
+    (dict(mode=7), INVALID),
+    (dict(conf_in=None), INVALID),             # neither hidden nor conf_in
+    (dict(hidden=FAKE, H=16, head_w=FAKE), INVALID),  # both given
+    (dict(sts_T=FAKE), INVALID),               # temperatures need the head's logits
+    (dict(alpha_len=4), INVALID),              # alpha_len must exceed B
+    (dict(theta_len=24), INVALID),             # theta_len must exceed B*gamma
+    (dict(out=None), INVALID),
+])
+def test_schedule_validation(kw, code):
+    assert _sched(**kw) == code
+    assert rva.lib().rva_last_error().decode() != ""
+
+
+def _pack(B=3, gamma=6, tiers=(4, 8, 12, 18), max_rows=18, src=None, dst=None, windows=FAKE):
+    t = (ctypes.c_int32 * len(tiers))(*tiers)
+    return rva.lib().rva_pack_ragged(B, gamma, windows, FAKE, ctypes.cast(t, ctypes.c_void_p), len(tiers),
+                                     src, 16 if src else 0, dst, max_rows, FAKE, FAKE, FAKE, FAKE, None, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), INVALID),
+    (dict(tiers=(4, 12, 8, 18)), INVALID),     # not ascending
+    (dict(tiers=(4, 8, 12, 16)), INVALID),     # largest tier below B*gamma = 18
+    (dict(max_rows=17), INVALID),
+    (dict(src=FAKE), INVALID),                 # src without dst
+    (dict(windows=None), INVALID),
+])
+def test_pack_validation(kw, code):
+    assert _pack(**kw) == code
+
+
+def _attn(B=2, max_window=6, max_rows=16, Hq=32, Hkv=8, D=128, page=64, num_pages=10, max_pages=5,
+          dtype=1, ws=None, ws_bytes=0, q=FAKE):
+    return rva.lib().rva_verify_attention(B, max_window, max_rows, Hq, Hkv, D, page, num_pages, max_pages,
+                                          dtype, q, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.1,
+                                          FAKE, None, ws, ws_bytes, None)
+
+
+def test_attention_validation():
+    need = rva.verify_attention_workspace_size(2, 6, 32, 8, 128, 64, 5, 1)
+    assert need > 0
+    assert _attn(Hq=30) == INVALID                        # Hq % Hkv != 0
+    assert _attn(D=96) == UNSUPPORTED
+    assert _attn(max_window=17) == UNSUPPORTED            # 17 * 4 > 64 rows per kv head
+    assert _attn(dtype=5) == INVALID
+    assert _attn(q=None) == INVALID
+    assert _attn(q=ctypes.c_void_p(0x100002)) == INVALID  # misaligned
+    assert _attn(ws=None) == WS_SMALL
+    assert _attn(ws=FAKE, ws_bytes=need - 1) == WS_SMALL
+    # the float32 generic path needs no workspace
+    assert rva.verify_attention_workspace_size(2, 6, 4, 2, 64, 16, 5, 0) == 0
+
+
+def _accept(B=2, gamma=6, V=1024, dtype=1, max_rows=16, ws=FAKE, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = rva.accept_workspace_size(B, max(gamma, 2), V, max_rows)
+    return rva.lib().rva_accept_and_commit(B, gamma, V, dtype, max_rows, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                           FAKE, FAKE, FAKE, None, None, None, None, ws, ws_bytes, None)
+
+
+def test_accept_validation():
+    assert _accept(B=0) == INVALID
+    assert _accept(gamma=1) == INVALID
+    assert _accept(V=0) == INVALID
+    assert _accept(dtype=3) == INVALID
+    assert _accept(ws_bytes=0) == WS_SMALL
+    assert _accept(ws=None) == WS_SMALL
+    assert _accept(max_rows=70000) == INVALID   # grid rows beyond 65535
+    big = rva.accept_workspace_size(256, 16, 151936, 4096)
+    assert big > rva.accept_workspace_size(64, 8, 151936, 512) > 0
