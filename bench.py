@@ -1,0 +1,218 @@
+"""Benchmark of the verify path on one MI355X.
+
+A step is one pass of the whole path over one batch: rva_schedule_windows ->
+rva_pack_ragged -> rva_verify_attention -> rva_accept_and_commit (with the TV labels
+fused), on the mixed-traffic workload (B = 64, gamma = 8, GQA 32/8 D = 128 bf16 paged KV,
+contexts U[512, 8K], V = 151936 bf16 logits), compact mode.  Inputs are resident in HBM
+before the timed region; between steps context_lens is restored (a 256-byte device copy,
+inside the timed region) so every step redoes the same work.
+
+Prints ONE JSON line: packed verify tokens/s for the step, plus the achieved HBM GB/s of
+verify attention + acceptance, the roofline of the dominant kernel (verify attention,
+timed with HIP events on the stream it runs on) and the CPU oracle's rate on a bounded
+sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0  # MI355X published HBM3E bandwidth
+METRIC = "packed verify tokens/s + achieved HBM GB/s (% peak), verify attn + accept, B=64"
+
+
+def algorithmic_bytes(wl, context_lens, windows):
+    """Bytes each stage must move at minimum (one read of every input byte it needs,
+    one write of every output byte)."""
+    s_kv = 2 if wl.kv_dtype == "bf16" else 4
+    s_lg = 2 if wl.logit_dtype == "bf16" else 4
+    L = context_lens.astype(np.int64)
+    w = windows.astype(np.int64)
+    kvrow = wl.Hkv * wl.D * s_kv
+    attn = int(np.sum(2 * (L + w) * kvrow      # read context K/V + window K/V
+                      + 2 * w * kvrow          # append window K/V to the cache
+                      + 2 * w * wl.Hq * wl.D * s_kv))  # read Q, write O
+    accept = int(np.sum((2 * w - 1) * wl.V * s_lg))   # every target and draft row once
+    flops = int(np.sum(4 * w * wl.Hq * wl.D * (L + (w + 1) / 2)))
+    return attn, accept, flops
+
+
+def cpu_baseline(inp, windows, n_req):
+    """The oracle, single-threaded, on the first n_req requests of the same workload."""
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    from tests.reference import sub_pool
+
+    wl = inp.wl
+    reqs = list(range(n_req))
+    # inputs prepared outside the timed region
+    k_pool, v_pool, bt, _ = sub_pool(inp, reqs)
+    ws = [int(windows[b]) for b in reqs]
+    cu = np.concatenate([[0], np.cumsum(ws)]).astype(np.int32)
+    R = int(cu[-1])
+    q = np.zeros((R, wl.Hq, wl.D))
+    kn = np.zeros((R, wl.Hkv, wl.D))
+    vn = np.zeros((R, wl.Hkv, wl.D))
+    logits = []
+    for j, b in enumerate(reqs):
+        qb, kb, vb = inp.request_qkv(b)
+        q[cu[j]:cu[j + 1]] = qb[: ws[j]].double().numpy()
+        kn[cu[j]:cu[j + 1]] = kb[: ws[j]].double().numpy()
+        vn[cu[j]:cu[j + 1]] = vb[: ws[j]].double().numpy()
+        tl, dl, toks = inp.request_logits(b)
+        logits.append((tl[: ws[j]].double().numpy(), dl[: ws[j] - 1].double().numpy(), toks))
+    ua, ur = inp.uniforms()
+    conf = inp.conf()
+    bias, alpha, theta = inp.cost_tables()
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        a = oracle.survival(conf)
+        oracle.schedule_windows(a, wl.gamma, bias, alpha, theta)
+        oracle.pack_ragged(windows, inp.context_lens, wl.tiers)
+        oracle.verify_attention(q, kn, vn, k_pool, v_pool, bt, inp.context_lens[reqs], cu, R,
+                                np.float32(1.0 / np.sqrt(wl.D)))
+        for j, b in enumerate(reqs):
+            tl, dl, toks = logits[j]
+            oracle.accept_request(tl, dl, toks[: ws[j] - 1], ua[b, : ws[j] - 1], ur[b])
+        dt = time.perf_counter() - t0
+    return {"value": R / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {n_req} of {inp.B} requests of mixed-b64 ({R} packed verify rows): "
+                      f"full-batch scheduling + pack, then attention and acceptance+labels of the "
+                      f"sample, float64 NumPy, 1 thread, {dt:.1f} s on {platform.processor() or platform.machine()}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="mixed-b64")
+    ap.add_argument("--mode", default="compact", choices=["compact", "static"])
+    ap.add_argument("--cpu-sample", type=int, default=24, help="requests in the oracle sample (0: skip)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run one 1 GiB device-to-device copy first (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the verify path is sharded by request across GPUs by the caller, see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from __graft_entry__ import _ensure_built
+    _ensure_built()
+    from workloads import Inputs, get
+    from workloads.device import DeviceStep
+
+    torch.cuda.set_device(0)
+    wl = get(args.workload)
+    inp = Inputs(wl)
+    ds = DeviceStep(inp, mode=args.mode)
+    ds.prepare()
+    torch.cuda.synchronize()
+    windows = ds.windows.cpu().numpy()
+    M, tier = (int(x) for x in ds.total_tier.cpu().numpy())
+    attn_b, acc_b, attn_flops = algorithmic_bytes(wl, inp.context_lens, windows)
+
+    if args.copy_calibration:
+        x = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        y = torch.empty_like(x)
+        y.copy_(x)
+        torch.cuda.synchronize()
+        del x, y
+
+    stream = torch.cuda.current_stream()
+
+    def step():
+        ds.restore()
+        ds.step()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly `steps` whole steps
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    t_host = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_host = time.perf_counter() - t_host
+    ms_step = e0.elapsed_time(e1) / args.steps
+
+    # ---- per-stage durations inside whole steps (HIP events on the launch stream)
+    n_ev = max(10, args.steps // 2)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(n_ev)]
+    for i in range(n_ev):
+        ds.restore()
+        ev[i][0].record(stream)
+        ds.schedule()
+        ds.pack()
+        ev[i][1].record(stream)
+        ds.attention()
+        ev[i][2].record(stream)
+        ds.accept(labels=True)
+        ev[i][3].record(stream)
+    torch.cuda.synchronize()
+    t_front = np.mean([ev[i][0].elapsed_time(ev[i][1]) for i in range(n_ev)])
+    t_attn = np.mean([ev[i][1].elapsed_time(ev[i][2]) for i in range(n_ev)])
+    t_acc = np.mean([ev[i][2].elapsed_time(ev[i][3]) for i in range(n_ev)])
+    status = int(ds.status.item())
+
+    attn_gbs = attn_b / (t_attn * 1e-3) / 1e9
+    acc_gbs = acc_b / (t_acc * 1e-3) / 1e9
+    path_gbs = (attn_b + acc_b) / ((t_attn + t_acc) * 1e-3) / 1e9
+    res = {
+        "metric": METRIC,
+        "value": M / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "mode": args.mode, "B": wl.B, "gamma": wl.gamma,
+                   "Hq": wl.Hq, "Hkv": wl.Hkv, "D": wl.D, "page": wl.page, "V": wl.V,
+                   "packed_rows_M": M, "tier": tier, "mean_window": float(windows.mean()),
+                   "mean_context": float(inp.context_lens.mean())},
+        "verify_attn_accept": {
+            "achieved_GBps": path_gbs, "pct_peak": 100.0 * path_gbs / PEAK_HBM_GBS,
+            "tokens_per_s": M / ((t_attn + t_acc) * 1e-3),
+            "attn_ms": t_attn, "accept_ms": t_acc, "schedule_pack_ms": t_front,
+            "attn_bytes": attn_b, "accept_bytes": acc_b,
+            "attn_GBps": attn_gbs, "accept_GBps": acc_gbs,
+            "attn_TFLOPs": attn_flops / (t_attn * 1e-3) / 1e12,
+        },
+        "roofline": {"kernel": "rva_verify_attention (attn_mfma_kernel + attn_combine_kernel)",
+                     "bound": "hbm", "achieved": attn_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": attn_gbs / PEAK_HBM_GBS, "traffic": None},
+        "device_status": status,
+        "host_wall_s": t_host,
+    }
+    if args.cpu_sample > 0:
+        res["cpu_baseline"] = cpu_baseline(inp, windows, min(args.cpu_sample, inp.B))
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()
