@@ -7,7 +7,9 @@ device, [SGL] "Zero-overhead scheduling 与 kernel"; the layout below is this li
 documented choice):
 
 * ``k_cache[page, kv_head, slot, d]``  -- shape [num_pages, Hkv, page_size, D]
-* ``v_cache[page, kv_head, d, slot]``  -- shape [num_pages, Hkv, D, page_size]
+* ``v_cache[page, kv_head, slot // VB, d, slot % VB]`` -- shape
+  [num_pages, Hkv, page_size // VB, D, VB]: V transposed in column blocks of VB slots,
+  VB = 32 when page_size is a multiple of 32, else VB = page_size
 * sequence position p of request b lives in physical page
   ``block_table[b, p // page_size]`` at slot ``p % page_size``.
 """
@@ -42,7 +44,7 @@ def verify_attention(q, k_new, v_new, k_cache, v_cache, block_table, context_len
     cache at positions ``L_b + i`` (returned as updated copies of both caches).
 
     Shapes: q [R, Hq, D], k_new/v_new [R, Hkv, D] with R >= tier, k_cache
-    [P, Hkv, page, D], v_cache [P, Hkv, D, page], block_table [B, max_pages].
+    [P, Hkv, page, D], v_cache [P, Hkv, page // VB, D, VB], block_table [B, max_pages].
     Returns (out [R, Hq, D] float64, k_cache', v_cache').
     """
     q = np.asarray(q, dtype=np.float64)
@@ -53,6 +55,8 @@ def verify_attention(q, k_new, v_new, k_cache, v_cache, block_table, context_len
     R, Hq, D = q.shape
     Hkv = k_new.shape[1]
     page = k_cache.shape[2]
+    VB = v_cache.shape[4]
+    assert VB == v_block(page) and v_cache.shape[2] * VB == page
     assert Hq % Hkv == 0
     group = Hq // Hkv
     scale = float(np.float32(softmax_scale))
@@ -70,7 +74,7 @@ def verify_attention(q, k_new, v_new, k_cache, v_cache, block_table, context_len
             pg = int(block_table[b, p // page])
             s = p % page
             Kc[:, p, :] = k_cache[pg, :, s, :]
-            Vc[:, p, :] = v_cache[pg, :, :, s]
+            Vc[:, p, :] = v_cache[pg, :, s // VB, :, s % VB]
         for i in range(w):
             r = r0 + i
             for h in range(Hq):
@@ -85,9 +89,14 @@ def verify_attention(q, k_new, v_new, k_cache, v_cache, block_table, context_len
             pg = int(block_table[b, p // page])
             s = p % page
             k_cache[pg, :, s, :] = k_new[r0 + i]
-            v_cache[pg, :, :, s] = v_new[r0 + i]
+            v_cache[pg, :, s // VB, :, s % VB] = v_new[r0 + i]
     # rows M .. tier-1 stay zero (already zero)
     return out, k_cache, v_cache
+
+
+def v_block(page_size):
+    """Column-block width of the V cache layout (see the module docstring)."""
+    return 32 if page_size % 32 == 0 else page_size
 
 
 def default_scale(D):

@@ -6,52 +6,68 @@
 // and section 3 of the devpress.csdn.net DSpark-in-SGLang article: each packed verify
 // token attends only to its own request's KV, delimited by cu_seqlens.
 //
-// Design (bf16, D in {64, 128}, page_size % 32 == 0):
-//   * Work item = (request b, kv head g, chunk of kChunk keys); grid (chunks, Hkv, B),
-//     chunks beyond a request's length exit at once.  Every K/V byte of the request is
-//     read exactly once for ALL window rows and ALL Hq/Hkv query heads of the group: the
-//     (window row, head-in-group) pairs form the N side of the MFMA tiles (NB blocks of 16).
-//   * Each of the 4 waves streams kKeysPerWave keys in tiles of 32 keys.  Scores are
-//     computed transposed, S^T = K Q^T, with mfma_f32_16x16x32_bf16: K rows are the A
-//     operand, loaded as 16-byte vectors straight from the (page, head) block, which is a
-//     contiguous [page_size, D] tile in this layout.  The accumulator lane layout leaves
-//     each lane with 4 keys x 1 query column per 16-key block; with the contraction index
-//     of the PV product permuted to match (slot 8q+t <-> key 4q+t, slot 8q+4+t <-> key
-//     16+4q+t), the probabilities P^T are ALREADY the B operand of O^T = V^T P^T: no LDS
-//     round trip.  V is stored transposed per page ([D, page_size]), so the A operand V^T
-//     is two 8-byte loads per lane.
-//   * Online softmax in the log2 domain per query column; the 4 waves of a workgroup are
-//     merged through LDS in a fixed order (deterministic), then either the final output
-//     (one chunk) or a normalised partial + log-sum-exp goes out; a small combine kernel
-//     merges the chunks and zero-fills the pad rows [M, tier).
-//   * The tile that reaches past the cached context takes the window keys from k_new /
-//     v_new (packed rows) and applies the causal mask; the last chunk's workgroup writes
-//     the window K/V into the cache (positions L .. L+w-1), which no other work item of
-//     this launch reads.
-// Any other dtype / page size uses attn_generic_kernel (one wave per query column, one key
-// per lane, online softmax), which is also the float32 path.
+// bf16 path (D in {64, 128}, page_size a power of two >= 32, B <= 1024): attn_sk_kernel
+//   * Work: a segment is one (request b, kv head g); it is cut into tiles of 32 keys.
+//     Every K/V byte of a segment is read once for ALL window rows and ALL Hq/Hkv query
+//     heads of the group: the (window row, head-in-group) pairs are the N side of the
+//     MFMA tiles (NB blocks of 16 columns, NB chosen per segment from its window).
+//   * Balance: persistent grid, one workgroup per CU slot; all segments form one weighted
+//     sequence (each segment = its tiles + a fixed start cost of kSegCost tile units) and
+//     workgroup p owns the contiguous share [W p / P, W (p+1) / P) (stream-K over bytes AND
+//     per-segment overhead).  A segment that lies inside one share is finished by that
+//     workgroup; a segment cut by share boundaries leaves at most one partial per workgroup
+//     side and attn_merge_kernel combines them.  No workgroup ever waits for another.
+//   * Inside a workgroup the 4 waves take the segment's tiles round-robin, one wave per
+//     SIMD.  Each wave rotates three register buffers, so two tiles (32 KB) are in flight
+//     while it computes a third.  Page numbers for 64 tiles at a time are preloaded into
+//     lanes and read back with readlane; operand addresses are a uniform SGPR base per
+//     tile plus lane-constant 32-bit offsets (global loads, no 64-bit lane arithmetic).
+//   * Scores are computed transposed, S^T = K Q^T, with mfma_f32_16x16x32_bf16 (K rows are
+//     the A operand, 16-byte loads from the (page, head) block, a contiguous
+//     [page_size, D] tile in this cache layout).  Row m of 16-key block mb holds key
+//     8(m/4) + 4mb + m%4, so each lane's accumulator holds 8 CONSECUTIVE keys for one
+//     query column; those probabilities are then directly the B operand of
+//     O^T = V^T P^T, and the V^T operand is one 16-byte load per lane from the transposed
+//     per-page V tile [D, page_size].  No LDS round trip on the streaming path.
+//   * Online softmax in the log2 domain with lazy rescaling: the running max only moves
+//     (and the accumulators are only rescaled) when a tile's max exceeds it by more than
+//     2^8, so most tiles cost no rescale.  P is narrowed to bf16 with v_cvt_pk_bf16_f32.
+//   * The 1-2 tiles of a segment that reach past the cached context take the window keys
+//     from k_new / v_new (packed rows) and apply the causal mask.  The window K/V is
+//     appended to the cache (positions L .. L+w-1) by attn_merge_kernel, after every read.
+//   * The V cache is transposed in column blocks of 32 slots ([D][32] per block), so each
+//     tile's V^T operand is one contiguous 8 KB block, like its K rows: every load
+//     instruction fetches full cache lines.
+// Any other dtype / shape uses attn_generic_kernel (one wave per query column, one key per
+// lane, online softmax), which is also the float32 path.
 #include "rva_common.h"
+
+#include <mutex>
 
 namespace rva {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short short8 __attribute__((ext_vector_type(8)));
-typedef short short4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kAttnWaves = 4;
-constexpr int kAttnThreads = kAttnWaves * kWave;
-constexpr int kKeysPerWave = 256;
-constexpr int kChunk = kAttnWaves * kKeysPerWave;  // keys per workgroup
-constexpr int kTile = 32;
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * kWave;
+constexpr int kTile = 32;     // keys per tile
+constexpr int kMaxB = 1024;   // requests the persistent path takes
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRescale = 8.f;  // lazy-rescale threshold, log2 units
+// Fixed cost of starting a segment (Q load, pipeline fill, merge, stores), in tile units:
+// shares are balanced over tiles + kSegCost per segment.
+constexpr int kSegCost = 16;
 
 struct ReqInfo {
   int L, r0, w, ok;
 };
 
-// Validates request b's metadata; raises device-status bits once per request.
+// Validates request b's metadata; raises device-status bits when `report`.
 __device__ __forceinline__ ReqInfo req_info(const AttnArgs& a, int b, bool report) {
   ReqInfo r;
   r.L = a.context_lens[b];
@@ -71,11 +87,24 @@ __device__ __forceinline__ ReqInfo req_info(const AttnArgs& a, int b, bool repor
   return r;
 }
 
-__device__ __forceinline__ short8 load16(const uint16_t* p) {
-  return *reinterpret_cast<const short8*>(p);
+__device__ __forceinline__ short8 load16(const uint16_t* p) { return *reinterpret_cast<const short8*>(p); }
+
+// Global-address-space views: loads through them become global_load (not flat) with a
+// uniform 64-bit base in SGPRs and a 32-bit per-lane offset.
+typedef const __attribute__((address_space(1))) uint16_t* gptr16;
+__device__ __forceinline__ gptr16 as_global(const void* p) {
+  return reinterpret_cast<gptr16>(reinterpret_cast<uintptr_t>(p));
 }
-__device__ __forceinline__ short4 load8(const uint16_t* p) {
-  return *reinterpret_cast<const short4*>(p);
+__device__ __forceinline__ short8 gload16(gptr16 base, uint32_t off) {
+  return *reinterpret_cast<const __attribute__((address_space(1))) short8*>(base + off);
+}
+
+// V cache: transposed in column blocks of vblk(P) slots, element (page, g, slot, d) at
+// ((page * Hkv + g) * P + (slot / VB) * VB) * D + d * VB + slot % VB.
+__host__ __device__ __forceinline__ int vblk(int P) { return P % 32 == 0 ? 32 : P; }
+__device__ __forceinline__ size_t v_index(int pg, int g, int Hkv, int P, int D, int slot, int d) {
+  const int VB = vblk(P);
+  return (size_t(pg) * Hkv + g) * P * D + size_t(slot / VB) * VB * D + size_t(d) * VB + slot % VB;
 }
 
 __device__ __forceinline__ int page_of(const AttnArgs& a, int b, int p, bool& bad) {
@@ -87,315 +116,593 @@ __device__ __forceinline__ int page_of(const AttnArgs& a, int b, int p, bool& ba
   return pg;
 }
 
-template <int D, int NB>
-__global__ __launch_bounds__(kAttnThreads) void attn_mfma_kernel(AttnArgs a, int max_splits) {
-  constexpr int DS = D / 32;  // k-steps of the score MFMA
-  constexpr int DB = D / 16;  // 16-row blocks of O^T
-  constexpr int ROWS = NB * 16;
-  __shared__ float sm_m[kAttnWaves][ROWS];
-  __shared__ float sm_l[kAttnWaves][ROWS];
-  __shared__ float sm_M[ROWS];
-  __shared__ float sm_L[ROWS];
-  __shared__ float sm_o[ROWS][D + 4];
+// ------------------------------------------------------------------ work split
+struct ReqTable {
+  int nt[kMaxB];       // tiles per segment of request b (0 if the request is invalid)
+  int pre[kMaxB + 1];  // exclusive prefix of Hkv * span(b), span = nt + kSegCost (0 if nt = 0):
+                       // first work unit of request b in the weighted sequence
+  int L[kMaxB];
+  int r0[kMaxB];
+  int w[kMaxB];
+};
 
-  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-  const int lc = lane % 16, lq = lane / 16;
-  const ReqInfo ri = req_info(a, b, split == 0 && g == 0 && tid == 0);
-  if (!ri.ok) return;
-  const int L = ri.L, r0 = ri.r0, w = ri.w, Lw = L + w;
-  const int nsplit = (Lw + kChunk - 1) / kChunk;
-  if (split >= nsplit) return;
-  const int G = a.Hq / a.Hkv;
-  const int nq = w * G;
+// Work units of one segment: its tiles plus the fixed start cost (none if it has no tiles).
+__device__ __forceinline__ int seg_span(int nt) { return nt > 0 ? nt + kSegCost : 0; }
+
+// Every workgroup (of both kernels) builds the same table from the same device data.
+__device__ __forceinline__ void build_table(const AttnArgs& a, ReqTable& t, bool report) {
+  __shared__ int part[kThreads];
+  const int tid = threadIdx.x, B = a.B;
+  for (int b = tid; b < B; b += kThreads) {
+    const ReqInfo ri = req_info(a, b, report);
+    t.L[b] = ri.L;
+    t.r0[b] = ri.r0;
+    t.w[b] = ri.w;
+    t.nt[b] = ri.ok ? (ri.L + ri.w + kTile - 1) / kTile : 0;
+  }
+  __syncthreads();
+  const int per = (B + kThreads - 1) / kThreads;
+  const int b0 = tid * per;
+  int run = 0;
+  for (int i = 0; i < per; ++i)
+    if (b0 + i < B) run += seg_span(t.nt[b0 + i]) * a.Hkv;
+  part[tid] = run;
+  __syncthreads();
+  for (int o = 1; o < kThreads; o <<= 1) {
+    const int v = tid >= o ? part[tid - o] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int acc = tid > 0 ? part[tid - 1] : 0;
+  for (int i = 0; i < per; ++i)
+    if (b0 + i < B) {
+      t.pre[b0 + i] = acc;
+      acc += seg_span(t.nt[b0 + i]) * a.Hkv;
+    }
+  if (tid == kThreads - 1) t.pre[B] = part[kThreads - 1];
+  __syncthreads();
+}
+
+// First global tile of workgroup p's share, and the workgroup whose share holds tile x.
+__device__ __forceinline__ int share_lo(int T, int P, int p) { return int((long long)T * p / P); }
+__device__ __forceinline__ int share_owner(int T, int P, int x) {
+  return int(((long long)(x + 1) * P - 1) / T);
+}
+
+// Largest b with pre[b] <= x (skips requests without tiles).
+__device__ __forceinline__ int find_req(const ReqTable& t, int B, int x) {
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (t.pre[mid] <= x) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// ------------------------------------------------------------------ tile math
+template <int D, int NB, bool MASK>
+__device__ __forceinline__ void tile_compute(const short8 (&kop)[2][D / 32], const short8 (&vop)[D / 16],
+                                             const short8 (&qop)[NB][D / 32], f32x4 (&oacc)[D / 16][NB],
+                                             float (&m)[NB], float (&l)[NB], float sl2, int key0,
+                                             const int (&limit)[NB], int lq) {
+  constexpr int DS = D / 32, DB = D / 16;
+  f32x4 s[2][NB];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < DS; ++k)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kop[mb][k]),
+                                                      __builtin_bit_cast(bf16x8, qop[nb][k]), acc, 0, 0, 0);
+      s[mb][nb] = acc;
+    }
+  // this lane: column lc, keys key0 + 8 lq + 4 mb + t
+  float sc[NB][8];
+  bool need = false;
+  float mt[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        float v = s[mb][nb][t] * sl2;
+        if (MASK && key0 + 8 * lq + 4 * mb + t > limit[nb]) v = -INFINITY;
+        sc[nb][mb * 4 + t] = v;
+        mx = fmaxf(mx, v);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mt[nb] = mx;
+    need |= mx > m[nb] + kRescale;
+  }
+  if (__ballot(need)) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const float mn = fmaxf(m[nb], mt[nb]);
+      if (mn != m[nb]) {
+        const float alpha = (m[nb] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m[nb] - mn);
+        l[nb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[db][nb] *= alpha;
+        m[nb] = mn;
+      }
+    }
+  }
+  short8 pop[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    float ps = 0.f;
+    uint32_t packed[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {  // two probabilities per v_cvt_pk_bf16_f32
+      f32x2 p2;
+      p2[0] = __builtin_amdgcn_exp2f(sc[nb][2 * i] - m[nb]);
+      p2[1] = __builtin_amdgcn_exp2f(sc[nb][2 * i + 1] - m[nb]);
+      if (MASK && m[nb] == -INFINITY) p2 = f32x2{0.f, 0.f};
+      ps += p2[0] + p2[1];
+      packed[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(p2, bf16x2));
+    }
+    l[nb] += ps;
+    pop[nb] = __builtin_bit_cast(short8, packed);
+  }
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+      oacc[db][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vop[db]),
+                                                             __builtin_bit_cast(bf16x8, pop[nb]), oacc[db][nb], 0, 0, 0);
+}
+
+// Key held by A-operand row m of 16-key block mb (see the file comment).
+__device__ __forceinline__ int row_key(int m, int mb) { return 8 * (m >> 2) + 4 * mb + (m & 3); }
+
+// Lane-constant element offsets of the fast-path operands inside one (page, head) block.
+template <int D>
+struct LaneOffsets {
+  uint32_t k[2];  // + 32 k per MFMA k-step (immediate offsets)
+  uint32_t v;     // + 512 db per 16-row block of the tile's [D][32] V^T block
+};
+
+// One 32-key tile: K rows [32][D] and the V^T block [D][32], each 8 KB contiguous (D = 128).
+template <int D>
+__device__ __forceinline__ void load_fast(gptr16 kbase, gptr16 vbase, const LaneOffsets<D>& lo,
+                                          short8 (&kop)[2][D / 32], short8 (&vop)[D / 16]) {
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int k = 0; k < D / 32; ++k) kop[mb][k] = gload16(kbase, lo.k[mb] + k * 32);
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db) vop[db] = gload16(vbase, lo.v + uint32_t(db * 16 * 32));
+}
+
+// Tile that reaches past the cached context.  The tile lies inside one page, so one page
+// lookup serves its cached keys (p < L); window keys (L <= p < Lw) come from the packed
+// k_new / v_new rows; keys past the window (masked later) read the window's first row so
+// that every lane issues a load from a valid, finite address.  Addresses are selected,
+// not branched on, so all loads are in flight together.
+template <int D>
+__device__ __forceinline__ void load_tail(const AttnArgs& a, int b, int g, int L, int r0, int Lw, int key0, int lc,
+                                          int lq, short8 (&kop)[2][D / 32], short8 (&vop)[D / 16], bool& bad) {
   const int Hkv = a.Hkv, P = a.page_size;
   const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache);
   const uint16_t* vc = static_cast<const uint16_t*>(a.v_cache);
   const uint16_t* kn = static_cast<const uint16_t*>(a.k_new);
   const uint16_t* vn = static_cast<const uint16_t*>(a.v_new);
-  const float sl2 = a.scale * kLog2e;
-  bool bad_page = false;
+  int pg = 0;
+  if (key0 < L) {
+    pg = a.block_table[size_t(b) * a.max_pages + key0 / P];
+    if (pg < 0 || pg >= a.num_pages) {
+      bad = true;
+      pg = 0;
+    }
+  }
+  const int slot0 = key0 % P;
+  const uint16_t* kpage = kc + ((size_t(pg) * Hkv + g) * P + slot0) * D;  // key key0 + i at kpage + i*D
+  const uint16_t* vtile = vc + ((size_t(pg) * Hkv + g) * P + slot0) * D;  // (d, key0 + i) at vtile + d*32 + i
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    const int i = row_key(lc, mb), p = key0 + i;
+    const uint16_t* krow = p < L ? kpage + size_t(i) * D
+                                 : kn + (size_t(r0 + (p < Lw ? p - L : 0)) * Hkv + g) * D;
+#pragma unroll
+    for (int k = 0; k < D / 32; ++k) kop[mb][k] = load16(krow + k * 32 + 8 * lq);
+  }
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db) {
+    const int d = db * 16 + lc;
+    short8 v;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int i = 8 * lq + t, p = key0 + i;
+      const uint16_t* src = p < L ? vtile + size_t(d) * 32 + i
+                                  : vn + (size_t(r0 + (p < Lw ? p - L : 0)) * Hkv + g) * D + d;
+      v[t] = short(*src);
+    }
+    vop[db] = v;
+  }
+}
 
-  // Q^T as the B operand: lane holds column n = nb*16 + lc, d = s*32 + 8*lq .. +7
+template <int D, int NBMAX>
+struct SkShared {
+  ReqTable tab;
+  float m[kWaves][NBMAX * 16];
+  float l[kWaves][NBMAX * 16];
+  float M[NBMAX * 16];
+  float Ls[NBMAX * 16];
+  // per-wave partial outputs for the segment-end merge (4 slices; 2 when NBMAX = 4, the
+  // other two waves add into them)
+  float o[NBMAX <= 2 ? 4 : 2][NBMAX * 16][D + 4];
+};
+
+// One segment's share: tiles [t0, t0 + n) of (b, g); `full`: the whole segment (final
+// output), otherwise a partial into workspace slot `slot_index`.
+template <int D, int NB, int NBMAX>
+__device__ __forceinline__ void run_segment(const AttnArgs& a, SkShared<D, NBMAX>& sh, int b, int g, int t0, int n, bool full,
+                            int slot_index) {
+  constexpr int DS = D / 32, DB = D / 16;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int lc = lane % 16, lq = lane / 16;
+  const int L = sh.tab.L[b], r0 = sh.tab.r0[b], w = sh.tab.w[b], Lw = L + w;
+  const int Hkv = a.Hkv, P = a.page_size, G = a.Hq / a.Hkv, nq = w * G;
+  const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache);
+  const uint16_t* vc = static_cast<const uint16_t*>(a.v_cache);
+  const float sl2 = a.scale * kLog2e;
+  bool bad = false;
+
   short8 qop[NB][DS];
-  int limit[NB];  // last visible key position for column n
+  int limit[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    const int n = nb * 16 + lc;
-    const bool valid = n < nq;
-    limit[nb] = valid ? L + n / G : Lw - 1;
+    const int col = nb * 16 + lc;
+    const bool valid = col < nq;
+    limit[nb] = valid ? L + col / G : Lw - 1;
     const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
-                           (size_t(r0 + (valid ? n / G : 0)) * a.Hq + g * G + (valid ? n % G : 0)) * D;
+                           (size_t(r0 + (valid ? col / G : 0)) * a.Hq + g * G + (valid ? col % G : 0)) * D;
 #pragma unroll
-    for (int s = 0; s < DS; ++s) qop[nb][s] = valid ? load16(qrow + s * 32 + 8 * lq) : short8{0, 0, 0, 0, 0, 0, 0, 0};
+    for (int k = 0; k < DS; ++k) qop[nb][k] = valid ? load16(qrow + k * 32 + 8 * lq) : short8{0, 0, 0, 0, 0, 0, 0, 0};
   }
-
   f32x4 oacc[DB][NB];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) oacc[db][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run[NB], l_run[NB];
+  float m[NB], l[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    m_run[nb] = -INFINITY;
-    l_run[nb] = 0.f;
+    m[nb] = -INFINITY;
+    l[nb] = 0.f;
   }
 
-  const int kb = split * kChunk + wave * kKeysPerWave;
-  const int ke = min(kb + kKeysPerWave, Lw);
-  for (int t0 = kb; t0 < ke; t0 += kTile) {
-    short8 kop[2][DS];
-    short8 vop[DB];
-    const bool fast = t0 + kTile <= L;
-    if (fast) {
-      const int pg = page_of(a, b, t0, bad_page);
-      if (pg < 0) break;
-      const int slot0 = t0 % P;
-      const uint16_t* kbase = kc + ((size_t(pg) * Hkv + g) * P + slot0) * D;
+  // ---- fully cached tiles of this share: [t0, tf); this wave takes every 4th one
+  const int tf = min(t0 + n, L / kTile);
+  const int nfast = max(0, tf - t0);
+  const int nk = nfast > wave ? (nfast - wave + kWaves - 1) / kWaves : 0;
+  const int lp = a.log2_page;
+  const size_t page_elems = size_t(Hkv) * P * D;  // one physical page of K (or V), all heads
+  const gptr16 kseg = as_global(kc) + size_t(g) * P * D;
+  const gptr16 vseg = as_global(vc) + size_t(g) * D * P;
+  LaneOffsets<D> lo;
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int s = 0; s < DS; ++s) kop[mb][s] = load16(kbase + size_t(mb * 16 + lc) * D + s * 32 + 8 * lq);
-      const uint16_t* vbase = vc + (size_t(pg) * Hkv + g) * D * P + slot0 + 4 * lq;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const uint16_t* vrow = vbase + size_t(db * 16 + lc) * P;
-        const short4 lo = load8(vrow), hi = load8(vrow + 16);
-        vop[db] = short8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  for (int mb = 0; mb < 2; ++mb) lo.k[mb] = uint32_t(row_key(lc, mb) * D + 8 * lq);
+  lo.v = uint32_t(lc * 32 + 8 * lq);
+  // block-table row through the scalar cache: page lookups are s_load (lgkmcnt), so they
+  // never make a vector-memory wait drain the tile loads in flight
+  const __attribute__((address_space(4))) int* btrow =
+      reinterpret_cast<const __attribute__((address_space(4))) int*>(
+          reinterpret_cast<uintptr_t>(a.block_table + size_t(b) * a.max_pages));
+  const int num_pages = a.num_pages;
+  auto page_k = [&](int k) -> int {  // physical page of this wave's k-th cached tile (clamped)
+    const int kk = min(k, nk - 1);
+    int pg = btrow[((t0 + wave + kWaves * kk) * kTile) >> lp];
+    if (pg < 0 || pg >= num_pages) {
+      bad = true;
+      pg = 0;
+    }
+    return pg;
+  };
+  // register ring: with three buffers tiles k+1 and k+2 are in flight while tile k is
+  // computed (two buffers for NB = 4, whose accumulators take the registers).  Loads are
+  // issued unconditionally (past the end they repeat the last tile), so every path has the
+  // same number of loads outstanding and each wait is exact.
+  constexpr int kStages = NB >= 4 ? 1 : 2;  // NB = 4's accumulators leave room for one buffer
+  short8 kA[2][DS], vA[DB], kB[2][DS], vB[DB], kC[2][DS], vC[DB];
+  int pg_next = 0;
+  auto issue = [&](int k, short8 (&kb)[2][DS], short8 (&vb)[DB]) {
+    const int pg = pg_next;
+    pg_next = page_k(k + 1);
+    const int slot0 = ((t0 + wave + kWaves * min(k, nk - 1)) * kTile) & (P - 1);
+    load_fast<D>(kseg + size_t(pg) * page_elems + size_t(slot0) * D, vseg + size_t(pg) * page_elems + size_t(slot0) * D,
+                 lo, kb, vb);
+  };
+  auto key_k = [&](int k) { return (t0 + wave + kWaves * k) * kTile; };
+  // A tile that reaches past the cached context (at most one per wave) is loaded first, into
+  // ring buffer C, so its loads overlap the first two cached tiles' loads; it is computed
+  // before the ring starts.  Both branches leave the same loads in flight.
+  const int jt = nfast + ((wave - nfast) % kWaves + kWaves) % kWaves;
+  // NB = 4 keeps too many accumulators for a third buffer: its tail goes after the ring
+  constexpr bool kTailFirst = NB <= 2;
+  const bool has_tail = kTailFirst && jt < n;
+  auto tail_compute = [&]() {
+    tile_compute<D, NB, true>(kC, vC, qop, oacc, m, l, sl2, (t0 + jt) * kTile, limit, lq);
+  };
+  if (nk == 0) {
+    if (kTailFirst && jt < n) {
+      load_tail<D>(a, b, g, L, r0, Lw, (t0 + jt) * kTile, lc, lq, kC, vC, bad);
+      tail_compute();
+    }
+  } else {
+    pg_next = page_k(0);
+    if (has_tail) {
+      load_tail<D>(a, b, g, L, r0, Lw, (t0 + jt) * kTile, lc, lq, kC, vC, bad);
+      issue(0, kA, vA);
+      if (kStages == 3) issue(1, kB, vB);
+      tail_compute();
+    } else {
+      issue(0, kA, vA);
+      if (kStages == 3) issue(1, kB, vB);
+    }
+    if constexpr (kStages == 3) {
+      for (int k = 0; k < nk; k += 3) {
+        issue(k + 2, kC, vC);
+        tile_compute<D, NB, false>(kA, vA, qop, oacc, m, l, sl2, key_k(k), limit, lq);
+        if (k + 1 >= nk) break;
+        issue(k + 3, kA, vA);
+        tile_compute<D, NB, false>(kB, vB, qop, oacc, m, l, sl2, key_k(k + 1), limit, lq);
+        if (k + 2 >= nk) break;
+        issue(k + 4, kB, vB);
+        tile_compute<D, NB, false>(kC, vC, qop, oacc, m, l, sl2, key_k(k + 2), limit, lq);
+      }
+    } else if constexpr (kStages == 2) {
+      for (int k = 0; k < nk; k += 2) {
+        issue(k + 1, kB, vB);
+        tile_compute<D, NB, false>(kA, vA, qop, oacc, m, l, sl2, key_k(k), limit, lq);
+        if (k + 1 >= nk) break;
+        issue(k + 2, kA, vA);
+        tile_compute<D, NB, false>(kB, vB, qop, oacc, m, l, sl2, key_k(k + 1), limit, lq);
       }
     } else {
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const int p = t0 + mb * 16 + lc;
-        const uint16_t* krow = nullptr;
-        if (p < L) {
-          const int pg = page_of(a, b, p, bad_page);
-          if (pg >= 0) krow = kc + ((size_t(pg) * Hkv + g) * P + p % P) * D;
-        } else if (p < Lw) {
-          krow = kn + (size_t(r0 + p - L) * Hkv + g) * D;
-        }
-#pragma unroll
-        for (int s = 0; s < DS; ++s)
-          kop[mb][s] = krow ? load16(krow + s * 32 + 8 * lq) : short8{0, 0, 0, 0, 0, 0, 0, 0};
-      }
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int d = db * 16 + lc;
-        short8 v;
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const int p = t0 + h * 16 + 4 * lq + t;
-            short x = 0;
-            if (p < L) {
-              const int pg = page_of(a, b, p, bad_page);
-              if (pg >= 0) x = short(vc[((size_t(pg) * Hkv + g) * D + d) * P + p % P]);
-            } else if (p < Lw) {
-              x = short(vn[(size_t(r0 + p - L) * Hkv + g) * D + d]);
-            }
-            v[h * 4 + t] = x;
-          }
-        vop[db] = v;
+      for (int k = 0; k < nk; ++k) {
+        if (k > 0) issue(k, kA, vA);
+        tile_compute<D, NB, false>(kA, vA, qop, oacc, m, l, sl2, key_k(k), limit, lq);
       }
     }
-
-    // scores S^T[key][col] for the 32 keys of the tile
-    f32x4 sacc[2][NB];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < DS; ++s)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kop[mb][s]),
-                                                        __builtin_bit_cast(bf16x8, qop[nb][s]), acc, 0, 0, 0);
-        sacc[mb][nb] = acc;
-      }
-
-    short8 pop[NB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      float sc[2][4];
-      float mt = -INFINITY;
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int p = t0 + mb * 16 + 4 * lq + t;
-          const float v = (p <= limit[nb]) ? sacc[mb][nb][t] * sl2 : -INFINITY;
-          sc[mb][t] = v;
-          mt = fmaxf(mt, v);
-        }
-      mt = fmaxf(mt, __shfl_xor(mt, 16));
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
-      const float mnew = fmaxf(m_run[nb], mt);
-      const bool none = mnew == -INFINITY;
-      const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(m_run[nb] - mnew);
-      float psum = 0.f;
-      short8 pv;
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const float pf = none ? 0.f : __builtin_amdgcn_exp2f(sc[mb][t] - mnew);
-          const uint16_t pb = f32_to_bf16(pf);
-          psum += bf16_to_f32(pb);
-          pv[mb * 4 + t] = short(pb);
-        }
-      l_run[nb] = l_run[nb] * alpha + psum;
-      m_run[nb] = mnew;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) oacc[db][nb] *= alpha;
-      pop[nb] = pv;
-    }
-
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-        oacc[db][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vop[db]),
-                                                               __builtin_bit_cast(bf16x8, pop[nb]),
-                                                               oacc[db][nb], 0, 0, 0);
   }
-  if (bad_page) flag(a.status, RVA_DEV_BAD_PAGE);
+  if (!kTailFirst && jt < n) {
+    load_tail<D>(a, b, g, L, r0, Lw, (t0 + jt) * kTile, lc, lq, kA, vA, bad);
+    tile_compute<D, NB, true>(kA, vA, qop, oacc, m, l, sl2, (t0 + jt) * kTile, limit, lq);
+  }
+  if (bad) flag(a.status, RVA_DEV_BAD_PAGE);
 
-  // ---- merge the 4 waves (fixed order) ----
+  // ---- merge the 4 waves: exchange (m, l), rescale, park in LDS slices, combine
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    float l = l_run[nb];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
-    l_run[nb] = l;
+    float sum = l[nb];
+    sum += __shfl_xor(sum, 16);
+    sum += __shfl_xor(sum, 32);
     if (lq == 0) {
-      sm_m[wave][nb * 16 + lc] = m_run[nb];
-      sm_l[wave][nb * 16 + lc] = l;
+      sh.m[wave][nb * 16 + lc] = m[nb];
+      sh.l[wave][nb * 16 + lc] = sum;
     }
   }
   __syncthreads();
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    const int n = nb * 16 + lc;
+    const int col = nb * 16 + lc;
     float M = -INFINITY;
 #pragma unroll
-    for (int v = 0; v < kAttnWaves; ++v) M = fmaxf(M, sm_m[v][n]);
-    float Lsum = 0.f;
+    for (int v = 0; v < kWaves; ++v) M = fmaxf(M, sh.m[v][col]);
+    float Ls = 0.f;
 #pragma unroll
-    for (int v = 0; v < kAttnWaves; ++v)
-      if (sm_m[v][n] != -INFINITY) Lsum += sm_l[v][n] * __builtin_amdgcn_exp2f(sm_m[v][n] - M);
-    const float e = (m_run[nb] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run[nb] - M);
+    for (int v = 0; v < kWaves; ++v)
+      if (sh.m[v][col] != -INFINITY) Ls += sh.l[v][col] * __builtin_amdgcn_exp2f(sh.m[v][col] - M);
+    const float e = (m[nb] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m[nb] - M);
 #pragma unroll
     for (int db = 0; db < DB; ++db) oacc[db][nb] *= e;
     if (wave == 0 && lq == 0) {
-      sm_M[n] = M;
-      sm_L[n] = Lsum;
+      sh.M[col] = M;
+      sh.Ls[col] = Ls;
     }
   }
-  for (int v = 0; v < kAttnWaves; ++v) {
-    if (wave == v) {
+  constexpr int S = NBMAX <= 2 ? 4 : 2;
+  if (wave < S) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) sh.o[wave][nb * 16 + lc][db * 16 + 4 * lq + t] = oacc[db][nb][t];
+  }
+  if constexpr (S < kWaves) {
+    __syncthreads();
+    if (wave >= S) {
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            float& dst = sm_o[nb * 16 + lc][db * 16 + 4 * lq + t];
-            dst = (v == 0) ? oacc[db][nb][t] : dst + oacc[db][nb][t];
-          }
+          for (int t = 0; t < 4; ++t) sh.o[wave - S][nb * 16 + lc][db * 16 + 4 * lq + t] += oacc[db][nb][t];
     }
-    __syncthreads();
   }
-
-  // ---- write: final output (single chunk) or normalised partial + lse ----
-  const size_t bg = size_t(b) * Hkv + g;
-  float* ws_o = static_cast<float*>(a.ws);
-  float* ws_lse = ws_o + size_t(a.B) * Hkv * max_splits * ROWS * D;
-  for (int idx = tid; idx < nq * D; idx += kAttnThreads) {
-    const int n = idx / D, d = idx % D;
-    const float Ls = sm_L[n];
-    const float val = Ls > 0.f ? sm_o[n][d] / Ls : 0.f;
-    if (nsplit == 1) {
-      uint16_t* o = static_cast<uint16_t*>(a.out);
-      o[(size_t(r0 + n / G) * a.Hq + g * G + n % G) * D + d] = f32_to_bf16(val);
+  __syncthreads();
+  constexpr int ROWS = NBMAX * 16;
+  for (int it = tid; it < nq * (D / 8); it += kThreads) {  // 8 consecutive d per thread
+    const int col = it / (D / 8), d0 = (it % (D / 8)) * 8;
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = 0.f;
+#pragma unroll
+    for (int sl = 0; sl < S; ++sl)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] += sh.o[sl][col][d0 + u];
+    const float Ls = sh.Ls[col];
+    const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+    if (full) {
+      uint32_t pk[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        pk[u] = uint32_t(f32_to_bf16(v[2 * u] * inv)) | (uint32_t(f32_to_bf16(v[2 * u + 1] * inv)) << 16);
+      uint16_t* o = static_cast<uint16_t*>(a.out) + (size_t(r0 + col / G) * a.Hq + g * G + col % G) * D + d0;
+      *reinterpret_cast<uint4*>(o) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
     } else {
-      ws_o[((bg * max_splits + split) * ROWS + n) * D + d] = val;
-      if (d == 0) ws_lse[(bg * max_splits + split) * ROWS + n] = Ls > 0.f ? sm_M[n] + __log2f(Ls) : -INFINITY;
+      float* ws_o = static_cast<float*>(a.ws) + (size_t(slot_index) * ROWS + col) * D + d0;
+      reinterpret_cast<float4*>(ws_o)[0] = make_float4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+      reinterpret_cast<float4*>(ws_o)[1] = make_float4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
+      if (d0 == 0) {
+        float* ws_lse = static_cast<float*>(a.ws) + size_t(gridDim.x) * 2 * ROWS * D;
+        ws_lse[size_t(slot_index) * ROWS + col] = Ls > 0.f ? sh.M[col] + __log2f(Ls) : -INFINITY;
+      }
     }
   }
+  __syncthreads();  // LDS merge buffers are reused by the next segment
+}
 
-  // ---- append the window K/V (positions L .. L+w-1) from the last chunk ----
-  if (split == nsplit - 1) {
+template <int D, int NBMAX>
+__global__ __launch_bounds__(kThreads, 1) void attn_sk_kernel(AttnArgs a) {
+  __shared__ SkShared<D, NBMAX> sh;
+  build_table(a, sh.tab, blockIdx.x == 0);
+  const int B = a.B, P = gridDim.x, W = sh.tab.pre[B];
+  if (W == 0) return;
+  const int x0 = share_lo(W, P, blockIdx.x), x1 = share_lo(W, P, blockIdx.x + 1);
+  const int G = a.Hq / a.Hkv;
+  for (int x = x0; x < x1;) {
+    const int b = find_req(sh.tab, B, x);
+    const int nt = sh.tab.nt[b], span = seg_span(nt);
+    const int rel = x - sh.tab.pre[b];
+    const int g = rel / span;
+    const int seg_w0 = sh.tab.pre[b] + g * span, seg_w1 = seg_w0 + span;
+    const int t0 = max(0, rel - g * span - kSegCost);
+    const int t_end = max(0, min(x1, seg_w1) - seg_w0 - kSegCost);
+    if (t_end > t0) {
+      const int n = t_end - t0;
+      const bool full = (t0 == 0 && t_end == nt);
+      const int slot = blockIdx.x * 2 + (x0 < seg_w0 ? 1 : 0);
+      const int cols = sh.tab.w[b] * G;
+      if (cols <= 16) run_segment<D, 1, NBMAX>(a, sh, b, g, t0, n, full, slot);
+      else if (cols <= 32) run_segment<D, (NBMAX >= 2 ? 2 : 1), NBMAX>(a, sh, b, g, t0, n, full, slot);
+      else run_segment<D, NBMAX, NBMAX>(a, sh, b, g, t0, n, full, slot);
+    }
+    x = min(x1, seg_w1);
+  }
+}
+
+// Appends each segment's window K/V to the cache, combines the partials of segments cut by
+// share boundaries, and zero-fills output rows [M, tier).  Blocks [0, B*Hkv) handle one
+// segment each, the rest zero-fill.  Every load of
+// a thread is independent of its others (partials are read four at a time), so a merge
+// costs about one memory round trip.
+template <int D, int NBMAX>
+__global__ __launch_bounds__(kThreads) void attn_merge_kernel(AttnArgs a, int P, int merge_blocks, int pad_blocks) {
+  constexpr int ROWS = NBMAX * 16;
+  __shared__ int red[kThreads / kWave][2];
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  if (int(blockIdx.x) >= merge_blocks) {
+    const int M = max(a.total_tier[0], 0);
+    const int tier = min(a.total_tier[1], a.max_rows);
+    const size_t row_elems = size_t(a.Hq) * D;
+    for (int r = M + int(blockIdx.x) - merge_blocks; r < tier; r += pad_blocks) {
+      uint4* o = reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + size_t(r) * row_elems);
+      for (size_t k = tid; k < row_elems / 8; k += kThreads) o[k] = make_uint4(0, 0, 0, 0);
+    }
+    return;
+  }
+  const int b = blockIdx.x / a.Hkv, g = blockIdx.x % a.Hkv;
+  // tile counts: this request's, all requests', and those before b (same rule as the main kernel)
+  int all = 0, before = 0;
+  for (int r = tid; r < a.B; r += kThreads) {
+    const ReqInfo ri = req_info(a, r, false);
+    const int span = seg_span(ri.ok ? (ri.L + ri.w + kTile - 1) / kTile : 0);
+    all += span;
+    before += r < b ? span : 0;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    all += __shfl_xor(all, o);
+    before += __shfl_xor(before, o);
+  }
+  if (lane == 0) {
+    red[wave][0] = all;
+    red[wave][1] = before;
+  }
+  __syncthreads();
+  all = 0;
+  before = 0;
+#pragma unroll
+  for (int v = 0; v < kThreads / kWave; ++v) {
+    all += red[v][0];
+    before += red[v][1];
+  }
+  const ReqInfo ri = req_info(a, b, false);
+  if (!ri.ok) return;
+  // append the window's K/V to the cache at positions L .. L+w-1 (the attention kernel,
+  // which has finished, took these keys from k_new / v_new)
+  {
+    const int Hkv = a.Hkv, P = a.page_size;
+    const uint16_t* kn = static_cast<const uint16_t*>(a.k_new);
+    const uint16_t* vn = static_cast<const uint16_t*>(a.v_new);
     uint16_t* kcw = static_cast<uint16_t*>(a.k_cache);
     uint16_t* vcw = static_cast<uint16_t*>(a.v_cache);
-    for (int idx = tid; idx < w * D; idx += kAttnThreads) {
-      const int j = idx / D, d = idx % D;
-      const int p = L + j;
+    for (int idx = tid; idx < ri.w * D; idx += kThreads) {
+      const int j = idx / D, d = idx % D, p = ri.L + j;
       bool badp = false;
       const int pg = page_of(a, b, p, badp);
       if (pg < 0) {
         flag(a.status, RVA_DEV_BAD_PAGE);
         continue;
       }
-      const size_t src = (size_t(r0 + j) * Hkv + g) * D + d;
+      const size_t src = (size_t(ri.r0 + j) * Hkv + g) * D + d;
       kcw[((size_t(pg) * Hkv + g) * P + p % P) * D + d] = kn[src];
-      vcw[((size_t(pg) * Hkv + g) * D + d) * P + p % P] = vn[src];
+      vcw[v_index(pg, g, Hkv, P, D, p % P, d)] = vn[src];
     }
   }
-}
-
-// Merges the per-chunk partials of every (request, kv head) with more than one chunk, and
-// zero-fills output rows [M, tier).  Blocks [0, B*Hkv) merge, the rest zero-fill.
-template <typename T, int D>
-__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, int max_splits, int rows_cap,
-                                                           int merge_blocks, int pad_blocks) {
-  __shared__ float sm_M[64];
-  __shared__ float sm_inv[64];
-  const int tid = threadIdx.x;
-  if (int(blockIdx.x) >= merge_blocks) {
-    const int M = max(a.total_tier[0], 0);
-    const int tier = min(a.total_tier[1], a.max_rows);
-    const size_t row_elems = size_t(a.Hq) * D;
-    for (int r = M + int(blockIdx.x) - merge_blocks; r < tier; r += pad_blocks) {
-      T* o = static_cast<T*>(a.out) + size_t(r) * row_elems;
-      for (size_t k = tid; k < row_elems; k += 256) Elem<T>::store(o, k, 0.f);
-    }
-    return;
-  }
-  if (rows_cap == 0) return;  // single-pass kernels wrote every output
-  const int b = blockIdx.x / a.Hkv, g = blockIdx.x % a.Hkv;
-  const ReqInfo ri = req_info(a, b, false);
-  if (!ri.ok) return;
-  const int Lw = ri.L + ri.w;
-  const int nsplit = (Lw + kChunk - 1) / kChunk;
-  if (nsplit <= 1) return;
+  const int span = seg_span((ri.L + ri.w + kTile - 1) / kTile);
+  const int W = all * a.Hkv;
+  const int seg_w0 = before * a.Hkv + g * span, seg_w1 = seg_w0 + span;
+  const int pa = share_owner(W, P, seg_w0 + kSegCost), pb = share_owner(W, P, seg_w1 - 1);
+  if (pa == pb) return;  // finished inside one share
   const int G = a.Hq / a.Hkv, nq = ri.w * G;
-  const size_t bg = size_t(b) * a.Hkv + g;
   const float* ws_o = static_cast<const float*>(a.ws);
-  const float* ws_lse = ws_o + size_t(a.B) * a.Hkv * max_splits * rows_cap * D;
-  for (int n = tid; n < nq; n += 256) {
-    float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ws_lse[(bg * max_splits + s) * rows_cap + n]);
-    float sum = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
-      const float l = ws_lse[(bg * max_splits + s) * rows_cap + n];
-      if (l != -INFINITY) sum += __builtin_amdgcn_exp2f(l - M);
+  const float* ws_lse = ws_o + size_t(P) * 2 * ROWS * D;
+  const int first_slot = pa * 2 + (share_lo(W, P, pa) < seg_w0 ? 1 : 0);  // then p * 2 for p > pa
+  for (int it = tid; it < nq * (D / 4); it += kThreads) {
+    const int col = it / (D / 4), c4 = it % (D / 4);
+    float M = -INFINITY, sum = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int p0 = pa; p0 <= pb; p0 += 4) {
+      float lse[4];
+      float4 o[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int p = min(p0 + u, pb);
+        const size_t sl = p == pa ? first_slot : size_t(p) * 2;
+        lse[u] = p0 + u <= pb ? ws_lse[sl * ROWS + col] : -INFINITY;
+        o[u] = reinterpret_cast<const float4*>(ws_o + (sl * ROWS + col) * D)[c4];
+      }
+      float m4 = M;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) m4 = fmaxf(m4, lse[u]);
+      if (m4 != -INFINITY) {
+        const float r = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - m4);
+        sum *= r;
+        acc.x *= r; acc.y *= r; acc.z *= r; acc.w *= r;
+        M = m4;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float e = lse[u] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(lse[u] - M);
+          sum += e;
+          acc.x += e * o[u].x; acc.y += e * o[u].y; acc.z += e * o[u].z; acc.w += e * o[u].w;
+        }
+      }
     }
-    sm_M[n] = M;
-    sm_inv[n] = sum > 0.f ? 1.f / sum : 0.f;
-  }
-  __syncthreads();
-  for (int idx = tid; idx < nq * D; idx += 256) {
-    const int n = idx / D, d = idx % D;
-    const float M = sm_M[n];
-    float acc = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
-      const float l = ws_lse[(bg * max_splits + s) * rows_cap + n];
-      if (l != -INFINITY) acc += __builtin_amdgcn_exp2f(l - M) * ws_o[((bg * max_splits + s) * rows_cap + n) * D + d];
-    }
-    T* o = static_cast<T*>(a.out);
-    Elem<T>::store(o, (size_t(ri.r0 + n / G) * a.Hq + g * G + n % G) * D + d, acc * sm_inv[n]);
+    const float inv = sum > 0.f ? 1.f / sum : 0.f;
+    uint16_t* out = static_cast<uint16_t*>(a.out) + (size_t(ri.r0 + col / G) * a.Hq + g * G + col % G) * D + c4 * 4;
+    const uint32_t lo16 = f32_to_bf16(acc.x * inv) | (uint32_t(f32_to_bf16(acc.y * inv)) << 16);
+    const uint32_t hi16 = f32_to_bf16(acc.z * inv) | (uint32_t(f32_to_bf16(acc.w * inv)) << 16);
+    *reinterpret_cast<uint2*>(out) = make_uint2(lo16, hi16);
   }
 }
 
@@ -409,7 +716,7 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnArgs a) {
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const ReqInfo ri = req_info(a, b, g == 0 && tid == 0);
   if (!ri.ok) return;
-  const int L = ri.L, r0 = ri.r0, w = ri.w, Lw = L + w;
+  const int L = ri.L, r0 = ri.r0, w = ri.w;
   const int G = a.Hq / a.Hkv, nq = w * G, Hkv = a.Hkv, P = a.page_size;
   const T* kc = static_cast<const T*>(a.k_cache);
   const T* vc = static_cast<const T*>(a.v_cache);
@@ -437,8 +744,8 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnArgs a) {
           const int pg = page_of(a, b, p, bad_page);
           if (pg < 0) continue;
           krow = kc + ((size_t(pg) * Hkv + g) * P + p % P) * D;
-          vbase = vc + (size_t(pg) * Hkv + g) * D * P + p % P;
-          vstride = P;
+          vbase = vc + v_index(pg, g, Hkv, P, D, p % P, 0);
+          vstride = vblk(P);
         } else {
           krow = kn + (size_t(r0 + p - L) * Hkv + g) * D;
           vbase = vn + (size_t(r0 + p - L) * Hkv + g) * D;
@@ -483,34 +790,63 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnArgs a) {
     }
     const size_t src = (size_t(r0 + j) * Hkv + g) * D + d;
     kcw[((size_t(pg) * Hkv + g) * P + p % P) * D + d] = kn[src];
-    vcw[((size_t(pg) * Hkv + g) * D + d) * P + p % P] = vn[src];
+    vcw[v_index(pg, g, Hkv, P, D, p % P, d)] = vn[src];
   }
 }
 
-int rows_for(int max_window, int G) {
+// Zero-fills output rows [M, tier) for the generic path.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void attn_pad_kernel(AttnArgs a) {
+  const int M = max(a.total_tier[0], 0);
+  const int tier = min(a.total_tier[1], a.max_rows);
+  const size_t row_elems = size_t(a.Hq) * D;
+  for (int r = M + int(blockIdx.x); r < tier; r += gridDim.x) {
+    T* o = static_cast<T*>(a.out) + size_t(r) * row_elems;
+    for (size_t k = threadIdx.x; k < row_elems; k += 256) Elem<T>::store(o, k, 0.f);
+  }
+}
+
+int nbmax_for(int max_window, int G) {
   const int r = max_window * G;
-  return r <= 16 ? 16 : r <= 32 ? 32 : 64;
+  return r <= 16 ? 1 : r <= 32 ? 2 : 4;
 }
 
-bool use_mfma(int kv_dtype, int D, int page_size, int max_window, int G) {
-  return kv_dtype == RVA_BF16 && (D == 64 || D == 128) && page_size % kTile == 0 &&
-         max_window * G <= 64;
+bool use_sk(int kv_dtype, int D, int page_size, int max_window, int G, int B) {
+  return kv_dtype == RVA_BF16 && (D == 64 || D == 128) && page_size >= kTile &&
+         (page_size & (page_size - 1)) == 0 && max_window * G <= 64 && B <= kMaxB;
 }
 
-int max_splits_for(int page_size, int max_pages) {
-  const long long cap = (long long)page_size * max_pages;
-  return int((cap + kChunk - 1) / kChunk);
+// Persistent grid: CUs x resident workgroups per CU of the current device (cached).
+template <int D, int NBMAX>
+int sk_grid() {
+  static std::mutex mu;
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!cache[dev]) {
+    int cus = 0, per = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, attn_sk_kernel<D, NBMAX>, kThreads, 0) != hipSuccess)
+      per = 0;
+    cache[dev] = (cus > 0 ? cus : 256) * (per > 0 ? per : 1);
+  }
+  return cache[dev];
 }
 
-template <int D, int NB>
-hipError_t launch_mfma(const AttnArgs& a, hipStream_t stream) {
-  const int ms = max_splits_for(a.page_size, a.max_pages);
-  hipLaunchKernelGGL((attn_mfma_kernel<D, NB>), dim3(ms, a.Hkv, a.B), dim3(kAttnThreads), 0, stream, a, ms);
+int sk_grid_for(int D, int nbmax) {
+  if (D == 128) return nbmax == 1 ? sk_grid<128, 1>() : nbmax == 2 ? sk_grid<128, 2>() : sk_grid<128, 4>();
+  return nbmax == 1 ? sk_grid<64, 1>() : nbmax == 2 ? sk_grid<64, 2>() : sk_grid<64, 4>();
+}
+
+template <int D, int NBMAX>
+hipError_t launch_sk(const AttnArgs& a, hipStream_t stream) {
+  const int P = sk_grid<D, NBMAX>();
+  hipLaunchKernelGGL((attn_sk_kernel<D, NBMAX>), dim3(P), dim3(kThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int merge = a.B * a.Hkv, pad = 32;
-  hipLaunchKernelGGL((attn_combine_kernel<uint16_t, D>), dim3(merge + pad), dim3(256), 0, stream, a, ms,
-                     NB * 16, merge, pad);
+  hipLaunchKernelGGL((attn_merge_kernel<D, NBMAX>), dim3(merge + pad), dim3(kThreads), 0, stream, a, P, merge, pad);
   return hipGetLastError();
 }
 
@@ -519,8 +855,7 @@ hipError_t launch_generic(const AttnArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((attn_generic_kernel<T, D>), dim3(a.Hkv, a.B), dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int pad = 32;
-  hipLaunchKernelGGL((attn_combine_kernel<T, D>), dim3(pad), dim3(256), 0, stream, a, 1, 0, 0, pad);
+  hipLaunchKernelGGL((attn_pad_kernel<T, D>), dim3(32), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -529,24 +864,25 @@ hipError_t launch_generic(const AttnArgs& a, hipStream_t stream) {
 size_t attention_workspace_bytes(int B, int max_window, int Hq, int Hkv, int D, int page_size,
                                  int max_pages, int kv_dtype) {
   const int G = Hq / Hkv;
-  if (!use_mfma(kv_dtype, D, page_size, max_window, G)) return 0;
-  const size_t rows = rows_for(max_window, G);
-  const size_t ms = max_splits_for(page_size, max_pages);
-  return size_t(B) * Hkv * ms * rows * (D + 1) * sizeof(float);
+  (void)max_pages;
+  if (!use_sk(kv_dtype, D, page_size, max_window, G, B)) return 0;
+  const int nbmax = nbmax_for(max_window, G);
+  const size_t P = sk_grid_for(D, nbmax);
+  return P * 2 * size_t(nbmax * 16) * (D + 1) * sizeof(float);
 }
 
 hipError_t launch_attention(const AttnArgs& a, int kv_dtype, hipStream_t stream) {
   const int G = a.Hq / a.Hkv;
-  if (use_mfma(kv_dtype, a.D, a.page_size, a.max_window, G)) {
-    const int rows = rows_for(a.max_window, G);
+  if (use_sk(kv_dtype, a.D, a.page_size, a.max_window, G, a.B)) {
+    const int nbmax = nbmax_for(a.max_window, G);
     if (a.D == 128) {
-      if (rows == 16) return launch_mfma<128, 1>(a, stream);
-      if (rows == 32) return launch_mfma<128, 2>(a, stream);
-      return launch_mfma<128, 4>(a, stream);
+      if (nbmax == 1) return launch_sk<128, 1>(a, stream);
+      if (nbmax == 2) return launch_sk<128, 2>(a, stream);
+      return launch_sk<128, 4>(a, stream);
     }
-    if (rows == 16) return launch_mfma<64, 1>(a, stream);
-    if (rows == 32) return launch_mfma<64, 2>(a, stream);
-    return launch_mfma<64, 4>(a, stream);
+    if (nbmax == 1) return launch_sk<64, 1>(a, stream);
+    if (nbmax == 2) return launch_sk<64, 2>(a, stream);
+    return launch_sk<64, 4>(a, stream);
   }
   if (kv_dtype == RVA_BF16)
     return a.D == 128 ? launch_generic<uint16_t, 128>(a, stream) : launch_generic<uint16_t, 64>(a, stream);

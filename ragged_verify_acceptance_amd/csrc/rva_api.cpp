@@ -153,6 +153,9 @@ rva_status rva_verify_attention(int B, int max_window, int max_rows, int Hq, int
   a.Hkv = Hkv;
   a.D = D;
   a.page_size = page_size;
+  a.log2_page = -1;
+  for (int lp = 0; lp < 31; ++lp)
+    if ((1 << lp) == page_size) a.log2_page = lp;
   a.num_pages = num_pages;
   a.max_pages = max_pages;
   a.q = q;

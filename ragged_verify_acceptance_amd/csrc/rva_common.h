@@ -77,6 +77,7 @@ hipError_t launch_pack(int B, int gamma, const int32_t* windows, const int32_t* 
 
 struct AttnArgs {
   int B, max_window, max_rows, Hq, Hkv, D, page_size, num_pages, max_pages;
+  int log2_page;  // log2(page_size) when it is a power of two, else -1
   const void* q;
   const void* k_new;
   const void* v_new;

@@ -40,7 +40,8 @@ def sub_pool(inp: Inputs, reqs):
     local = {p: i for i, p in enumerate(sorted(pages))}
     P = len(local)
     k_pool = np.full((P, wl.Hkv, wl.page, wl.D), np.nan)
-    v_pool = np.full((P, wl.Hkv, wl.D, wl.page), np.nan)
+    VB = oracle.attention.v_block(wl.page)
+    v_pool = np.full((P, wl.Hkv, wl.page // VB, wl.D, VB), np.nan)
     bt = np.zeros((len(reqs), inp.max_pages), np.int32)
     for j, b in enumerate(reqs):
         K, V = inp.request_context_kv(b)
@@ -53,7 +54,8 @@ def sub_pool(inp: Inputs, reqs):
             lo, hi = pj * wl.page, min(L, (pj + 1) * wl.page)
             if hi > lo:
                 k_pool[lp, :, : hi - lo, :] = K[lo:hi].transpose(1, 0, 2)
-                v_pool[lp, :, :, : hi - lo] = V[lo:hi].transpose(1, 2, 0)
+                for s0 in range(lo, hi):
+                    v_pool[lp, :, (s0 - lo) // VB, :, (s0 - lo) % VB] = V[s0]
     return k_pool, v_pool, bt, local
 
 

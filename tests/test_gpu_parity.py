@@ -142,7 +142,8 @@ def test_attention(ds):
             pg = int(inp.block_table[b, p // wl.page])
             s = p % wl.page
             assert np.array_equal(kc[pg, :, s, :].float().cpu().numpy(), app[b][0][i])
-            assert np.array_equal(vc[pg, :, :, s].float().cpu().numpy(), app[b][1][i])
+            VB = vc.shape[4]
+            assert np.array_equal(vc[pg, :, s // VB, :, s % VB].float().cpu().numpy(), app[b][1][i])
 
 
 def _accept_compare(ds, name, windows, reqs, labels_on=True):

@@ -246,7 +246,8 @@ def _paged_case(rng, B=3, Hq=4, Hkv=2, D=16, page=4, lens=(0, 5, 9), windows=(3,
         k_new=rng.standard_normal((R, Hkv, D)),
         v_new=rng.standard_normal((R, Hkv, D)),
         k_cache=rng.standard_normal((P, Hkv, page, D)),
-        v_cache=rng.standard_normal((P, Hkv, D, page)),
+        v_cache=rng.standard_normal((P, Hkv, page // oracle.attention.v_block(page), D,
+                                     oracle.attention.v_block(page))),
         block_table=bt,
         context_lens=np.array(lens, np.int32),
         cu_seqlens=cu,
@@ -264,17 +265,21 @@ def _logical_kv(case, b, g):
     V = np.zeros((L, D))
     for p in range(L):
         K[p] = case["k_cache"][case["block_table"][b, p // page], g, p % page]
-        V[p] = case["v_cache"][case["block_table"][b, p // page], g, :, p % page]
+        VB = case["v_cache"].shape[4]
+        s = p % page
+        V[p] = case["v_cache"][case["block_table"][b, p // page], g, s // VB, :, s % VB]
     return K, V
 
 
-def test_attention_against_torch_sdpa():
+@pytest.mark.parametrize("page,lens", [(4, (0, 5, 9)), (64, (0, 70, 131))])
+def test_attention_against_torch_sdpa(page, lens):
     """Library special case: per request, masked scaled-dot-product attention from
     torch (float64, CPU) over [context ; window] with a causal window mask.  Catches a
     wrong scale, a missing causal mask, a mask that lets a row see later window rows,
-    and a wrong GQA group mapping."""
+    a wrong GQA group mapping, and a wrong slot -> V column-block mapping (page 64
+    holds two 32-slot blocks)."""
     rng = np.random.default_rng(11)
-    case = _paged_case(rng)
+    case = _paged_case(rng, page=page, lens=lens)
     out, _, _ = oracle.verify_attention(**case)
     Hq, Hkv = case["q"].shape[1], case["k_new"].shape[1]
     for b in range(3):
@@ -354,7 +359,8 @@ def test_attention_causal_and_append():
             p = L + i
             pg, s = case["block_table"][bb, p // page], p % page
             assert np.array_equal(kc[pg, :, s, :], case["k_new"][rr + i])
-            assert np.array_equal(vc[pg, :, :, s], case["v_new"][rr + i])
+            VB = vc.shape[4]
+            assert np.array_equal(vc[pg, :, s // VB, :, s % VB], case["v_new"][rr + i])
             touched.add((int(pg), s))
     for pg in range(case["k_cache"].shape[0]):
         for s in range(page):

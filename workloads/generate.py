@@ -167,11 +167,17 @@ class Inputs:
         return ua, ur
 
 
+def v_block(page: int) -> int:
+    """Column-block width of the V cache layout (32 slots, or the page if not a multiple of 32)."""
+    return 32 if page % 32 == 0 else page
+
+
 def paged_cache(inp: Inputs, fill_unused=float("nan"), requests=None):
     """Host page pools in the library's layout, filled with each request's context.
 
     k_pool [num_pages, Hkv, page, D] (element (page, g, slot, d)), v_pool
-    [num_pages, Hkv, D, page] (element (page, g, d, slot)).  Slots that hold no context
+    [num_pages, Hkv, page // VB, D, VB] (element (page, g, slot // VB, d, slot % VB), VB = 32
+    when page is a multiple of 32, else the page).  Slots that hold no context
     position (the tail of each request's last pages) are set to ``fill_unused`` so that a
     kernel reading them would be noticed.  ``requests`` limits the fill to a subset.
     """
@@ -179,7 +185,8 @@ def paged_cache(inp: Inputs, fill_unused=float("nan"), requests=None):
     dt = _TORCH[wl.kv_dtype]
     P = inp.num_pages
     k_pool = torch.full((P, wl.Hkv, wl.page, wl.D), fill_unused, dtype=dt)
-    v_pool = torch.full((P, wl.Hkv, wl.D, wl.page), fill_unused, dtype=dt)
+    VB = v_block(wl.page)
+    v_pool = torch.full((P, wl.Hkv, wl.page // VB, wl.D, VB), fill_unused, dtype=dt)
     reqs = range(inp.B) if requests is None else requests
     for b in reqs:
         K, V = inp.request_context_kv(b)
@@ -188,5 +195,7 @@ def paged_cache(inp: Inputs, fill_unused=float("nan"), requests=None):
             pg = int(inp.block_table[b, j])
             lo, hi = j * wl.page, min(L, (j + 1) * wl.page)
             k_pool[pg, :, : hi - lo, :] = K[lo:hi].permute(1, 0, 2)
-            v_pool[pg, :, :, : hi - lo] = V[lo:hi].permute(1, 2, 0)
+            for s0 in range(lo, hi, VB):
+                s1 = min(hi, s0 + VB)
+                v_pool[pg, :, (s0 - lo) // VB, :, : s1 - s0] = V[s0:s1].permute(1, 2, 0)
     return k_pool, v_pool
