@@ -6,35 +6,94 @@
 // section 07 (label c* = 1 - 0.5 ||p_d - p_t||_1); "DFlash 到 DSpark in SGLang" section
 // "Background" (each verify forward also yields one target token).
 //
-// Rows are split into segments of kSeg vocabulary entries; every kernel below is a grid
-// over (segment, row or request) so that hundreds of rows spread over all CUs.
-//   stats_kernel   per (row, segment): exact max, and sum of exp(x - max) (float32 exp,
-//                  float64 accumulation).  One HBM pass over every active row.
-//   tv_kernel      per (draft pair, segment): row normalisers from the segment stats,
-//                  then sum over the segment of max(0, p_t - p_d) in float64 (= the
-//                  segment's share of the TV distance).  Only launched when labels are
-//                  requested.
-//   decide_kernel  one wave per request, one lane per draft: p_t(x), p_d(x) with a float64
-//                  exp at the drafted token, accept bits, first rejection by ballot;
-//                  labels = 1 - sum of the TV shares; records which row pair to draw from.
-//   draw_sum_kernel / draw_q_kernel / draw_pick_kernel: the residual or bonus draw in
-//                  float64 throughout (exp and sums), because its result is an index that
-//                  must match a float64 definition bit for bit: first the two float64
-//                  normalisers, then per-segment masses of the draw weights, then one
-//                  workgroup per request locates the segment holding u * S and scans it.
-//                  The pick kernel also commits (accept_len, committed, context_lens).
+// Rows are cut into segments of kSeg vocabulary entries (32 KB of bf16).  Four kernels:
+//   stats_kernel    grid (segment, row): exact max m_s and sum of exp(x - m_s) of every
+//                   active row (float32 exp2, float32 runs of 8, float64 accumulation).  The
+//                   one full HBM pass over the logits.
+//   decide_kernel   one workgroup per request: row normalisers (max M, sum S) of the
+//                   request's rows from the segment stats, p_t(x) and p_d(x) at the drafted
+//                   tokens in float64, accept bits, first rejection, which rows the draw uses.
+//   pair_kernel     grid (segment, slot).  Draw slots (one per request, dispatched first):
+//                   float64 sums over the draw rows (target row n, and draft row n for a
+//                   residual draw) of e_t = exp(x_t - M_t), e_d = exp(x_d - M_d), and of the
+//                   unnormalised residual max(0, e_t - rho' e_d) with the draft entries it
+//                   keeps, at rho' = S_t / S_d from the float32-accurate stats.  Pair slots:
+//                   the segment's share of the TV distance sum max(0, p_t - p_d) (float32
+//                   terms, float64 sum) of every other draft pair.
+//   pick_kernel     one workgroup per request: labels = 1 - TV; the exact ratio
+//                   rho = S_t / S_d from the float64 sums corrects each segment's residual
+//                   mass to first order, A(rho) = A(rho') - (rho - rho') D (exact up to the
+//                   entries whose sign differs between rho' and rho, a second-order term);
+//                   u * Q locates the segment, which is rescanned with exact weights
+//                   max(0, e_t - rho e_d) and a block-wide prefix sum; then the commit
+//                   (accept_len, committed, context_lens).
+// The draw returns an index that has to agree with a float64 definition, so everything the
+// draw reads is float64: exp is 2^y by range reduction and a degree-13 Taylor polynomial of
+// 2^f on |f| <= 1/2 (truncation < 2e-16).
 #include "rva_common.h"
 
 namespace rva {
 namespace {
 
-constexpr int kSeg = 8192;
-constexpr int kThreads = 256;
-constexpr int kPer = kSeg / kThreads;  // elements per thread per segment
+constexpr int kSeg = 16384;
+constexpr int kThreads = 256;          // stats pass
+constexpr int kPer = kSeg / kThreads;  // entries per thread per segment in the stats pass
+constexpr int kWideThreads = 512;      // float64 passes (draw sums, pair pass)
+constexpr int kWidePer = kSeg / kWideThreads;
+constexpr int kPickThreads = 512;
+constexpr int kPickPer = kSeg / kPickThreads;  // consecutive entries per thread in the pick
+constexpr float kLog2e = 1.44269504088896341f;
+
+// e^(x - m) in float32 (x = -inf gives 0; m must be finite)
+__device__ __forceinline__ float exp_shift(float x, float m) {
+  return __builtin_amdgcn_exp2f((x - m) * kLog2e);
+}
+
+// Taylor coefficients ln(2)^k / k! of 2^f, k = 0..13, correctly rounded.  They travel in
+// the kernel arguments (scalar registers), so the FMAs take them as scalar operands instead of
+// rebuilding 64-bit literals in vector registers at every use.
+struct Exp2Poly {
+  double c[14];
+};
+constexpr Exp2Poly kExp2Taylor = {{
+    0x1.0000000000000p+0,  0x1.62e42fefa39efp-1,  0x1.ebfbdff82c58fp-3,  0x1.c6b08d704a0c0p-5,
+    0x1.3b2ab6fba4e77p-7,  0x1.5d87fe78a6731p-10, 0x1.430912f86c787p-13, 0x1.ffcbfc588b0c7p-17,
+    0x1.62c0223a5c824p-20, 0x1.b5253d395e7c4p-24, 0x1.e4cf5158b8ecap-28, 0x1.e8cac7351bb25p-32,
+    0x1.c3bd650fc2986p-36, 0x1.816193166d0f9p-40}};
+
+// 2^y in float64 for y <= 0: y = n + f with n = rint(y), |f| <= 1/2; 2^f from the Taylor
+// series of exp(f ln 2) to degree 13 (truncation < 2e-16), then scaled by 2^n.
+__device__ __forceinline__ double exp2_f64(const Exp2Poly& P, double y) {
+  if (!(y > -1100.0)) return 0.0;  // also maps -inf and NaN (fully masked rows) to 0
+  const double n = rint(y);
+  const double f = y - n;
+  double p = P.c[13];
+#pragma unroll
+  for (int k = 12; k >= 0; --k) p = fma(p, f, P.c[k]);
+  return ldexp(p, int(n));
+}
+constexpr double kLog2eF64 = 1.4426950408889634074;
+// e^(x - m) in float64 for float32 x <= m (x = -inf gives 0)
+__device__ __forceinline__ double exp_shift_f64(const Exp2Poly& P, float x, float m) {
+  return exp2_f64(P, (double(x) - double(m)) * kLog2eF64);
+}
+
+// Per-request decision record written by decide_kernel.
+struct Decision {
+  int n;         // accepted drafts; -1: request skipped (invalid window)
+  int id_t;      // row id of the draw's target row
+  int id_d;      // row id of the residual draw's draft row, -1 for the bonus draw
+  int pad;
+  float Mt, Md;  // maxima of those rows
+  double rho32;  // S_t / S_d from the float32-accurate segment stats
+};
+
+// Float64 per-segment sums of a draw slot: S_t, S_d, A(rho'), D (see the header).
+constexpr int kDrawSums = 4;
 
 struct WsLayout {
   int nseg, n_ids;
-  size_t off_m, off_s, off_tv, off_dec, off_r1, off_r2, total;
+  size_t off_m, off_s, off_nm, off_tv, off_dec, off_r1, total;
 };
 
 __host__ __device__ inline WsLayout ws_layout(int B, int gamma, int V, int max_rows) {
@@ -50,29 +109,26 @@ __host__ __device__ inline WsLayout ws_layout(int B, int gamma, int V, int max_r
   };
   w.off_m = take(sizeof(float) * size_t(w.n_ids) * w.nseg);
   w.off_s = take(sizeof(double) * size_t(w.n_ids) * w.nseg);
+  w.off_nm = take(sizeof(float2) * size_t(w.n_ids));
   w.off_tv = take(sizeof(double) * size_t(B) * G1 * w.nseg);
-  w.off_dec = take(sizeof(int) * size_t(B) * 4);
-  w.off_r1 = take(sizeof(double) * size_t(B) * w.nseg * 2);
-  w.off_r2 = take(sizeof(double) * size_t(B) * w.nseg);
+  w.off_dec = take(sizeof(Decision) * size_t(B));
+  w.off_r1 = take(sizeof(double) * size_t(B) * w.nseg * kDrawSums);
   w.total = off;
   return w;
 }
 
+// Row ids: target row r (packed row index) is id r; draft row (b, k) is id max_rows + b*G1 + k.
 struct Ctx {
   AcceptArgs a;
+  Exp2Poly P;
   WsLayout L;
-  float* st_m;
-  double* st_s;
-  double* tv;
-  int* dec;
-  double* r1;
-  double* r2;
+  float* st_m;    // [n_ids][nseg] segment maxima
+  double* st_s;   // [n_ids][nseg] segment sums of exp(x - m_s)
+  float2* nm;     // [n_ids] (row max, 1 / row sum) of the rows decide_kernel covered
+  double* tv;     // [B*G1][nseg] TV shares
+  Decision* dec;  // [B]
+  double* r1;     // [B][nseg][kDrawSums] float64 sums of the draw slots
 };
-
-__device__ __forceinline__ int window_of(const Ctx& c, int b) {
-  const int w = c.a.cu[b + 1] - c.a.cu[b];
-  return w < 1 ? 1 : (w > c.a.gamma ? c.a.gamma : w);
-}
 
 // Request b's packed rows [cu[b], cu[b] + w) lie inside [0, max_rows) and w in [1, gamma].
 __device__ __forceinline__ bool req_ok(const Ctx& c, int b) {
@@ -86,57 +142,116 @@ __device__ __forceinline__ const T* row_ptr(const Ctx& c, int id) {
   return static_cast<const T*>(c.a.draft) + size_t(id - c.a.max_rows) * c.a.V;
 }
 
-// Loads this thread's kPer elements of segment `seg` (as float; -inf past the row end).
-template <typename T>
-__device__ __forceinline__ void load_seg(const T* row, int V, int seg, float (&x)[kPer]) {
-  const int base = seg * kSeg;
-  if constexpr (sizeof(T) == 2) {
+// A thread's share (kSeg / NT entries) of one segment, interleaved in 16-byte groups across
+// the NT threads of the block and kept as loaded: bf16 as packed pairs (half the registers of
+// float32), float32 as is.  Entries past the row end read as -inf.  Any fixed assignment of
+// entries to (thread, i) serves the sums; rows of the same V get the same one.
+template <typename T, int NT>
+struct SegData;
+
+template <int NT>
+struct SegData<uint16_t, NT> {
+  static constexpr int P = kSeg / NT;
+  uint32_t w[P / 2];
+  __device__ __forceinline__ float operator[](int i) const {
+    return (i & 1) ? __uint_as_float(w[i >> 1] & 0xffff0000u) : __uint_as_float(w[i >> 1] << 16);
+  }
+  __device__ __forceinline__ void load(const uint16_t* row, int V, int seg) {
+    constexpr uint32_t kNegInf2 = 0xff80ff80u;  // two bf16 -inf
+    const int base = seg * kSeg;
     if (V % 8 == 0) {
 #pragma unroll
-      for (int i = 0; i < kPer / 8; ++i) {
-        const int v = base + (i * kThreads + int(threadIdx.x)) * 8;
+      for (int i = 0; i < P / 8; ++i) {
+        const int v = base + (i * NT + int(threadIdx.x)) * 8;
         if (v < V) {
           const uint4 u = *reinterpret_cast<const uint4*>(row + v);
-          const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            x[i * 8 + 2 * j] = __uint_as_float(w[j] << 16);
-            x[i * 8 + 2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
-          }
+          w[4 * i] = u.x;
+          w[4 * i + 1] = u.y;
+          w[4 * i + 2] = u.z;
+          w[4 * i + 3] = u.w;
         } else {
+          w[4 * i] = w[4 * i + 1] = w[4 * i + 2] = w[4 * i + 3] = kNegInf2;
+        }
+      }
+    } else {
 #pragma unroll
-          for (int j = 0; j < 8; ++j) x[i * 8 + j] = -INFINITY;
+      for (int i = 0; i < P / 2; ++i) {
+        const int v = base + (i * NT + int(threadIdx.x)) * 2;
+        const uint32_t lo = v < V ? row[v] : 0xff80u;
+        const uint32_t hi = v + 1 < V ? row[v + 1] : 0xff80u;
+        w[i] = lo | (hi << 16);
+      }
+    }
+  }
+};
+
+template <int NT>
+struct SegData<float, NT> {
+  static constexpr int P = kSeg / NT;
+  float f[P];
+  __device__ __forceinline__ float operator[](int i) const { return f[i]; }
+  __device__ __forceinline__ void load(const float* row, int V, int seg) {
+    const int base = seg * kSeg;
+    if (V % 4 == 0) {
+#pragma unroll
+      for (int i = 0; i < P / 4; ++i) {
+        const int v = base + (i * NT + int(threadIdx.x)) * 4;
+        if (v < V) {
+          const float4 u = *reinterpret_cast<const float4*>(row + v);
+          f[4 * i] = u.x;
+          f[4 * i + 1] = u.y;
+          f[4 * i + 2] = u.z;
+          f[4 * i + 3] = u.w;
+        } else {
+          f[4 * i] = f[4 * i + 1] = f[4 * i + 2] = f[4 * i + 3] = -INFINITY;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < P; ++i) {
+        const int v = base + i * NT + int(threadIdx.x);
+        f[i] = v < V ? row[v] : -INFINITY;
+      }
+    }
+  }
+};
+
+// kPickPer consecutive entries starting at v0 (-inf past the row end).
+template <typename T>
+__device__ __forceinline__ void load_run(const T* row, int V, int v0, float (&x)[kPickPer]) {
+  if constexpr (sizeof(T) == 2) {
+    if (V % 8 == 0 && v0 + kPickPer <= V) {
+#pragma unroll
+      for (int i = 0; i < kPickPer / 8; ++i) {
+        const uint4 u = *reinterpret_cast<const uint4*>(row + v0 + 8 * i);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          x[i * 8 + 2 * j] = __uint_as_float(w[j] << 16);
+          x[i * 8 + 2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
         }
       }
       return;
     }
   } else {
-    if (V % 4 == 0) {
+    if (V % 4 == 0 && v0 + kPickPer <= V) {
 #pragma unroll
-      for (int i = 0; i < kPer / 4; ++i) {
-        const int v = base + (i * kThreads + int(threadIdx.x)) * 4;
-        if (v < V) {
-          const float4 u = *reinterpret_cast<const float4*>(row + v);
-          x[i * 4] = u.x;
-          x[i * 4 + 1] = u.y;
-          x[i * 4 + 2] = u.z;
-          x[i * 4 + 3] = u.w;
-        } else {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) x[i * 4 + j] = -INFINITY;
-        }
+      for (int i = 0; i < kPickPer / 4; ++i) {
+        const float4 u = *reinterpret_cast<const float4*>(row + v0 + 4 * i);
+        x[i * 4] = u.x;
+        x[i * 4 + 1] = u.y;
+        x[i * 4 + 2] = u.z;
+        x[i * 4 + 3] = u.w;
       }
       return;
     }
   }
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int v = base + i * kThreads + int(threadIdx.x);
-    x[i] = v < V ? Elem<T>::load(row, v) : -INFINITY;
-  }
+  for (int i = 0; i < kPickPer; ++i) x[i] = v0 + i < V ? Elem<T>::load(row, v0 + i) : -INFINITY;
 }
 
-__device__ float block_max(float v, float* sm) {
+template <int NT>
+__device__ __forceinline__ float block_max(float v, float* sm) {
   v = wave_max(v);
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   __syncthreads();
@@ -144,12 +259,14 @@ __device__ float block_max(float v, float* sm) {
   __syncthreads();
   float r = sm[0];
 #pragma unroll
-  for (int i = 1; i < kThreads / kWave; ++i) r = fmaxf(r, sm[i]);
+  for (int i = 1; i < NT / kWave; ++i) r = fmaxf(r, sm[i]);
   return r;
 }
 
-// float64 sum in a fixed order (wave tree, then the 4 wave totals in order).
-__device__ double block_sum_f64(double v, double* sm) {
+// float64 sum in a fixed order (wave butterfly, then the wave totals in order); every thread
+// receives the same value.
+template <int NT>
+__device__ __forceinline__ double block_sum_f64(double v, double* sm) {
   v = wave_sum_f64(v);
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   __syncthreads();
@@ -157,29 +274,39 @@ __device__ double block_sum_f64(double v, double* sm) {
   __syncthreads();
   double r = sm[0];
 #pragma unroll
-  for (int i = 1; i < kThreads / kWave; ++i) r += sm[i];
+  for (int i = 1; i < NT / kWave; ++i) r += sm[i];
   return r;
 }
 
-// Row normaliser from the segment stats: exact max, and S = sum_s s_s * exp(m_s - max).
-__device__ __forceinline__ void row_norm(const Ctx& c, int id, float& M, double& S) {
-  const int nseg = c.L.nseg;
-  float m = -INFINITY;
-  for (int s = 0; s < nseg; ++s) m = fmaxf(m, c.st_m[size_t(id) * nseg + s]);
-  double acc = 0.0;
-  for (int s = 0; s < nseg; ++s) {
-    const float ms = c.st_m[size_t(id) * nseg + s];
-    if (ms != -INFINITY) acc += c.st_s[size_t(id) * nseg + s] * exp(double(ms) - double(m));
+// Draw-row totals S_t, S_d over all segments: one wave, lanes over segments, butterfly sum
+// (every lane gets the same value).
+__device__ __forceinline__ void draw_totals(const Ctx& c, int b, double& St, double& Sd) {
+  const int lane = threadIdx.x % kWave;
+  double st = 0.0, sd = 0.0;
+  for (int s = lane; s < c.L.nseg; s += kWave) {
+    const double* r = c.r1 + (size_t(b) * c.L.nseg + s) * kDrawSums;
+    st += r[0];
+    sd += r[1];
   }
-  M = m;
-  S = acc;
+  St = wave_sum_f64(st);
+  Sd = wave_sum_f64(sd);
 }
 
-__device__ __forceinline__ bool id_active(const Ctx& c, int id, int M_rows) {
-  if (id < c.a.max_rows) return id < M_rows;
+// Draw mass of segment s: the residual A(rho) (first-order corrected, clamped at 0) or the
+// target mass S_t of the segment (bonus draw and the all-zero-residual fallback).
+__device__ __forceinline__ double seg_mass(const Ctx& c, int b, int s, bool residual, double drho) {
+  const double* r = c.r1 + (size_t(b) * c.L.nseg + s) * kDrawSums;
+  if (!residual) return r[0];
+  const double m = r[2] - drho * r[3];
+  return m > 0.0 ? m : 0.0;
+}
+
+// ------------------------------------------------------------------ stats
+__device__ __forceinline__ bool id_active(const Ctx& c, int id) {
+  if (id < c.a.max_rows) return id < c.a.cu[c.a.B];
   const int j = id - c.a.max_rows, G1 = c.a.gamma - 1;
   const int b = j / G1, k = j % G1;
-  return req_ok(c, b) && k < window_of(c, b) - 1;
+  return req_ok(c, b) && k < c.a.cu[b + 1] - c.a.cu[b] - 1;
 }
 
 template <typename T>
@@ -187,322 +314,350 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(Ctx c) {
   __shared__ float smf[kThreads / kWave];
   __shared__ double smd[kThreads / kWave];
   const int seg = blockIdx.x, id = blockIdx.y;
-  const int M_rows = c.a.cu[c.a.B];
-  if (!id_active(c, id, M_rows)) return;
-  float x[kPer];
-  load_seg<T>(row_ptr<T>(c, id), c.a.V, seg, x);
+  if (!id_active(c, id)) return;
+  SegData<T, kThreads> x;
+  x.load(row_ptr<T>(c, id), c.a.V, seg);
   float m = -INFINITY;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) m = fmaxf(m, x[i]);
-  m = block_max(m, smf);
+  m = block_max<kThreads>(m, smf);
+  const float ms = m == -INFINITY ? 0.f : m;  // fully masked segment: every term is 0
   double s = 0.0;
 #pragma unroll
-  for (int i = 0; i < kPer; ++i)
-    if (x[i] != -INFINITY) s += double(expf(x[i] - m));
-  s = block_sum_f64(s, smd);
+  for (int i = 0; i < kPer; i += 8) {
+    float run = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) run += exp_shift(x[i + j], ms);
+    s += double(run);
+  }
+  s = block_sum_f64<kThreads>(s, smd);
   if (threadIdx.x == 0) {
     c.st_m[size_t(id) * c.L.nseg + seg] = m;
     c.st_s[size_t(id) * c.L.nseg + seg] = s;
   }
 }
 
-template <typename T>
-__global__ __launch_bounds__(kThreads) void tv_kernel(Ctx c) {
-  __shared__ double smd[kThreads / kWave];
-  __shared__ float sM[2];
-  __shared__ double sInv[2];
-  const int seg = blockIdx.x, j = blockIdx.y;
-  const int G1 = c.a.gamma - 1;
-  const int b = j / G1, kk = j % G1;
-  if (!req_ok(c, b) || kk >= window_of(c, b) - 1) return;
-  const int id_t = c.a.cu[b] + kk;
-  const int id_d = c.a.max_rows + j;
-  if (threadIdx.x < 2) {
-    float M;
-    double S;
-    row_norm(c, threadIdx.x == 0 ? id_t : id_d, M, S);
-    sM[threadIdx.x] = M;
-    sInv[threadIdx.x] = 1.0 / S;
-  }
-  __syncthreads();
-  float xt[kPer], xd[kPer];
-  load_seg<T>(row_ptr<T>(c, id_t), c.a.V, seg, xt);
-  load_seg<T>(row_ptr<T>(c, id_d), c.a.V, seg, xd);
-  const float Mt = sM[0], Md = sM[1];
-  const double it = sInv[0], id = sInv[1];
-  double acc = 0.0;
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    if (xt[i] == -INFINITY && xd[i] == -INFINITY) continue;
-    const double pt = double(expf(xt[i] - Mt)) * it;
-    const double pd = double(expf(xd[i] - Md)) * id;
-    acc += pt > pd ? pt - pd : 0.0;
-  }
-  acc = block_sum_f64(acc, smd);
-  if (threadIdx.x == 0) c.tv[size_t(j) * c.L.nseg + seg] = acc;
+// ------------------------------------------------------------------ decide
+constexpr int kDecideThreads = 512;
+
+// Row rr of request b in decide order: target rows 0..w-1, then draft rows 0..w-2.
+__device__ __forceinline__ int decide_row_id(const Ctx& c, int b, int r0, int w, int rr) {
+  return rr < w ? r0 + rr : c.a.max_rows + b * (c.a.gamma - 1) + (rr - w);
 }
 
-// One wave per request.  commit == false: labels only.
 template <typename T>
-__global__ __launch_bounds__(kThreads) void decide_kernel(Ctx c, int with_labels, int commit) {
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int b = blockIdx.x * (kThreads / kWave) + wave;
-  if (b >= c.a.B) return;
+__global__ __launch_bounds__(kDecideThreads) void decide_kernel(Ctx c, int commit) {
+  __shared__ float sM[2 * 64];
+  __shared__ double sS[2 * 64];
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int G1 = c.a.gamma - 1;
   if (!req_ok(c, b)) {
-    if (lane == 0) {
+    if (tid == 0) {
       flag(c.a.status, RVA_DEV_BAD_WINDOW);
-      if (commit) c.dec[size_t(b) * 4 + 1] = -1;  // nothing to draw or commit
+      if (commit) c.dec[b].n = -1;
     }
     return;
   }
-  const int w = window_of(c, b);
-  const float qnan = __int_as_float(0x7fc00000);
-  bool reject = false;
-  for (int kk = lane; kk < G1; kk += kWave) {
-    const size_t o = size_t(b) * G1 + kk;
-    if (kk >= w - 1) {
-      if (c.a.labels) c.a.labels[o] = qnan;
-      if (commit && c.a.pt_at) c.a.pt_at[o] = qnan;
-      if (commit && c.a.pd_at) c.a.pd_at[o] = qnan;
-      continue;
-    }
-    if (with_labels && c.a.labels) {
-      double tv = 0.0;
-      for (int s = 0; s < c.L.nseg; ++s) tv += c.tv[o * c.L.nseg + s];
-      c.a.labels[o] = float(1.0 - tv);
-    }
-    if (!commit) continue;
-    const int id_t = c.a.cu[b] + kk, id_d = c.a.max_rows + int(o);
-    float Mt, Md;
-    double St, Sd;
-    row_norm(c, id_t, Mt, St);
-    row_norm(c, id_d, Md, Sd);
+  const int r0 = c.a.cu[b];
+  const int w = c.a.cu[b + 1] - r0;
+  // wave 0, lane k < w-1: issue the drafted token's logit loads before the stats sweep
+  float lt = 0.f, ld = 0.f, u = 0.f;
+  if (commit && wave == 0 && lane < w - 1) {
+    const size_t o = size_t(b) * G1 + lane;
     int x = c.a.tokens[o];
+    u = c.a.u_acc[o];
     if (x < 0 || x >= c.a.V) {
       flag(c.a.status, RVA_DEV_BAD_TOKEN);
       x = x < 0 ? 0 : c.a.V - 1;
     }
-    const double lt = Elem<T>::load(row_ptr<T>(c, id_t), x);
-    const double ld = Elem<T>::load(row_ptr<T>(c, id_d), x);
-    const double pt = exp(lt - double(Mt)) / St;
-    const double pd = exp(ld - double(Md)) / Sd;
-    if (c.a.pt_at) c.a.pt_at[o] = float(pt);
-    if (c.a.pd_at) c.a.pd_at[o] = float(pd);
-    const double r = pd == 0.0 ? INFINITY : pt / pd;
-    const double u = double(c.a.u_acc[o]);
-    if (!(u < (r < 1.0 ? r : 1.0))) reject = true;
+    lt = Elem<T>::load(row_ptr<T>(c, r0 + lane), x);
+    ld = Elem<T>::load(row_ptr<T>(c, c.a.max_rows + int(o)), x);
+  }
+  // row normalisers: one wave per row, lanes over segments
+  const int nrows = 2 * w - 1;
+  for (int rr = wave; rr < nrows; rr += kDecideThreads / kWave) {
+    const int id = decide_row_id(c, b, r0, w, rr);
+    const float* rm = c.st_m + size_t(id) * c.L.nseg;
+    const double* rs = c.st_s + size_t(id) * c.L.nseg;
+    float m = -INFINITY;
+    for (int s = lane; s < c.L.nseg; s += kWave) m = fmaxf(m, rm[s]);
+    m = wave_max(m);
+    double acc = 0.0;
+    for (int s = lane; s < c.L.nseg; s += kWave) acc += rs[s] * exp_shift_f64(c.P, rm[s], m);
+    acc = wave_sum_f64(acc);
+    if (lane == 0) {
+      sM[rr] = m;
+      sS[rr] = acc;
+      c.nm[id] = make_float2(m, float(1.0 / acc));
+    }
   }
   if (!commit) return;
-  // first rejected draft (lanes cover kk = lane; G1 <= 63 so one pass suffices)
+  __syncthreads();
+  if (wave != 0) return;
+  const float qnan = __int_as_float(0x7fc00000);
+  bool reject = false;
+  if (lane < G1) {
+    const size_t o = size_t(b) * G1 + lane;
+    if (lane < w - 1) {
+      const double pt = exp_shift_f64(c.P, lt, sM[lane]) / sS[lane];
+      const double pd = exp_shift_f64(c.P, ld, sM[w + lane]) / sS[w + lane];
+      if (c.a.pt_at) c.a.pt_at[o] = float(pt);
+      if (c.a.pd_at) c.a.pd_at[o] = float(pd);
+      const double r = pd == 0.0 ? INFINITY : pt / pd;
+      reject = !(double(u) < (r < 1.0 ? r : 1.0));
+    } else {
+      if (c.a.pt_at) c.a.pt_at[o] = qnan;
+      if (c.a.pd_at) c.a.pd_at[o] = qnan;
+    }
+  }
+  // first rejected draft (G1 <= 63: one lane per draft)
   const unsigned long long rej = __ballot(reject);
   const int n = rej ? __ffsll(rej) - 1 : w - 1;
   if (lane == 0) {
-    int* d = c.dec + size_t(b) * 4;
-    d[0] = n;
-    d[1] = c.a.cu[b] + n;                                   // target row of the draw
-    d[2] = n < w - 1 ? c.a.max_rows + b * G1 + n : -1;      // draft row (residual) or -1 (bonus)
+    Decision d;
+    d.n = n;
+    d.id_t = r0 + n;
+    d.id_d = n < w - 1 ? c.a.max_rows + b * G1 + n : -1;
+    d.pad = 0;
+    d.Mt = sM[n];
+    d.Md = n < w - 1 ? sM[w + n] : 0.f;
+    d.rho32 = n < w - 1 ? sS[n] / sS[w + n] : 0.0;
+    c.dec[b] = d;
   }
 }
 
-// float64 normaliser pieces of the draw rows, per segment.
-template <typename T>
-__global__ __launch_bounds__(kThreads) void draw_sum_kernel(Ctx c) {
-  __shared__ double smd[kThreads / kWave];
-  __shared__ float sM[2];
-  const int seg = blockIdx.x, b = blockIdx.y;
-  const int* d = c.dec + size_t(b) * 4;
-  const int id_t = d[1], id_d = d[2];
-  if (id_t < 0) return;
-  if (threadIdx.x < 2) {
-    const int id = threadIdx.x == 0 ? id_t : id_d;
-    float m = -INFINITY;
-    if (id >= 0)
-      for (int s = 0; s < c.L.nseg; ++s) m = fmaxf(m, c.st_m[size_t(id) * c.L.nseg + s]);
-    sM[threadIdx.x] = m;
-  }
+// ------------------------------------------------------------------ pair pass
+// Wave butterfly then wave totals in order, for N sums at once; thread 0 gets the results.
+template <int N>
+__device__ __forceinline__ void block_sums_f64(double (&v)[N], double (*sm)[N]) {
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+#pragma unroll
+  for (int q = 0; q < N; ++q) v[q] = wave_sum_f64(v[q]);
+  if (lane == 0)
+#pragma unroll
+    for (int q = 0; q < N; ++q) sm[wave][q] = v[q];
   __syncthreads();
-  float x[kPer];
-  load_seg<T>(row_ptr<T>(c, id_t), c.a.V, seg, x);
-  double st = 0.0;
+  if (threadIdx.x == 0)
 #pragma unroll
-  for (int i = 0; i < kPer; ++i)
-    if (x[i] != -INFINITY) st += exp(double(x[i]) - double(sM[0]));
-  st = block_sum_f64(st, smd);
-  double sd = 0.0;
-  if (id_d >= 0) {
-    load_seg<T>(row_ptr<T>(c, id_d), c.a.V, seg, x);
-#pragma unroll
-    for (int i = 0; i < kPer; ++i)
-      if (x[i] != -INFINITY) sd += exp(double(x[i]) - double(sM[1]));
-    sd = block_sum_f64(sd, smd);
-  }
-  if (threadIdx.x == 0) {
-    c.r1[(size_t(b) * c.L.nseg + seg) * 2] = st;
-    c.r1[(size_t(b) * c.L.nseg + seg) * 2 + 1] = sd;
-  }
-}
-
-struct DrawRow {
-  float Mt, Md;
-  double St, Sd;
-  int id_t, id_d;
-};
-
-__device__ __forceinline__ DrawRow draw_row(const Ctx& c, int b) {
-  DrawRow r;
-  const int* d = c.dec + size_t(b) * 4;
-  r.id_t = d[1];
-  r.id_d = d[2];
-  r.Mt = -INFINITY;
-  r.Md = -INFINITY;
-  r.St = 0.0;
-  r.Sd = 0.0;
-  for (int s = 0; s < c.L.nseg; ++s) {  // same order everywhere: identical values
-    r.Mt = fmaxf(r.Mt, c.st_m[size_t(r.id_t) * c.L.nseg + s]);
-    r.St += c.r1[(size_t(b) * c.L.nseg + s) * 2];
-    if (r.id_d >= 0) {
-      r.Md = fmaxf(r.Md, c.st_m[size_t(r.id_d) * c.L.nseg + s]);
-      r.Sd += c.r1[(size_t(b) * c.L.nseg + s) * 2 + 1];
+    for (int q = 0; q < N; ++q) {
+      double r = sm[0][q];
+      for (int i = 1; i < kWideThreads / kWave; ++i) r += sm[i][q];
+      v[q] = r;
     }
-  }
-  return r;
 }
 
-// Draw weight of one vocabulary entry: residual max(0, p_t - p_d), or the unnormalised
-// target weight for the bonus draw (and for the all-zero-residual fallback).
-__device__ __forceinline__ double draw_weight(const DrawRow& r, bool residual, float xt, float xd) {
-  if (xt == -INFINITY) return 0.0;
-  const double et = exp(double(xt) - double(r.Mt));
-  if (!residual) return et;
-  const double q = et / r.St - exp(double(xd) - double(r.Md)) / r.Sd;
-  return q > 0.0 ? q : 0.0;
-}
-
+// blockIdx.y < draw_slots: the draw slot of request blockIdx.y; above: draft pair
+// (blockIdx.y - draw_slots) = b*G1 + k for the labels (when per_pair).
 template <typename T>
-__global__ __launch_bounds__(kThreads) void draw_q_kernel(Ctx c) {
-  __shared__ double smd[kThreads / kWave];
-  __shared__ DrawRow sr;
-  const int seg = blockIdx.x, b = blockIdx.y;
-  if (c.dec[size_t(b) * 4 + 1] < 0) return;
-  if (threadIdx.x == 0) sr = draw_row(c, b);
-  __syncthreads();
-  const DrawRow r = sr;
-  if (r.id_d < 0) {  // bonus: the weights are exp(x - M); their segment mass is already known
-    if (threadIdx.x == 0) c.r2[size_t(b) * c.L.nseg + seg] = c.r1[(size_t(b) * c.L.nseg + seg) * 2];
+__global__ __launch_bounds__(kWideThreads) void pair_kernel(Ctx c, int draw_slots, int per_pair) {
+  __shared__ double sm[kWideThreads / kWave][kDrawSums + 1];
+  __shared__ double smd[kWideThreads / kWave];
+  const int seg = blockIdx.x, y = blockIdx.y;
+  const int G1 = c.a.gamma - 1;
+  if (y < draw_slots) {
+    const int b = y;
+    const Decision d = c.dec[b];
+    if (d.n < 0) return;
+    const bool residual = d.id_d >= 0;
+    const bool lab = per_pair && residual;  // this pair's TV share is taken here too
+    SegData<T, kWideThreads> xt, xd;
+    xt.load(row_ptr<T>(c, d.id_t), c.a.V, seg);
+    double v[kDrawSums + 1] = {0.0, 0.0, 0.0, 0.0, 0.0};
+    if (residual) {
+      xd.load(row_ptr<T>(c, d.id_d), c.a.V, seg);
+      double it = 0.0, id = 0.0;
+      if (lab) {
+        it = double(c.nm[d.id_t].y);
+        id = double(c.nm[d.id_d].y);
+      }
+#pragma unroll
+      for (int i = 0; i < kWidePer; ++i) {
+        const double et = exp_shift_f64(c.P, xt[i], d.Mt);
+        const double ed = exp_shift_f64(c.P, xd[i], d.Md);
+        v[0] += et;
+        v[1] += ed;
+        const double r = et - d.rho32 * ed;
+        if (r > 0.0) {
+          v[2] += r;
+          v[3] += ed;
+        }
+        const double g = et * it - ed * id;
+        v[4] += g > 0.0 ? g : 0.0;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kWidePer; ++i) v[0] += exp_shift_f64(c.P, xt[i], d.Mt);
+    }
+    block_sums_f64<kDrawSums + 1>(v, sm);
+    if (threadIdx.x == 0) {
+      double* r = c.r1 + (size_t(b) * c.L.nseg + seg) * kDrawSums;
+#pragma unroll
+      for (int q = 0; q < kDrawSums; ++q) r[q] = v[q];
+      if (lab) c.tv[(size_t(b) * G1 + d.n) * c.L.nseg + seg] = v[4];
+    }
     return;
   }
-  float xt[kPer], xd[kPer];
-  load_seg<T>(row_ptr<T>(c, r.id_t), c.a.V, seg, xt);
-  load_seg<T>(row_ptr<T>(c, r.id_d), c.a.V, seg, xd);
-  double q = 0.0;
+  const int j = y - draw_slots;
+  const int b = j / G1, k = j % G1;
+  if (!req_ok(c, b)) return;
+  if (k >= c.a.cu[b + 1] - c.a.cu[b] - 1) return;
+  if (draw_slots > 0) {
+    const Decision d = c.dec[b];
+    if (d.id_d >= 0 && d.n == k) return;  // done by the draw slot
+  }
+  const int id_t = c.a.cu[b] + k;
+  const int id_d = c.a.max_rows + b * G1 + k;
+  SegData<T, kWideThreads> xt, xd;
+  xt.load(row_ptr<T>(c, id_t), c.a.V, seg);
+  xd.load(row_ptr<T>(c, id_d), c.a.V, seg);
+  const float2 nt = c.nm[id_t], nd = c.nm[id_d];
+  double acc = 0.0;
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) q += draw_weight(r, true, xt[i], xd[i]);
-  q = block_sum_f64(q, smd);
-  if (threadIdx.x == 0) c.r2[size_t(b) * c.L.nseg + seg] = q;
+  for (int i = 0; i < kWidePer; i += 8) {
+    float run = 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float pt = exp_shift(xt[i + u], nt.x) * nt.y;
+      const float pd = exp_shift(xd[i + u], nd.x) * nd.y;
+      run += fmaxf(pt - pd, 0.f);
+    }
+    acc += double(run);
+  }
+  acc = block_sum_f64<kWideThreads>(acc, smd);
+  if (threadIdx.x == 0) c.tv[(size_t(b) * G1 + k) * c.L.nseg + seg] = acc;
 }
 
+// ------------------------------------------------------------------ pick + commit + labels
 template <typename T>
-__global__ __launch_bounds__(kThreads) void draw_pick_kernel(Ctx c) {
-  __shared__ DrawRow sr;
-  __shared__ double s_t, s_base;
+__global__ __launch_bounds__(kPickThreads) void pick_kernel(Ctx c, int commit) {
+  __shared__ double s_t, s_base, s_rho;
   __shared__ int s_seg, s_residual;
-  __shared__ double run_tot[kThreads];
-  __shared__ int s_y;
+  __shared__ double s_wave[kPickThreads / kWave];
+  __shared__ int s_y, s_last;
   const int b = blockIdx.x;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int G1 = c.a.gamma - 1;
   const int nseg = c.L.nseg;
-  if (c.dec[size_t(b) * 4 + 1] < 0) return;
-  if (tid == 0) {
-    sr = draw_row(c, b);
-    bool residual = sr.id_d >= 0;
-    double Q = 0.0;
-    for (int s = 0; s < nseg; ++s) Q += residual ? c.r2[size_t(b) * nseg + s] : c.r1[(size_t(b) * nseg + s) * 2];
+  if (!req_ok(c, b)) return;
+  const int w = c.a.cu[b + 1] - c.a.cu[b];
+  if (c.a.labels && tid < G1) {
+    const size_t o = size_t(b) * G1 + tid;
+    float lab = __int_as_float(0x7fc00000);
+    if (tid < w - 1) {
+      double tv = 0.0;
+      for (int s = 0; s < nseg; ++s) tv += c.tv[o * nseg + s];
+      lab = float(1.0 - tv);
+    }
+    c.a.labels[o] = lab;
+  }
+  if (!commit) return;
+  const Decision d = c.dec[b];
+  if (d.n < 0) return;
+  if (wave == 0) {
+    double St, Sd;
+    draw_totals(c, b, St, Sd);
+    bool residual = d.id_d >= 0;
+    const double rho = residual ? St / Sd : 0.0;
+    const double drho = rho - d.rho32;
+    double q = 0.0;
+    for (int s = lane; s < nseg; s += kWave) q += seg_mass(c, b, s, residual, drho);
+    double Q = wave_sum_f64(q);
     if (residual && !(Q > 0.0)) {  // residual identically zero: draw from p_t instead
       residual = false;
-      Q = 0.0;
-      for (int s = 0; s < nseg; ++s) Q += c.r1[(size_t(b) * nseg + s) * 2];
+      Q = St;
     }
     const double t = double(c.a.u_res[b]) * Q;
-    double cum = 0.0;
-    int seg = -1, last_pos = 0;
-    double base = 0.0, base_last = 0.0;
-    for (int s = 0; s < nseg; ++s) {
-      const double qs = residual ? c.r2[size_t(b) * nseg + s] : c.r1[(size_t(b) * nseg + s) * 2];
-      if (qs > 0.0) {
-        last_pos = s;
-        base_last = cum;
+    // running sum over the segments in index order, 64 segments at a time
+    int seg = -1, last_seg = 0;
+    double base = 0.0, base_last = 0.0, carry = 0.0;
+    for (int s0 = 0; s0 < nseg && seg < 0; s0 += kWave) {
+      const int s = s0 + lane;
+      const double qs = s < nseg ? seg_mass(c, b, s, residual, drho) : 0.0;
+      double inc = qs;  // inclusive scan across the wave
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const double v = __shfl_up(inc, o);
+        if (lane >= o) inc += v;
       }
-      if (seg < 0 && cum + qs > t) {
-        seg = s;
-        base = cum;
+      inc += carry;
+      const double exc = inc - qs;
+      const unsigned long long hit = __ballot(s < nseg && qs > 0.0 && inc > t);
+      const unsigned long long pos = __ballot(s < nseg && qs > 0.0);
+      if (pos) {
+        const int l = 63 - __clzll(pos);
+        last_seg = s0 + l;
+        base_last = __shfl(exc, l);
       }
-      cum += qs;
+      if (hit) {
+        const int l = __ffsll(hit) - 1;
+        seg = s0 + l;
+        base = __shfl(exc, l);
+      }
+      carry = __shfl(inc, kWave - 1);
     }
-    if (seg < 0) {  // u*Q reached the end by rounding: take the last segment with mass
-      seg = last_pos;
+    if (seg < 0) {  // u * Q reached the end by rounding: last segment with mass
+      seg = last_seg;
       base = base_last;
     }
-    s_t = t;
-    s_base = base;
-    s_seg = seg;
-    s_residual = residual;
-    s_y = 0x7fffffff;
+    if (lane == 0) {
+      s_t = t;
+      s_base = base;
+      s_seg = seg;
+      s_residual = residual;
+      s_rho = rho;
+      s_y = 0x7fffffff;
+      s_last = -1;
+    }
   }
   __syncthreads();
-  const DrawRow r = sr;
   const int seg = s_seg;
   const bool residual = s_residual;
-  // each thread owns kPer consecutive indices of the segment (index order for the scan)
-  const int v0 = seg * kSeg + tid * kPer;
-  double wgt[kPer];
-  const T* rowt = row_ptr<T>(c, r.id_t);
-  const T* rowd = residual ? row_ptr<T>(c, r.id_d) : nullptr;
+  const double rho = s_rho;
+  const int v0 = seg * kSeg + tid * kPickPer;
+  float xt[kPickPer], xd[kPickPer];
+  load_run<T>(row_ptr<T>(c, d.id_t), c.a.V, v0, xt);
+  if (residual) load_run<T>(row_ptr<T>(c, d.id_d), c.a.V, v0, xd);
+  double wgt[kPickPer];
   double tot = 0.0;
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int v = v0 + i;
-    double q = 0.0;
-    if (v < c.a.V) q = draw_weight(r, residual, Elem<T>::load(rowt, v), residual ? Elem<T>::load(rowd, v) : 0.f);
+  for (int i = 0; i < kPickPer; ++i) {
+    const double et = exp_shift_f64(c.P, xt[i], d.Mt);
+    double q = et;
+    if (residual) {
+      q = et - rho * exp_shift_f64(c.P, xd[i], d.Md);
+      q = q > 0.0 ? q : 0.0;
+    }
     wgt[i] = q;
     tot += q;
   }
-  run_tot[tid] = tot;
-  __syncthreads();
-  if (tid == 0) {  // sequential scan of the 256 run totals (index order)
-    double acc = s_base;
-    for (int i = 0; i < kThreads; ++i) {
-      const double t = run_tot[i];
-      run_tot[i] = acc;
-      acc += t;
-    }
-  }
-  __syncthreads();
-  double cum = run_tot[tid];
-  const double t = s_t;
-  int found = 0x7fffffff;
-  int last_pos = -1;
+  // exclusive prefix of the thread totals in thread order
+  double inc = tot;
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
+  for (int o = 1; o < kWave; o <<= 1) {
+    const double v = __shfl_up(inc, o);
+    if (lane >= o) inc += v;
+  }
+  if (lane == kWave - 1) s_wave[wave] = inc;
+  __syncthreads();
+  double cum = s_base;
+  for (int i = 0; i < wave; ++i) cum += s_wave[i];
+  cum += inc - tot;
+  const double t = s_t;
+  int found = 0x7fffffff, last_pos = -1;
+#pragma unroll
+  for (int i = 0; i < kPickPer; ++i) {
     if (wgt[i] > 0.0) last_pos = v0 + i;
     cum += wgt[i];
     if (found == 0x7fffffff && cum > t && wgt[i] > 0.0) found = v0 + i;
   }
-  atomicMin(&s_y, found);
+  if (found != 0x7fffffff) atomicMin(&s_y, found);
+  if (last_pos >= 0) atomicMax(&s_last, last_pos);
   __syncthreads();
-  if (s_y == 0x7fffffff) {  // rounding left u*S past this segment's end: last positive entry
-    __shared__ int s_last;
-    if (tid == 0) s_last = -1;
-    __syncthreads();
-    atomicMax(&s_last, last_pos);
-    __syncthreads();
-    if (tid == 0) s_y = s_last < 0 ? seg * kSeg : s_last;
-    __syncthreads();
-  }
   if (tid == 0) {
-    const int y = s_y;
-    const int n = c.dec[size_t(b) * 4];
-    const int G1 = c.a.gamma - 1;
+    // rounding left u * Q past this segment's end: its last positive entry
+    const int y = s_y != 0x7fffffff ? s_y : (s_last >= 0 ? s_last : seg * kSeg);
+    const int n = d.n;
     int32_t* com = c.a.committed + size_t(b) * c.a.gamma;
     for (int i = 0; i < c.a.gamma; ++i) com[i] = i < n ? c.a.tokens[size_t(b) * G1 + i] : (i == n ? y : -1);
     c.a.accept_len[b] = n;
@@ -514,24 +669,20 @@ template <typename T>
 hipError_t launch_typed(const Ctx& c, bool commit, hipStream_t stream) {
   const AcceptArgs& a = c.a;
   const int nseg = c.L.nseg, G1 = a.gamma - 1;
+  const bool with_labels = a.labels != nullptr;
   hipLaunchKernelGGL(stats_kernel<T>, dim3(nseg, c.L.n_ids), dim3(kThreads), 0, stream, c);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const bool with_labels = a.labels != nullptr;
-  if (with_labels) {
-    hipLaunchKernelGGL(tv_kernel<T>, dim3(nseg, a.B * G1), dim3(kThreads), 0, stream, c);
+  hipLaunchKernelGGL(decide_kernel<T>, dim3(a.B), dim3(kDecideThreads), 0, stream, c, int(commit));
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int draw_slots = commit ? a.B : 0;
+  const int slots = draw_slots + (with_labels ? a.B * G1 : 0);
+  if (slots > 0) {
+    hipLaunchKernelGGL(pair_kernel<T>, dim3(nseg, slots), dim3(kWideThreads), 0, stream, c,
+                       draw_slots, int(with_labels));
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  const int wpb = kThreads / kWave;
-  hipLaunchKernelGGL(decide_kernel<T>, dim3((a.B + wpb - 1) / wpb), dim3(kThreads), 0, stream, c,
-                     int(with_labels), int(commit));
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (!commit) return hipSuccess;
-  hipLaunchKernelGGL(draw_sum_kernel<T>, dim3(nseg, a.B), dim3(kThreads), 0, stream, c);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(draw_q_kernel<T>, dim3(nseg, a.B), dim3(kThreads), 0, stream, c);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(draw_pick_kernel<T>, dim3(a.B), dim3(kThreads), 0, stream, c);
+  hipLaunchKernelGGL(pick_kernel<T>, dim3(a.B), dim3(kPickThreads), 0, stream, c, int(commit));
   return hipGetLastError();
 }
 
@@ -544,14 +695,15 @@ size_t accept_workspace_bytes(int B, int gamma, int V, int max_rows) {
 hipError_t launch_accept(const AcceptArgs& a, int logit_dtype, bool commit, hipStream_t stream) {
   Ctx c;
   c.a = a;
+  c.P = kExp2Taylor;
   c.L = ws_layout(a.B, a.gamma, a.V, a.max_rows);
   char* base = static_cast<char*>(a.ws);
   c.st_m = reinterpret_cast<float*>(base + c.L.off_m);
   c.st_s = reinterpret_cast<double*>(base + c.L.off_s);
+  c.nm = reinterpret_cast<float2*>(base + c.L.off_nm);
   c.tv = reinterpret_cast<double*>(base + c.L.off_tv);
-  c.dec = reinterpret_cast<int*>(base + c.L.off_dec);
+  c.dec = reinterpret_cast<Decision*>(base + c.L.off_dec);
   c.r1 = reinterpret_cast<double*>(base + c.L.off_r1);
-  c.r2 = reinterpret_cast<double*>(base + c.L.off_r2);
   return logit_dtype == RVA_BF16 ? launch_typed<uint16_t>(c, commit, stream)
                                  : launch_typed<float>(c, commit, stream);
 }

@@ -191,6 +191,7 @@ rva_status accept_common(const char* name, int B, int gamma, int V, int logit_dt
   REQUIRE(logit_dtype == RVA_BF16 || logit_dtype == RVA_F32, "unknown logit_dtype %d", logit_dtype);
   REQUIRE((long long)max_rows + (long long)B * (gamma - 1) <= 65535,
           "max_rows + B*(gamma-1) must be <= 65535");
+  REQUIRE((long long)B * gamma <= 65535, "B*gamma must be <= 65535");
   REQUIRE(target_logits && draft_logits && cu_seqlens, "logits and cu_seqlens are required");
   REQUIRE(aligned(target_logits, 16) && aligned(draft_logits, 16), "logits must be 16-byte aligned");
   const size_t need = rva::accept_workspace_bytes(B, gamma, V, max_rows);
