@@ -17,16 +17,17 @@
 //                   float64 sums over the draw rows (target row n, and draft row n for a
 //                   residual draw) of e_t = exp(x_t - M_t), e_d = exp(x_d - M_d), and of the
 //                   unnormalised residual max(0, e_t - rho' e_d) with the draft entries it
-//                   keeps, at rho' = S_t / S_d from the float32-accurate stats.  Pair slots:
-//                   the segment's share of the TV distance sum max(0, p_t - p_d) (float32
-//                   terms, float64 sum) of every other draft pair.
+//                   keeps, at rho' = S_t / S_d from the float32-accurate stats; per segment
+//                   and per 512-entry sub-segment.  Pair slots: the segment's share of the TV
+//                   distance sum max(0, p_t - p_d) (float32 terms, float64 sum) of every
+//                   other draft pair.
 //   pick_kernel     one workgroup per request: labels = 1 - TV; the exact ratio
-//                   rho = S_t / S_d from the float64 sums corrects each segment's residual
-//                   mass to first order, A(rho) = A(rho') - (rho - rho') D (exact up to the
-//                   entries whose sign differs between rho' and rho, a second-order term);
-//                   u * Q locates the segment, which is rescanned with exact weights
-//                   max(0, e_t - rho e_d) and a block-wide prefix sum; then the commit
-//                   (accept_len, committed, context_lens).
+//                   rho = S_t / S_d from the float64 sums corrects each residual mass to
+//                   first order, A(rho) = A(rho') - (rho - rho') D (exact up to the entries
+//                   whose sign differs between rho' and rho, a second-order term); u * Q
+//                   locates the segment, then the sub-segment, whose 512 entries are
+//                   rescanned with exact weights max(0, e_t - rho e_d) and a block-wide
+//                   prefix sum; then the commit (accept_len, committed, context_lens).
 // The draw returns an index that has to agree with a float64 definition, so everything the
 // draw reads is float64: exp is 2^y by range reduction and a degree-13 Taylor polynomial of
 // 2^f on |f| <= 1/2 (truncation < 2e-16).
@@ -40,8 +41,10 @@ constexpr int kThreads = 256;          // stats pass
 constexpr int kPer = kSeg / kThreads;  // entries per thread per segment in the stats pass
 constexpr int kWideThreads = 512;      // float64 passes (draw sums, pair pass)
 constexpr int kWidePer = kSeg / kWideThreads;
-constexpr int kPickThreads = 512;
-constexpr int kPickPer = kSeg / kPickThreads;  // consecutive entries per thread in the pick
+constexpr int kSubLen = 512;                // sub-segment: what one wave covers per group
+constexpr int kSub = kSeg / kSubLen;         // sub-segments per segment
+constexpr int kPickThreads = kSubLen;        // the pick rescans one sub-segment, an entry a thread
+static_assert(kSubLen == 8 * kWave, "a wave's group of 8 entries per lane is one sub-segment");
 constexpr float kLog2e = 1.44269504088896341f;
 
 // e^(x - m) in float32 (x = -inf gives 0; m must be finite)
@@ -61,16 +64,21 @@ constexpr Exp2Poly kExp2Taylor = {{
     0x1.62c0223a5c824p-20, 0x1.b5253d395e7c4p-24, 0x1.e4cf5158b8ecap-28, 0x1.e8cac7351bb25p-32,
     0x1.c3bd650fc2986p-36, 0x1.816193166d0f9p-40}};
 
-// 2^y in float64 for y <= 0: y = n + f with n = rint(y), |f| <= 1/2; 2^f from the Taylor
-// series of exp(f ln 2) to degree 13 (truncation < 2e-16), then scaled by 2^n.
+// 2^y in float64 for y <= 0, without branches: y is clamped at -1100 (the result then
+// underflows to 0; NaN from fully masked rows also lands there), n = rint(y) by the
+// round-to-nearest of adding and removing 1.5 * 2^52 (whose low word is then n), f = y - n
+// with |f| <= 1/2, 2^f from the Taylor series of exp(f ln 2) to degree 13 (truncation
+// < 2e-16), scaled by 2^n.
 __device__ __forceinline__ double exp2_f64(const Exp2Poly& P, double y) {
-  if (!(y > -1100.0)) return 0.0;  // also maps -inf and NaN (fully masked rows) to 0
-  const double n = rint(y);
+  constexpr double kShifter = 0x1.8p52;
+  y = fmax(y, -1100.0);
+  const double s = y + kShifter;
+  const double n = s - kShifter;
   const double f = y - n;
   double p = P.c[13];
 #pragma unroll
   for (int k = 12; k >= 0; --k) p = fma(p, f, P.c[k]);
-  return ldexp(p, int(n));
+  return ldexp(p, int(__double2loint(s)));
 }
 constexpr double kLog2eF64 = 1.4426950408889634074;
 // e^(x - m) in float64 for float32 x <= m (x = -inf gives 0)
@@ -88,12 +96,14 @@ struct Decision {
   double rho32;  // S_t / S_d from the float32-accurate segment stats
 };
 
-// Float64 per-segment sums of a draw slot: S_t, S_d, A(rho'), D (see the header).
+// Float64 per-segment sums of a draw slot: S_t, S_d, A(rho'), D (see the header); per
+// sub-segment: S_t, A(rho'), D.
 constexpr int kDrawSums = 4;
+constexpr int kSubSums = 3;
 
 struct WsLayout {
   int nseg, n_ids;
-  size_t off_m, off_s, off_nm, off_tv, off_dec, off_r1, total;
+  size_t off_m, off_s, off_nm, off_tv, off_dec, off_r1, off_sub, total;
 };
 
 __host__ __device__ inline WsLayout ws_layout(int B, int gamma, int V, int max_rows) {
@@ -113,6 +123,7 @@ __host__ __device__ inline WsLayout ws_layout(int B, int gamma, int V, int max_r
   w.off_tv = take(sizeof(double) * size_t(B) * G1 * w.nseg);
   w.off_dec = take(sizeof(Decision) * size_t(B));
   w.off_r1 = take(sizeof(double) * size_t(B) * w.nseg * kDrawSums);
+  w.off_sub = take(sizeof(double) * size_t(B) * w.nseg * kSub * kSubSums);
   w.total = off;
   return w;
 }
@@ -128,6 +139,7 @@ struct Ctx {
   double* tv;     // [B*G1][nseg] TV shares
   Decision* dec;  // [B]
   double* r1;     // [B][nseg][kDrawSums] float64 sums of the draw slots
+  double* sub;    // [B][nseg][kSub][kSubSums] the same per sub-segment
 };
 
 // Request b's packed rows [cu[b], cu[b] + w) lie inside [0, max_rows) and w in [1, gamma].
@@ -142,10 +154,10 @@ __device__ __forceinline__ const T* row_ptr(const Ctx& c, int id) {
   return static_cast<const T*>(c.a.draft) + size_t(id - c.a.max_rows) * c.a.V;
 }
 
-// A thread's share (kSeg / NT entries) of one segment, interleaved in 16-byte groups across
-// the NT threads of the block and kept as loaded: bf16 as packed pairs (half the registers of
-// float32), float32 as is.  Entries past the row end read as -inf.  Any fixed assignment of
-// entries to (thread, i) serves the sums; rows of the same V get the same one.
+// A thread's share (kSeg / NT entries) of one segment, kept as loaded: bf16 as packed pairs
+// (half the registers of float32), float32 as is.  Entry q = 8 g + j of thread t is
+// segment entry g * 8 NT + 8 t + j, so for each group g a wave covers 512 consecutive
+// entries (sub-segment 8 g NT / 512 + wave).  Entries past the row end read as -inf.
 template <typename T, int NT>
 struct SegData;
 
@@ -153,34 +165,36 @@ template <int NT>
 struct SegData<uint16_t, NT> {
   static constexpr int P = kSeg / NT;
   uint32_t w[P / 2];
-  __device__ __forceinline__ float operator[](int i) const {
-    return (i & 1) ? __uint_as_float(w[i >> 1] & 0xffff0000u) : __uint_as_float(w[i >> 1] << 16);
+  __device__ __forceinline__ float operator[](int q) const {
+    return (q & 1) ? __uint_as_float(w[q >> 1] & 0xffff0000u) : __uint_as_float(w[q >> 1] << 16);
   }
   __device__ __forceinline__ void load(const uint16_t* row, int V, int seg) {
     constexpr uint32_t kNegInf2 = 0xff80ff80u;  // two bf16 -inf
-    const int base = seg * kSeg;
+    const int base = seg * kSeg + int(threadIdx.x) * 8;
     if (V % 8 == 0) {
 #pragma unroll
-      for (int i = 0; i < P / 8; ++i) {
-        const int v = base + (i * NT + int(threadIdx.x)) * 8;
+      for (int g = 0; g < P / 8; ++g) {
+        const int v = base + g * 8 * NT;
         if (v < V) {
           const uint4 u = *reinterpret_cast<const uint4*>(row + v);
-          w[4 * i] = u.x;
-          w[4 * i + 1] = u.y;
-          w[4 * i + 2] = u.z;
-          w[4 * i + 3] = u.w;
+          w[4 * g] = u.x;
+          w[4 * g + 1] = u.y;
+          w[4 * g + 2] = u.z;
+          w[4 * g + 3] = u.w;
         } else {
-          w[4 * i] = w[4 * i + 1] = w[4 * i + 2] = w[4 * i + 3] = kNegInf2;
+          w[4 * g] = w[4 * g + 1] = w[4 * g + 2] = w[4 * g + 3] = kNegInf2;
         }
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < P / 2; ++i) {
-        const int v = base + (i * NT + int(threadIdx.x)) * 2;
-        const uint32_t lo = v < V ? row[v] : 0xff80u;
-        const uint32_t hi = v + 1 < V ? row[v + 1] : 0xff80u;
-        w[i] = lo | (hi << 16);
-      }
+      for (int g = 0; g < P / 8; ++g)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int v = base + g * 8 * NT + 2 * k;
+          const uint32_t lo = v < V ? row[v] : 0xff80u;
+          const uint32_t hi = v + 1 < V ? row[v + 1] : 0xff80u;
+          w[4 * g + k] = lo | (hi << 16);
+        }
     }
   }
 };
@@ -189,66 +203,33 @@ template <int NT>
 struct SegData<float, NT> {
   static constexpr int P = kSeg / NT;
   float f[P];
-  __device__ __forceinline__ float operator[](int i) const { return f[i]; }
+  __device__ __forceinline__ float operator[](int q) const { return f[q]; }
   __device__ __forceinline__ void load(const float* row, int V, int seg) {
-    const int base = seg * kSeg;
+    const int base = seg * kSeg + int(threadIdx.x) * 8;
     if (V % 4 == 0) {
 #pragma unroll
-      for (int i = 0; i < P / 4; ++i) {
-        const int v = base + (i * NT + int(threadIdx.x)) * 4;
-        if (v < V) {
-          const float4 u = *reinterpret_cast<const float4*>(row + v);
-          f[4 * i] = u.x;
-          f[4 * i + 1] = u.y;
-          f[4 * i + 2] = u.z;
-          f[4 * i + 3] = u.w;
-        } else {
-          f[4 * i] = f[4 * i + 1] = f[4 * i + 2] = f[4 * i + 3] = -INFINITY;
+      for (int g = 0; g < P / 8; ++g)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int v = base + g * 8 * NT + 4 * h;
+          float4 u = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+          if (v < V) u = *reinterpret_cast<const float4*>(row + v);
+          f[8 * g + 4 * h] = u.x;
+          f[8 * g + 4 * h + 1] = u.y;
+          f[8 * g + 4 * h + 2] = u.z;
+          f[8 * g + 4 * h + 3] = u.w;
         }
-      }
     } else {
 #pragma unroll
-      for (int i = 0; i < P; ++i) {
-        const int v = base + i * NT + int(threadIdx.x);
-        f[i] = v < V ? row[v] : -INFINITY;
-      }
+      for (int g = 0; g < P / 8; ++g)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int v = base + g * 8 * NT + j;
+          f[8 * g + j] = v < V ? row[v] : -INFINITY;
+        }
     }
   }
 };
-
-// kPickPer consecutive entries starting at v0 (-inf past the row end).
-template <typename T>
-__device__ __forceinline__ void load_run(const T* row, int V, int v0, float (&x)[kPickPer]) {
-  if constexpr (sizeof(T) == 2) {
-    if (V % 8 == 0 && v0 + kPickPer <= V) {
-#pragma unroll
-      for (int i = 0; i < kPickPer / 8; ++i) {
-        const uint4 u = *reinterpret_cast<const uint4*>(row + v0 + 8 * i);
-        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          x[i * 8 + 2 * j] = __uint_as_float(w[j] << 16);
-          x[i * 8 + 2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
-        }
-      }
-      return;
-    }
-  } else {
-    if (V % 4 == 0 && v0 + kPickPer <= V) {
-#pragma unroll
-      for (int i = 0; i < kPickPer / 4; ++i) {
-        const float4 u = *reinterpret_cast<const float4*>(row + v0 + 4 * i);
-        x[i * 4] = u.x;
-        x[i * 4 + 1] = u.y;
-        x[i * 4 + 2] = u.z;
-        x[i * 4 + 3] = u.w;
-      }
-      return;
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < kPickPer; ++i) x[i] = v0 + i < V ? Elem<T>::load(row, v0 + i) : -INFINITY;
-}
 
 template <int NT>
 __device__ __forceinline__ float block_max(float v, float* sm) {
@@ -298,6 +279,15 @@ __device__ __forceinline__ double seg_mass(const Ctx& c, int b, int s, bool resi
   const double* r = c.r1 + (size_t(b) * c.L.nseg + s) * kDrawSums;
   if (!residual) return r[0];
   const double m = r[2] - drho * r[3];
+  return m > 0.0 ? m : 0.0;
+}
+
+// Draw mass of sub-segment u of segment s (same rule as seg_mass).
+__device__ __forceinline__ double sub_mass(const Ctx& c, int b, int s, int u, bool residual,
+                                           double drho) {
+  const double* r = c.sub + ((size_t(b) * c.L.nseg + s) * kSub + u) * kSubSums;
+  if (!residual) return r[0];
+  const double m = r[1] - drho * r[2];
   return m > 0.0 ? m : 0.0;
 }
 
@@ -464,30 +454,41 @@ __global__ __launch_bounds__(kWideThreads) void pair_kernel(Ctx c, int draw_slot
     SegData<T, kWideThreads> xt, xd;
     xt.load(row_ptr<T>(c, d.id_t), c.a.V, seg);
     double v[kDrawSums + 1] = {0.0, 0.0, 0.0, 0.0, 0.0};
-    if (residual) {
-      xd.load(row_ptr<T>(c, d.id_d), c.a.V, seg);
-      double it = 0.0, id = 0.0;
-      if (lab) {
-        it = double(c.nm[d.id_t].y);
-        id = double(c.nm[d.id_d].y);
-      }
+    double it = 0.0, id = 0.0;
+    if (residual) xd.load(row_ptr<T>(c, d.id_d), c.a.V, seg);
+    if (lab) {
+      it = double(c.nm[d.id_t].y);
+      id = double(c.nm[d.id_d].y);
+    }
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    double* subp = c.sub + (size_t(b) * c.L.nseg + seg) * kSub * kSubSums;
 #pragma unroll
-      for (int i = 0; i < kWidePer; ++i) {
-        const double et = exp_shift_f64(c.P, xt[i], d.Mt);
-        const double ed = exp_shift_f64(c.P, xd[i], d.Md);
-        v[0] += et;
-        v[1] += ed;
-        const double r = et - d.rho32 * ed;
-        if (r > 0.0) {
-          v[2] += r;
-          v[3] += ed;
+    for (int g = 0; g < kWidePer / 8; ++g) {
+      double gs[kSubSums] = {0.0, 0.0, 0.0};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const double et = exp_shift_f64(c.P, xt[8 * g + j], d.Mt);
+        gs[0] += et;
+        if (residual) {
+          const double ed = exp_shift_f64(c.P, xd[8 * g + j], d.Md);
+          v[1] += ed;
+          const double r = et - d.rho32 * ed;
+          if (r > 0.0) {
+            gs[1] += r;
+            gs[2] += ed;
+          }
+          const double q = et * it - ed * id;
+          v[4] += q > 0.0 ? q : 0.0;
         }
-        const double g = et * it - ed * id;
-        v[4] += g > 0.0 ? g : 0.0;
       }
-    } else {
+      v[0] += gs[0];
+      v[2] += gs[1];
+      v[3] += gs[2];
 #pragma unroll
-      for (int i = 0; i < kWidePer; ++i) v[0] += exp_shift_f64(c.P, xt[i], d.Mt);
+      for (int q = 0; q < kSubSums; ++q) gs[q] = wave_sum_f64(gs[q]);
+      if (lane == 0)
+#pragma unroll
+        for (int q = 0; q < kSubSums; ++q) subp[(g * (kWideThreads / kWave) + wave) * kSubSums + q] = gs[q];
     }
     block_sums_f64<kDrawSums + 1>(v, sm);
     if (threadIdx.x == 0) {
@@ -529,10 +530,52 @@ __global__ __launch_bounds__(kWideThreads) void pair_kernel(Ctx c, int draw_slot
 }
 
 // ------------------------------------------------------------------ pick + commit + labels
+// One wave: the first of n items (masses mass(i) >= 0, in index order) at which the running
+// sum, started at `start`, passes t; `found` = that item and `base` = the running sum before
+// it.  If rounding leaves t unpassed, the last item with mass (or item 0).
+template <typename F>
+__device__ __forceinline__ void locate(double t, double start, int n, F mass, int& found,
+                                       double& base) {
+  const int lane = threadIdx.x % kWave;
+  int last = 0;
+  double base_last = start, carry = start;
+  found = -1;
+  base = start;
+  for (int i0 = 0; i0 < n && found < 0; i0 += kWave) {
+    const int i = i0 + lane;
+    const double m = i < n ? mass(i) : 0.0;
+    double inc = m;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const double x = __shfl_up(inc, o);
+      if (lane >= o) inc += x;
+    }
+    inc += carry;
+    const double exc = inc - m;
+    const unsigned long long hit = __ballot(m > 0.0 && inc > t);
+    const unsigned long long pos = __ballot(m > 0.0);
+    if (pos) {
+      const int l = 63 - __clzll(pos);
+      last = i0 + l;
+      base_last = __shfl(exc, l);
+    }
+    if (hit) {
+      const int l = __ffsll(hit) - 1;
+      found = i0 + l;
+      base = __shfl(exc, l);
+    }
+    carry = __shfl(inc, kWave - 1);
+  }
+  if (found < 0) {
+    found = last;
+    base = base_last;
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(kPickThreads) void pick_kernel(Ctx c, int commit) {
   __shared__ double s_t, s_base, s_rho;
-  __shared__ int s_seg, s_residual;
+  __shared__ int s_pos, s_residual;
   __shared__ double s_wave[kPickThreads / kWave];
   __shared__ int s_y, s_last;
   const int b = blockIdx.x;
@@ -568,42 +611,17 @@ __global__ __launch_bounds__(kPickThreads) void pick_kernel(Ctx c, int commit) {
       Q = St;
     }
     const double t = double(c.a.u_res[b]) * Q;
-    // running sum over the segments in index order, 64 segments at a time
-    int seg = -1, last_seg = 0;
-    double base = 0.0, base_last = 0.0, carry = 0.0;
-    for (int s0 = 0; s0 < nseg && seg < 0; s0 += kWave) {
-      const int s = s0 + lane;
-      const double qs = s < nseg ? seg_mass(c, b, s, residual, drho) : 0.0;
-      double inc = qs;  // inclusive scan across the wave
-#pragma unroll
-      for (int o = 1; o < kWave; o <<= 1) {
-        const double v = __shfl_up(inc, o);
-        if (lane >= o) inc += v;
-      }
-      inc += carry;
-      const double exc = inc - qs;
-      const unsigned long long hit = __ballot(s < nseg && qs > 0.0 && inc > t);
-      const unsigned long long pos = __ballot(s < nseg && qs > 0.0);
-      if (pos) {
-        const int l = 63 - __clzll(pos);
-        last_seg = s0 + l;
-        base_last = __shfl(exc, l);
-      }
-      if (hit) {
-        const int l = __ffsll(hit) - 1;
-        seg = s0 + l;
-        base = __shfl(exc, l);
-      }
-      carry = __shfl(inc, kWave - 1);
-    }
-    if (seg < 0) {  // u * Q reached the end by rounding: last segment with mass
-      seg = last_seg;
-      base = base_last;
-    }
+    // first segment whose running mass passes t, then the first sub-segment inside it
+    int seg = -1;
+    double base = 0.0;
+    locate(t, 0.0, nseg, [&](int s) { return seg_mass(c, b, s, residual, drho); }, seg, base);
+    int sub = -1;
+    double base2 = base;
+    locate(t, base, kSub, [&](int u) { return sub_mass(c, b, seg, u, residual, drho); }, sub, base2);
     if (lane == 0) {
       s_t = t;
-      s_base = base;
-      s_seg = seg;
+      s_base = base2;
+      s_pos = seg * kSeg + sub * kSubLen;
       s_residual = residual;
       s_rho = rho;
       s_y = 0x7fffffff;
@@ -611,52 +629,36 @@ __global__ __launch_bounds__(kPickThreads) void pick_kernel(Ctx c, int commit) {
     }
   }
   __syncthreads();
-  const int seg = s_seg;
   const bool residual = s_residual;
-  const double rho = s_rho;
-  const int v0 = seg * kSeg + tid * kPickPer;
-  float xt[kPickPer], xd[kPickPer];
-  load_run<T>(row_ptr<T>(c, d.id_t), c.a.V, v0, xt);
-  if (residual) load_run<T>(row_ptr<T>(c, d.id_d), c.a.V, v0, xd);
-  double wgt[kPickPer];
-  double tot = 0.0;
-#pragma unroll
-  for (int i = 0; i < kPickPer; ++i) {
-    const double et = exp_shift_f64(c.P, xt[i], d.Mt);
-    double q = et;
+  const int v = s_pos + tid;
+  double wgt = 0.0;
+  if (v < c.a.V) {
+    wgt = exp_shift_f64(c.P, Elem<T>::load(row_ptr<T>(c, d.id_t), v), d.Mt);
     if (residual) {
-      q = et - rho * exp_shift_f64(c.P, xd[i], d.Md);
-      q = q > 0.0 ? q : 0.0;
+      wgt -= s_rho * exp_shift_f64(c.P, Elem<T>::load(row_ptr<T>(c, d.id_d), v), d.Md);
+      wgt = wgt > 0.0 ? wgt : 0.0;
     }
-    wgt[i] = q;
-    tot += q;
   }
-  // exclusive prefix of the thread totals in thread order
-  double inc = tot;
+  // inclusive prefix in index order: wave scan, then the wave totals
+  double inc = wgt;
 #pragma unroll
   for (int o = 1; o < kWave; o <<= 1) {
-    const double v = __shfl_up(inc, o);
-    if (lane >= o) inc += v;
+    const double x = __shfl_up(inc, o);
+    if (lane >= o) inc += x;
   }
   if (lane == kWave - 1) s_wave[wave] = inc;
   __syncthreads();
   double cum = s_base;
   for (int i = 0; i < wave; ++i) cum += s_wave[i];
-  cum += inc - tot;
-  const double t = s_t;
-  int found = 0x7fffffff, last_pos = -1;
-#pragma unroll
-  for (int i = 0; i < kPickPer; ++i) {
-    if (wgt[i] > 0.0) last_pos = v0 + i;
-    cum += wgt[i];
-    if (found == 0x7fffffff && cum > t && wgt[i] > 0.0) found = v0 + i;
+  cum += inc;
+  if (wgt > 0.0) {
+    if (cum > s_t) atomicMin(&s_y, v);
+    atomicMax(&s_last, v);
   }
-  if (found != 0x7fffffff) atomicMin(&s_y, found);
-  if (last_pos >= 0) atomicMax(&s_last, last_pos);
   __syncthreads();
   if (tid == 0) {
-    // rounding left u * Q past this segment's end: its last positive entry
-    const int y = s_y != 0x7fffffff ? s_y : (s_last >= 0 ? s_last : seg * kSeg);
+    // rounding left u * Q past this sub-segment's end: its last positive entry
+    const int y = s_y != 0x7fffffff ? s_y : (s_last >= 0 ? s_last : s_pos);
     const int n = d.n;
     int32_t* com = c.a.committed + size_t(b) * c.a.gamma;
     for (int i = 0; i < c.a.gamma; ++i) com[i] = i < n ? c.a.tokens[size_t(b) * G1 + i] : (i == n ? y : -1);
@@ -704,6 +706,7 @@ hipError_t launch_accept(const AcceptArgs& a, int logit_dtype, bool commit, hipS
   c.tv = reinterpret_cast<double*>(base + c.L.off_tv);
   c.dec = reinterpret_cast<Decision*>(base + c.L.off_dec);
   c.r1 = reinterpret_cast<double*>(base + c.L.off_r1);
+  c.sub = reinterpret_cast<double*>(base + c.L.off_sub);
   return logit_dtype == RVA_BF16 ? launch_typed<uint16_t>(c, commit, stream)
                                  : launch_typed<float>(c, commit, stream);
 }
