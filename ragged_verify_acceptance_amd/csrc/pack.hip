@@ -7,7 +7,7 @@
 // tier so that a smaller graph is replayed when the budget shrinks.
 //
 // One launch, destination-row oriented: every workgroup rebuilds cu_seqlens for the whole
-// batch in LDS (a 256-lane scan of at most a few hundred ints, cheaper than a second
+// batch in LDS (a 256-lane scan of at most a few thousand ints, cheaper than a second
 // launch), picks the tier, and then handles kRowsPerBlock destination rows: a binary
 // search in LDS finds the owning request, the row is copied with 16-byte vector accesses
 // when alignment allows, rows [M, tier) are zero-filled.  Workgroup 0 publishes
@@ -28,7 +28,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(
     int32_t* __restrict__ row_req, int32_t* __restrict__ row_pos,
     int32_t* __restrict__ total_tier, int32_t* status) {
   __shared__ int cu[kMaxPackB + 1];
-  __shared__ int part[kPackThreads];
+  __shared__ int part[kPackThreads / kWave];
   __shared__ int s_M, s_tier;
   const int tid = threadIdx.x;
 
@@ -48,15 +48,21 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(
       cu[b + 1] = w;  // temporarily the window
     }
   }
-  part[tid] = run;
-  __syncthreads();
-  for (int o = 1; o < kPackThreads; o <<= 1) {
-    const int v = tid >= o ? part[tid - o] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
+  // inclusive scan of the run totals: inside each wave by shuffles, then the wave totals
+  const int lane = tid % kWave, wave = tid / kWave;
+  int inc = run;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int v = __shfl_up(inc, o);
+    if (lane >= o) inc += v;
   }
-  int acc = tid > 0 ? part[tid - 1] : 0;
+  if (lane == kWave - 1) part[wave] = inc;
+  __syncthreads();
+  int wave_off = 0;
+  for (int w = 0; w < wave; ++w) wave_off += part[w];
+  int total = 0;
+  for (int w = 0; w < kPackThreads / kWave; ++w) total += part[w];
+  int acc = wave_off + inc - run;
   for (int i = 0; i < per; ++i) {
     const int b = b0 + i;
     if (b < B) {
@@ -64,17 +70,18 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(
       cu[b + 1] = acc;
     }
   }
+  // tier = the first (ascending) tier >= M = tiers.t[#tiers below M]; the count is taken by
+  // all threads at once (the table sits in the kernel arguments, and a sequential search
+  // would chain its loads)
+  static_assert(sizeof(tiers.t) / sizeof(tiers.t[0]) == 2 * kPackThreads, "two tiers a thread");
+  const int M_all = total;
+  const int n_below = __syncthreads_count(tid < tiers.n && tiers.t[tid] < M_all) +
+                      __syncthreads_count(tid + kPackThreads < tiers.n &&
+                                          tiers.t[tid + kPackThreads] < M_all);
   if (tid == 0) {
     cu[0] = 0;
-    const int M = part[kPackThreads - 1];
-    int tier = tiers.t[tiers.n - 1];
-    for (int t = 0; t < tiers.n; ++t)
-      if (tiers.t[t] >= M) {
-        tier = tiers.t[t];
-        break;
-      }
-    s_M = M;
-    s_tier = tier;
+    s_M = M_all;
+    s_tier = tiers.t[n_below < tiers.n ? n_below : tiers.n - 1];
   }
   __syncthreads();
   const int M = s_M, tier = s_tier;

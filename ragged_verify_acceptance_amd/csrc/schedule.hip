@@ -76,60 +76,119 @@ __device__ __forceinline__ double block_exclusive_scan_f64(double v, double* lds
   return wave_off + x - v;
 }
 
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int d) {
+  const uint32_t lo = __shfl_xor(uint32_t(v), d), hi = __shfl_xor(uint32_t(v >> 32), d);
+  return (uint64_t(hi) << 32) | lo;
+}
+
+// One compare-exchange step of a bitonic sort for the element with index i holding x and
+// partner value y (index i ^ j): the lower index of an ascending (i & k == 0) pair keeps the
+// minimum.
+__device__ __forceinline__ uint64_t bitonic_keep(uint64_t x, uint64_t y, int i, int j, int k) {
+  const bool keep_min = ((i & j) == 0) == ((i & k) == 0);
+  return keep_min ? (x < y ? x : y) : (x > y ? x : y);
+}
+
+// Ascending bitonic sort of Npad (a power of two, <= E * kSchedThreads) keys; thread t holds
+// the E consecutive elements t*E .. t*E + E - 1 in x.  Partners in the same thread are swapped
+// in registers, partners in the same wave by lane shuffles, and only partners in other waves
+// go through LDS (two barriers per such step).
+template <int E>
+__device__ __forceinline__ void bitonic_sort(uint64_t (&x)[E], uint64_t* lds, int Npad) {
+  const int tid = threadIdx.x;
+  for (int k = 2; k <= Npad; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      if (j >= kWave * E) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) lds[tid * E + e] = x[e];
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int i = tid * E + e;
+          x[e] = bitonic_keep(x[e], lds[i ^ j], i, j, k);
+        }
+        __syncthreads();
+      } else if (j >= E) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int i = tid * E + e;
+          x[e] = bitonic_keep(x[e], shfl_xor_u64(x[e], j / E), i, j, k);
+        }
+      } else {
+        uint64_t y[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          // j < E <= 4: j is 1 or 2; the partner index e ^ j is picked without dynamic indexing
+          uint64_t p = x[e];
+#pragma unroll
+          for (int f = 0; f < E; ++f)
+            if (f == (e ^ j)) p = x[f];
+          y[e] = bitonic_keep(x[e], p, tid * E + e, j, k);
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) x[e] = y[e];
+      }
+    }
+  }
+}
+
+template <int E>
 __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(
-    int B, int G, int mode, const float* __restrict__ conf, float* __restrict__ surv_out,
-    float bias, const float* __restrict__ alpha, const float* __restrict__ theta,
-    int32_t* __restrict__ windows, int32_t* __restrict__ K_out, double* __restrict__ ratio_out,
-    int32_t* status) {
+    int B, int G, int mode, const float* __restrict__ conf, float* __restrict__ conf_out,
+    float* __restrict__ surv_out, float bias, const float* __restrict__ alpha,
+    const float* __restrict__ theta, int32_t* __restrict__ windows, int32_t* __restrict__ K_out,
+    double* __restrict__ ratio_out, int32_t* status) {
   __shared__ uint64_t keys[kMaxCand];
+  __shared__ float sa[kMaxCand];
   __shared__ int cnt[kMaxCand];
   __shared__ double wave_tot[kSchedThreads / kWave];
   __shared__ double red_ratio[kSchedThreads / kWave];
   __shared__ int red_K[kSchedThreads / kWave];
-  __shared__ int bad;
 
   const int tid = threadIdx.x;
   const int N = B * G;
   int Npad = 2;
   while (Npad < N) Npad <<= 1;
-  if (tid == 0) bad = 0;
 
-  // (1) survival, one lane per request, float32 products in order
+  // (1) survival: the confidences are staged in LDS by one coalesced load, then one lane per
+  // request forms the float32 products left to right
+  for (int i = tid; i < N; i += kSchedThreads) {
+    const float c = conf[i];
+    if (!(c >= 0.f && c <= 1.f)) flag(status, RVA_DEV_BAD_CONF);
+    if (conf_out) conf_out[i] = c;
+    sa[i] = c;
+  }
+  __syncthreads();
   for (int b = tid; b < B; b += kSchedThreads) {
     float a = 1.f;
     for (int j = 0; j < G; ++j) {
-      const float c = conf[b * G + j];
-      if (!(c >= 0.f && c <= 1.f)) flag(status, RVA_DEV_BAD_CONF);
-      a = (j == 0) ? c : __fmul_rn(a, c);
-      surv_out[b * G + j] = a;
-      const uint32_t bits = (a == 0.f) ? 0u : __float_as_uint(a);
-      keys[b * G + j] = (uint64_t(~bits) << 32) | uint32_t(b * G + j);
+      a = (j == 0) ? sa[b * G + j] : __fmul_rn(a, sa[b * G + j]);
+      sa[b * G + j] = a;
     }
     cnt[b] = 0;
   }
-  for (int i = N + tid; i < Npad; i += kSchedThreads) keys[i] = ~0ull;
   __syncthreads();
-
-  // (2) bitonic sort, ascending key == (survival desc, index asc)
-  for (int k = 2; k <= Npad; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < Npad; i += kSchedThreads) {
-        const int p = i ^ j;
-        if (p > i) {
-          const uint64_t x = keys[i], y = keys[p];
-          const bool up = (i & k) == 0;
-          if ((x > y) == up) {
-            keys[i] = y;
-            keys[p] = x;
-          }
-        }
-      }
-      __syncthreads();
+  // (2) sort keys (inverted survival bits, candidate index): ascending key order is
+  // "survival desc, request asc, position asc"
+  uint64_t x[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = tid * E + e;
+    x[e] = ~0ull;
+    if (i < N) {
+      const float a = sa[i];
+      surv_out[i] = a;
+      const uint32_t bits = (a == 0.f) ? 0u : __float_as_uint(a);
+      x[e] = (uint64_t(~bits) << 32) | uint32_t(i);
     }
   }
+  bitonic_sort<E>(x, keys, Npad);
+#pragma unroll
+  for (int e = 0; e < E; ++e) keys[tid * E + e] = x[e];
+  __syncthreads();
 
   // (3) S_K: each thread owns a contiguous run of ranks
-  const int per = (Npad + kSchedThreads - 1) / kSchedThreads;
+  constexpr int per = E;
   const int r0 = tid * per;
   double run = 0.0;
   for (int i = 0; i < per; ++i) {
@@ -216,7 +275,6 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(
     *K_out = Kstar;
     *ratio_out = ratio;
   }
-  (void)bad;
 }
 
 }  // namespace
@@ -243,13 +301,20 @@ hipError_t launch_schedule(int B, int gamma, int mode, const void* hidden, int h
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     conf = conf_out;
-  } else {
-    hipError_t e = hipMemcpyAsync(conf_out, conf_in, sizeof(float) * rows,
-                                  hipMemcpyDeviceToDevice, stream);
-    if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(kSchedThreads), 0, stream, B, G, mode, conf,
-                     surv_out, bias, alpha, theta, windows, K_out, ratio_out, status);
+  // conf_in is echoed into conf_out by the schedule kernel itself
+  float* echo = conf_in ? conf_out : nullptr;
+  int Npad = 2;
+  while (Npad < rows) Npad <<= 1;
+  if (Npad <= kSchedThreads)
+    hipLaunchKernelGGL(schedule_kernel<1>, dim3(1), dim3(kSchedThreads), 0, stream, B, G, mode,
+                       conf, echo, surv_out, bias, alpha, theta, windows, K_out, ratio_out, status);
+  else if (Npad <= 2 * kSchedThreads)
+    hipLaunchKernelGGL(schedule_kernel<2>, dim3(1), dim3(kSchedThreads), 0, stream, B, G, mode,
+                       conf, echo, surv_out, bias, alpha, theta, windows, K_out, ratio_out, status);
+  else
+    hipLaunchKernelGGL(schedule_kernel<4>, dim3(1), dim3(kSchedThreads), 0, stream, B, G, mode,
+                       conf, echo, surv_out, bias, alpha, theta, windows, K_out, ratio_out, status);
   return hipGetLastError();
 }
 

@@ -1,0 +1,144 @@
+"""GPU edge cases through the C ABI, each against the oracle.
+
+Covers shapes the five workloads do not reach: scheduler candidate counts on every sort
+layout (up to 1024, 2048 and 4096 candidates), heavy survival ties, single-draft and
+single-request batches, and acceptance batches whose windows are all 1 (no drafts: every
+request takes the bonus draw) or all gamma.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from ragged_verify_acceptance_amd import rva
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _schedule_case(B, gamma, conf, theta_per_token, static=False):
+    G = gamma - 1
+    conf = np.asarray(conf, np.float32).reshape(B, G)
+    alpha = np.zeros(B + 1, np.float32)
+    theta = (np.float32(theta_per_token) * np.arange(B * gamma + 1, dtype=np.float32)).astype(np.float32)
+    bias = np.float32(20.0)
+    t = lambda a, dt=None: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    conf_out = torch.empty((B, G), dtype=torch.float32, device=DEV)
+    surv = torch.empty((B, G), dtype=torch.float32, device=DEV)
+    windows = torch.empty(B, dtype=torch.int32, device=DEV)
+    K = torch.empty(1, dtype=torch.int32, device=DEV)
+    ratio = torch.empty(1, dtype=torch.float64, device=DEV)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    rva.schedule_windows(B, gamma, 1 if static else 0, None, 0, None, 0.0, t(conf), None,
+                         float(bias), t(alpha), t(theta), conf_out, surv, windows, K, ratio,
+                         status)
+    torch.cuda.synchronize()
+    a = oracle.survival(conf)
+    ref = oracle.schedule_windows(a, gamma, bias, alpha, theta, static=static)
+    assert np.array_equal(conf_out.cpu().numpy().view(np.uint32), conf.view(np.uint32))
+    assert np.array_equal(surv.cpu().numpy().view(np.uint32), a.view(np.uint32))
+    if not ref["near_tie"]:
+        assert np.array_equal(windows.cpu().numpy(), ref["windows"])
+        assert int(K.item()) == ref["K"]
+    assert abs(float(ratio.item()) - ref["ratio"]) <= 1e-12 * abs(ref["ratio"])
+    assert int(status.item()) == 0
+    return ref
+
+
+@pytest.mark.parametrize("B,gamma", [(1, 2), (3, 5), (64, 17), (128, 16), (200, 8), (256, 16),
+                                     (64, 64)])
+@pytest.mark.parametrize("kind", ["beta", "ties"])
+def test_schedule_sizes(B, gamma, kind):
+    """Candidate counts 1 .. 4032 (every register layout of the sort), with and without ties."""
+    print(f"[schedule-size] B={B} gamma={gamma} {kind}", flush=True)
+    rng = np.random.default_rng(B * 100 + gamma)
+    G = gamma - 1
+    if kind == "beta":
+        conf = rng.beta(6.0, 1.5, size=(B, G))
+    else:  # few distinct values: long runs of equal survival across requests
+        conf = rng.choice([1.0, 0.875, 0.75, 0.5], size=(B, G))
+    for theta in (0.01, 0.19, 2.0):
+        _schedule_case(B, gamma, conf, theta)
+    _schedule_case(B, gamma, conf, 0.19, static=True)
+
+
+def _accept_case(B, gamma, V, windows, seed, dtype=torch.bfloat16):
+    rng = np.random.default_rng(seed)
+    G1 = gamma - 1
+    windows = np.asarray(windows, np.int64)
+    cu = np.concatenate([[0], np.cumsum(windows)]).astype(np.int32)
+    M = int(cu[-1])
+    max_rows = M + 3
+    tl = (rng.standard_normal((max_rows, V)) * 2.0).astype(np.float32)
+    dl = (rng.standard_normal((B * G1, V)) * 2.0).astype(np.float32)
+    # drafts close to the target rows for half the requests (high acceptance)
+    for b in range(B):
+        for k in range(windows[b] - 1):
+            if b % 2 == 0:
+                dl[b * G1 + k] = tl[cu[b] + k] + 0.3 * rng.standard_normal(V).astype(np.float32)
+    tl_t = torch.from_numpy(tl).to(dtype)
+    dl_t = torch.from_numpy(dl).to(dtype)
+    tokens = rng.integers(0, V, size=(B, G1)).astype(np.int32)
+    ua = rng.random((B, G1)).astype(np.float32)
+    ur = rng.random(B).astype(np.float32)
+    ctx0 = rng.integers(10, 100, size=B).astype(np.int32)
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    acc = torch.empty(B, dtype=torch.int32, device=DEV)
+    com = torch.empty((B, gamma), dtype=torch.int32, device=DEV)
+    ctx = d(ctx0)
+    pt = torch.empty((B, G1), dtype=torch.float32, device=DEV)
+    pd = torch.empty((B, G1), dtype=torch.float32, device=DEV)
+    lab = torch.empty((B, G1), dtype=torch.float32, device=DEV)
+    ws = torch.empty(rva.accept_workspace_size(B, gamma, V, max_rows), dtype=torch.uint8, device=DEV)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    rva.accept_and_commit(B, gamma, V, max_rows, tl_t.to(DEV), dl_t.to(DEV), d(tokens), d(ua),
+                          d(ur), d(cu), acc, com, ctx, pt, pd, lab, ws, status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    tl64 = tl_t.double().numpy()
+    dl64 = dl_t.double().numpy()
+    acc_h, com_h, ctx_h = acc.cpu().numpy(), com.cpu().numpy(), ctx.cpu().numpy()
+    lab_h = lab.cpu().numpy()
+    flips = 0
+    for b in range(B):
+        w = int(windows[b])
+        r = oracle.accept_request(tl64[cu[b]:cu[b] + w], dl64[b * G1:b * G1 + w - 1],
+                                  tokens[b, : w - 1], ua[b, : w - 1], ur[b])
+        band = any(m < 1e-6 for m in r["margins"]) or r["draw_margin"] < 1e-9
+        same = acc_h[b] == r["n"] and list(com_h[b, : r["n"] + 1]) == list(r["committed"])
+        if not same:
+            assert band, f"request {b}: {acc_h[b]} {com_h[b]} vs {r['n']} {r['committed']}"
+            flips += 1
+            continue
+        assert np.all(com_h[b, r["n"] + 1:] == -1)
+        assert ctx_h[b] == ctx0[b] + r["n"] + 1
+        np.testing.assert_allclose(lab_h[b, : w - 1], r["labels"], atol=1e-5, rtol=0)
+        assert np.all(np.isnan(lab_h[b, w - 1:]))
+    assert flips <= 1
+
+
+@pytest.mark.parametrize("case", ["all-bonus", "all-full", "mixed", "one-request"])
+def test_accept_edges(case):
+    print(f"[accept-edge] {case}", flush=True)
+    V = 50_000  # not a multiple of the 16384-entry segment: a ragged last segment
+    if case == "all-bonus":
+        _accept_case(8, 6, V, [1] * 8, seed=1)
+    elif case == "all-full":
+        _accept_case(8, 6, V, [6] * 8, seed=2)
+    elif case == "mixed":
+        _accept_case(16, 9, V, [1, 9, 2, 8, 3, 7, 4, 6, 5, 5, 1, 9, 2, 2, 9, 1], seed=3)
+    else:
+        _accept_case(1, 4, V, [4], seed=4)
+
+
+@pytest.mark.parametrize("V", [1000, 16384, 16391])
+def test_accept_odd_vocab(V):
+    """Vocabulary sizes below, at and just past one segment; 16391 is not a multiple of 8,
+    so the unaligned load paths run."""
+    print(f"[accept-vocab] V={V}", flush=True)
+    _accept_case(6, 5, V, [5, 1, 3, 4, 2, 5], seed=V)
+    _accept_case(6, 5, V, [5, 1, 3, 4, 2, 5], seed=V + 1, dtype=torch.float32)
