@@ -47,6 +47,27 @@ def algorithmic_bytes(wl, context_lens, windows):
     return attn, accept, flops
 
 
+def counter_traffic(workload):
+    """HBM bytes per launch of rva_verify_attention from the committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE passes, each scaled by the copy calibration), or None
+    when there is none for this workload or the attention source changed since it was taken."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", f"verify_attention_{workload}_hbm_counters.md")
+    src = os.path.join(ROOT, "ragged_verify_acceptance_amd", "csrc", "attention.hip")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(("|", "#", "*", "cd ")):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if fields.get("attention_source_sha256") != sha or "traffic_bytes_per_launch" not in fields:
+        return None
+    return float(fields["traffic_bytes_per_launch"])
+
+
 def cpu_baseline(inp, windows, n_req):
     """The oracle, single-threaded, on the first n_req requests of the same workload."""
     from threadpoolctl import threadpool_limits
@@ -203,9 +224,10 @@ def main():
             "attn_GBps": attn_gbs, "accept_GBps": acc_gbs,
             "attn_TFLOPs": attn_flops / (t_attn * 1e-3) / 1e12,
         },
-        "roofline": {"kernel": "rva_verify_attention (attn_mfma_kernel + attn_combine_kernel)",
+        "roofline": {"kernel": "rva_verify_attention (attn_sk_kernel + attn_merge_kernel)",
                      "bound": "hbm", "achieved": attn_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": attn_gbs / PEAK_HBM_GBS, "traffic": None},
+                     "frac": attn_gbs / PEAK_HBM_GBS, "traffic": counter_traffic(wl.name),
+                     "algorithmic_bytes": attn_b},
         "device_status": status,
         "host_wall_s": t_host,
     }

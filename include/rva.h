@@ -157,14 +157,21 @@ rva_status rva_pack_ragged(int B, int gamma, const int32_t* windows,
  * Output rows [M, tier) are zeroed.  The window's K/V rows are appended to the cache at
  * positions L_b .. L_b + w_b - 1 (context_lens itself is not changed here).
  *
- * Cache layout (the pages only say "paged, page table on the device"):
- *   k_cache [num_pages, Hkv, page_size, D]   element (page, g, slot, d)
- *   v_cache [num_pages, Hkv, D, page_size]   element (page, g, d, slot)  (V transposed)
+ * Cache layout (the pages only say "paged, page table on the device"; this layout is the
+ * library's choice):
+ *   k_cache [num_pages, Hkv, page_size, D]             element (page, g, slot, d)
+ *   v_cache [num_pages, Hkv, page_size / VB, D, VB]    element (page, g, slot / VB, d, slot % VB)
+ *     V is stored transposed in column blocks of VB slots, VB = 32 when page_size is a
+ *     multiple of 32, else VB = page_size (the whole page is one block).  A block of 32
+ *     keys of one d is 64 contiguous bf16 bytes, so the P.V product reads V in full
+ *     128-byte lines for a 64-slot page instead of half lines.
  *   position p of request b -> page block_table[b * max_pages + p / page_size], slot p % page_size.
  *   Pages the append writes into must not be shared with another request.
  *
  * Arguments
- *   max_window      upper bound of every window (gamma); max_window * (Hq/Hkv) <= 64.
+ *   B               1 <= B <= 65535.
+ *   max_window      upper bound of every window (gamma); max_window * (Hq/Hkv) <= 64
+ *                   (otherwise RVA_ERR_UNSUPPORTED).
  *   max_rows        rows of q / k_new / v_new / out (>= the largest tier).
  *   Hq, Hkv, D      Hq % Hkv == 0; D in {64, 128}.
  *   page_size       >= 1 (the bf16 MFMA path needs a multiple of 32; others take the
@@ -208,12 +215,17 @@ size_t rva_verify_attention_workspace_size(int B, int max_window, int Hq, int Hk
  *   appended KV; y is the next anchor).
  *   [NOTES] section 07: labels[b, k-1] = 1 - 0.5 * ||p_d - p_t||_1 for the same row pair,
  *   k < w (NaN for k >= w).  p_t_at_draft / p_d_at_draft: p_t(x), p_d(x) for k < w (NaN
- *   otherwise).  Normalisers use float32 exp with float64 sums; the draw of y is done in
- *   float64.
+ *   otherwise).
+ *   Precision: the accept test evaluates p_t(x) and p_d(x) in float64 at the drafted token,
+ *   over normalisers summed from float32 exponentials in float64 (relative error ~1e-7);
+ *   the draw of y -- an index that must agree with a float64 definition -- uses float64
+ *   exponentials, float64 normalisers and float64 running sums throughout; the labels sum
+ *   float32 terms in float64 (absolute error well below 1e-5).
  *
  * Arguments
- *   B, gamma, V     V >= 1; gamma as in stage 1.
- *   logit_dtype     RVA_BF16 or RVA_F32.
+ *   B, gamma, V     V >= 1; 2 <= gamma <= 64; B * gamma <= 65535 and
+ *                   max_rows + B * (gamma-1) <= 65535.
+ *   logit_dtype     RVA_BF16 or RVA_F32.  Logit buffers must be 16-byte aligned.
  *   target_logits   [max_rows, V] packed rows; draft_logits [B, gamma-1, V].
  *   draft_tokens    [B, gamma-1] int32; u_accept [B, gamma-1] and u_resample [B] float32
  *                   uniforms in [0, 1).
