@@ -29,8 +29,9 @@
 //                   rescanned with exact weights max(0, e_t - rho e_d) and a block-wide
 //                   prefix sum; then the commit (accept_len, committed, context_lens).
 // The draw returns an index that has to agree with a float64 definition, so everything the
-// draw reads is float64: exp is 2^y by range reduction and a degree-13 Taylor polynomial of
-// 2^f on |f| <= 1/2 (truncation < 2e-16).
+// draw reads is float64: exp is 2^y by range reduction, a 256-entry table of 2^(j/256) and a
+// degree-4 Taylor polynomial of 2^f on |f| <= 1/512 (about 1.5 ulp); the table itself and the
+// few other float64 exponentials use a degree-13 polynomial on |f| <= 1/2.
 #include "rva_common.h"
 
 namespace rva {
@@ -84,6 +85,32 @@ constexpr double kLog2eF64 = 1.4426950408889634074;
 // e^(x - m) in float64 for float32 x <= m (x = -inf gives 0)
 __device__ __forceinline__ double exp_shift_f64(const Exp2Poly& P, float x, float m) {
   return exp2_f64(P, (double(x) - double(m)) * kLog2eF64);
+}
+
+// Faster 2^y in float64 for the bulk of the draw: y = (256 n + j) / 256 + f with k = 256 n + j
+// = rint(256 y) and |f| <= 1/512; 2^y = 2^n * tab[j] * 2^f, tab[j] = 2^(j/256) (built per
+// workgroup in LDS by exp2_f64), 2^f from its Taylor series to degree 4 (truncation
+// < 4e-17).  Relative error about 1.5 ulp.
+__device__ __forceinline__ double exp2_tab(const Exp2Poly& P, const double* tab, double y) {
+  constexpr double kShifter = 0x1.8p52;
+  y = fmax(y, -1100.0);
+  const double s = fma(y, 256.0, kShifter);  // y * 256 is exact; the add rounds it to k
+  const double kd = s - kShifter;
+  const int k = int(__double2loint(s));
+  const double f = fma(kd, -1.0 / 256.0, y);
+  double p = fma(P.c[4], f, P.c[3]);
+  p = fma(p, f, P.c[2]);
+  p = fma(p, f, P.c[1]);
+  p = fma(p, f, 1.0);
+  return ldexp(tab[k & 255] * p, k >> 8);
+}
+__device__ __forceinline__ double exp_shift_tab(const Exp2Poly& P, const double* tab, float x, float m) {
+  return exp2_tab(P, tab, (double(x) - double(m)) * kLog2eF64);
+}
+// Fills tab[j] = 2^(j/256), j < 256 (the workgroup must have >= 256 threads; ends with a barrier).
+__device__ __forceinline__ void fill_exp2_tab(const Exp2Poly& P, double* tab) {
+  if (threadIdx.x < 256) tab[threadIdx.x] = exp2_f64(P, double(threadIdx.x) / 256.0);
+  __syncthreads();
 }
 
 // Per-request decision record written by decide_kernel.
@@ -342,6 +369,14 @@ __global__ __launch_bounds__(kDecideThreads) void decide_kernel(Ctx c, int commi
   const int b = blockIdx.x;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int G1 = c.a.gamma - 1;
+  // wave 0, lane k: the drafted token and its uniform are loaded before the window is known
+  // (they do not depend on it), so that only the logit loads wait for cu_seqlens
+  int x = 0;
+  float u = 0.f;
+  if (commit && wave == 0 && lane < G1) {
+    x = c.a.tokens[size_t(b) * G1 + lane];
+    u = c.a.u_acc[size_t(b) * G1 + lane];
+  }
   if (!req_ok(c, b)) {
     if (tid == 0) {
       flag(c.a.status, RVA_DEV_BAD_WINDOW);
@@ -352,11 +387,9 @@ __global__ __launch_bounds__(kDecideThreads) void decide_kernel(Ctx c, int commi
   const int r0 = c.a.cu[b];
   const int w = c.a.cu[b + 1] - r0;
   // wave 0, lane k < w-1: issue the drafted token's logit loads before the stats sweep
-  float lt = 0.f, ld = 0.f, u = 0.f;
+  float lt = 0.f, ld = 0.f;
   if (commit && wave == 0 && lane < w - 1) {
     const size_t o = size_t(b) * G1 + lane;
-    int x = c.a.tokens[o];
-    u = c.a.u_acc[o];
     if (x < 0 || x >= c.a.V) {
       flag(c.a.status, RVA_DEV_BAD_TOKEN);
       x = x < 0 ? 0 : c.a.V - 1;
@@ -437,14 +470,15 @@ __device__ __forceinline__ void block_sums_f64(double (&v)[N], double (*sm)[N]) 
     }
 }
 
-// blockIdx.y < draw_slots: the draw slot of request blockIdx.y; above: draft pair
-// (blockIdx.y - draw_slots) = b*G1 + k for the labels (when per_pair).
+// blockIdx.y < draw_slots: the draw slot of request blockIdx.y (float64-heavy, dispatched
+// first); above: draft pair (blockIdx.y - draw_slots) = b*G1 + k for the labels (when per_pair).
 template <typename T>
 __global__ __launch_bounds__(kWideThreads) void pair_kernel(Ctx c, int draw_slots, int per_pair) {
   __shared__ double sm[kWideThreads / kWave][kDrawSums + 1];
   __shared__ double smd[kWideThreads / kWave];
-  const int seg = blockIdx.x, y = blockIdx.y;
+  const int seg = blockIdx.x;
   const int G1 = c.a.gamma - 1;
+  const int y = blockIdx.y;
   if (y < draw_slots) {
     const int b = y;
     const Decision d = c.dec[b];
@@ -456,6 +490,8 @@ __global__ __launch_bounds__(kWideThreads) void pair_kernel(Ctx c, int draw_slot
     double v[kDrawSums + 1] = {0.0, 0.0, 0.0, 0.0, 0.0};
     double it = 0.0, id = 0.0;
     if (residual) xd.load(row_ptr<T>(c, d.id_d), c.a.V, seg);
+    __shared__ double tab[256];
+    fill_exp2_tab(c.P, tab);  // overlaps the row loads
     if (lab) {
       it = double(c.nm[d.id_t].y);
       id = double(c.nm[d.id_d].y);
@@ -467,10 +503,10 @@ __global__ __launch_bounds__(kWideThreads) void pair_kernel(Ctx c, int draw_slot
       double gs[kSubSums] = {0.0, 0.0, 0.0};
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const double et = exp_shift_f64(c.P, xt[8 * g + j], d.Mt);
+        const double et = exp_shift_tab(c.P, tab, xt[8 * g + j], d.Mt);
         gs[0] += et;
         if (residual) {
-          const double ed = exp_shift_f64(c.P, xd[8 * g + j], d.Md);
+          const double ed = exp_shift_tab(c.P, tab, xd[8 * g + j], d.Md);
           v[1] += ed;
           const double r = et - d.rho32 * ed;
           if (r > 0.0) {
@@ -584,19 +620,21 @@ __global__ __launch_bounds__(kPickThreads) void pick_kernel(Ctx c, int commit) {
   const int nseg = c.L.nseg;
   if (!req_ok(c, b)) return;
   const int w = c.a.cu[b + 1] - c.a.cu[b];
-  if (c.a.labels && tid < G1) {
-    const size_t o = size_t(b) * G1 + tid;
-    float lab = __int_as_float(0x7fc00000);
-    if (tid < w - 1) {
+  if (c.a.labels) {  // one wave per draft: lanes sum the segment shares of the TV distance
+    for (int k = wave; k < G1; k += kPickThreads / kWave) {
+      const size_t o = size_t(b) * G1 + k;
       double tv = 0.0;
-      for (int s = 0; s < nseg; ++s) tv += c.tv[o * nseg + s];
-      lab = float(1.0 - tv);
+      if (k < w - 1)
+        for (int s = lane; s < nseg; s += kWave) tv += c.tv[o * nseg + s];
+      tv = wave_sum_f64(tv);
+      if (lane == 0) c.a.labels[o] = k < w - 1 ? float(1.0 - tv) : __int_as_float(0x7fc00000);
     }
-    c.a.labels[o] = lab;
   }
   if (!commit) return;
   const Decision d = c.dec[b];
   if (d.n < 0) return;
+  __shared__ double tab[256];
+  fill_exp2_tab(c.P, tab);
   if (wave == 0) {
     double St, Sd;
     draw_totals(c, b, St, Sd);
@@ -633,9 +671,9 @@ __global__ __launch_bounds__(kPickThreads) void pick_kernel(Ctx c, int commit) {
   const int v = s_pos + tid;
   double wgt = 0.0;
   if (v < c.a.V) {
-    wgt = exp_shift_f64(c.P, Elem<T>::load(row_ptr<T>(c, d.id_t), v), d.Mt);
+    wgt = exp_shift_tab(c.P, tab, Elem<T>::load(row_ptr<T>(c, d.id_t), v), d.Mt);
     if (residual) {
-      wgt -= s_rho * exp_shift_f64(c.P, Elem<T>::load(row_ptr<T>(c, d.id_d), v), d.Md);
+      wgt -= s_rho * exp_shift_tab(c.P, tab, Elem<T>::load(row_ptr<T>(c, d.id_d), v), d.Md);
       wgt = wgt > 0.0 ? wgt : 0.0;
     }
   }

@@ -345,7 +345,12 @@ template <int D, int NB, int NBMAX>
 __device__ __forceinline__ void run_segment(const AttnArgs& a, SkShared<D, NBMAX>& sh, int b, int g, int t0, int n, bool full,
                             int slot_index) {
   constexpr int DS = D / 32, DB = D / 16;
-  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  // The thread index passes through an empty asm so that the lane-constant addresses below
+  // are recomputed per segment instead of being hoisted to the kernel entry, where they
+  // would stay live (for every instantiation) across the whole kernel.
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int wave = tid / kWave, lane = tid % kWave;
   const int lc = lane % 16, lq = lane / 16;
   const int L = sh.tab.L[b], r0 = sh.tab.r0[b], w = sh.tab.w[b], Lw = L + w;
   const int Hkv = a.Hkv, P = a.page_size, G = a.Hq / a.Hkv, nq = w * G;
@@ -582,8 +587,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_sk_kernel(AttnArgs a) {
       const bool full = (t0 == 0 && t_end == nt);
       const int slot = blockIdx.x * 2 + (x0 < seg_w0 ? 1 : 0);
       const int cols = sh.tab.w[b] * G;
-      if (cols <= 16) run_segment<D, 1, NBMAX>(a, sh, b, g, t0, n, full, slot);
-      else if (cols <= 32) run_segment<D, (NBMAX >= 2 ? 2 : 1), NBMAX>(a, sh, b, g, t0, n, full, slot);
+      if (NBMAX == 1 || cols <= 16) run_segment<D, 1, NBMAX>(a, sh, b, g, t0, n, full, slot);
+      else if (NBMAX == 2 || cols <= 32) run_segment<D, (NBMAX >= 2 ? 2 : 1), NBMAX>(a, sh, b, g, t0, n, full, slot);
       else run_segment<D, NBMAX, NBMAX>(a, sh, b, g, t0, n, full, slot);
     }
     x = min(x1, seg_w1);

@@ -93,24 +93,30 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(
     }
   }
 
+  // largest b with cu[b] <= r (rows r < M)
+  auto owner = [&](int r) {
+    int lo = 0, hi = B - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (cu[mid] <= r) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+  };
+  // row metadata: one thread per row of this block, so the context_lens loads overlap
+  if (tid < kRowsPerBlock) {
+    const int r = blockIdx.x * kRowsPerBlock + tid;
+    if (r < max_rows) {
+      const int b = r < M ? owner(r) : -1;
+      row_req[r] = b;
+      row_pos[r] = b >= 0 ? context_lens[b] + (r - cu[b]) : -1;
+    }
+  }
+  if (!src) return;
   for (int rr = 0; rr < kRowsPerBlock; ++rr) {
     const int r = blockIdx.x * kRowsPerBlock + rr;
-    if (r >= max_rows) break;
-    int b = -1, i = 0;
-    if (r < M) {
-      int lo = 0, hi = B - 1;  // largest b with cu[b] <= r
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (cu[mid] <= r) lo = mid; else hi = mid - 1;
-      }
-      b = lo;
-      i = r - cu[b];
-    }
-    if (tid == 0) {
-      row_req[r] = b;
-      row_pos[r] = b >= 0 ? context_lens[b] + i : -1;
-    }
-    if (!src || r >= tier) continue;
+    if (r >= max_rows || r >= tier) break;
+    const int b = r < M ? owner(r) : -1;
+    const int i = b >= 0 ? r - cu[b] : 0;
     uint8_t* d = dst + size_t(r) * row_bytes;
     const uint8_t* s = b >= 0 ? src + (size_t(b) * gamma + i) * row_bytes : nullptr;
     const bool vec16 = (row_bytes % 16 == 0) && ((reinterpret_cast<uintptr_t>(src) |

@@ -150,6 +150,16 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(
   int Npad = 2;
   while (Npad < N) Npad <<= 1;
 
+  // the cost table entries this thread needs later (rank r = tid*E + e uses theta[B + r + 1])
+  // are loaded now, so their round trip overlaps the survival products and the sort
+  float th[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int r = tid * E + e;
+    th[e] = r < N ? theta[B + r + 1] : 0.f;
+  }
+  const float alpha_B = alpha[B], theta_0 = theta[B];
+  const float theta_N = theta[B + N];
   // (1) survival: the confidences are staged in LDS by one coalesced load, then one lane per
   // request forms the float32 products left to right
   for (int i = tid; i < N; i += kSchedThreads) {
@@ -199,21 +209,22 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(
   double prefix = block_exclusive_scan_f64(run, wave_tot, &total);
 
   // (4) ratio (B + S_K) / T(B, K); K = r + 1 for rank r, K = 0 handled by thread 0
-  const double ba = double(bias) + double(alpha[B]);
+  const double ba = double(bias) + double(alpha_B);
   double best = -INFINITY;
   int bestK = 0x7fffffff;
   if (tid == 0) {
-    const double T0 = ba + double(theta[B]);
+    const double T0 = ba + double(theta_0);
     if (!(T0 > 0.0)) flag(status, RVA_DEV_BAD_COST);
     best = T0 > 0.0 ? double(B) / T0 : -INFINITY;
     bestK = 0;
   }
   double S = prefix;
+#pragma unroll
   for (int i = 0; i < per; ++i) {
     const int r = r0 + i;
     if (r < N) {
       S += double(__uint_as_float(~uint32_t(keys[r] >> 32)));
-      const double T = ba + double(theta[B + r + 1]);
+      const double T = ba + double(th[i]);
       if (!(T > 0.0)) flag(status, RVA_DEV_BAD_COST);
       const double ratio = T > 0.0 ? (double(B) + S) / T : -INFINITY;
       if (ratio > best) {
@@ -260,7 +271,7 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(
   double ratio = red_ratio[0];
   if (mode == RVA_MODE_STATIC) {
     Kstar = N;
-    const double T = ba + double(theta[B + N]);
+    const double T = ba + double(theta_N);
     ratio = T > 0.0 ? (double(B) + total) / T : -INFINITY;
   }
 
