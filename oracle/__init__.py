@@ -18,7 +18,8 @@ Sources (web pages; cited by title and section, never by a line of any copy):
           "Confidence scheduler 与 verify 模式", "Ragged verify under full CUDA graphs".
 * [CSDN]  the devpress.csdn.net (awstech) article on DSpark in SGLang, sections
           "2. DSpark如何实现真正的动态验证预算", "3. 可变长度验证的工程实现挑战",
-          "4. 零开销调度如何隐藏计算成本" (the additive step-cost model T(bs, K)).
+          "4. 零开销调度如何隐藏计算成本" (the additive step-cost model T(bs, K)),
+          "5. 可观测性：理解修剪下的真实性能" (the cap-accept verify mode).
 * [NOTES] "DSpark：投机解码与生产级 Serving 学习笔记" (sorenprojections.com),
           sections "02 · Speculative Decoding", "07 · Confidence Head",
           "08 · Core Innovation B", "09 · End-to-End Cycle".
@@ -33,7 +34,8 @@ identity T = 1 and the limits are pinned).
 from .scheduling import confidence_from_head, survival, schedule_windows
 from .packing import pack_ragged
 from .attention import verify_attention
-from .acceptance import softmax64, inverse_cdf, accept_request, accept_and_commit, confidence_labels
+from .acceptance import (softmax64, inverse_cdf, accept_request, accept_request_capped,
+                         accept_and_commit, confidence_labels)
 
 __all__ = [
     "confidence_from_head",
@@ -44,6 +46,7 @@ __all__ = [
     "softmax64",
     "inverse_cdf",
     "accept_request",
+    "accept_request_capped",
     "accept_and_commit",
     "confidence_labels",
 ]

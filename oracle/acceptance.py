@@ -99,6 +99,57 @@ def tv_label(p_d, p_t):
     return 1.0 - 0.5 * float(np.sum(np.abs(np.asarray(p_d) - np.asarray(p_t))))
 
 
+def accept_request_capped(target_rows, draft_rows, tokens, u_accept, u_resample, cap):
+    """Cap-accept verify mode for one request.
+
+    [SGL] "Confidence scheduler 与 verify 模式" and [CSDN] section 5: the whole drafted block
+    is verified (as in static mode) but only positions inside the scheduler's window may be
+    committed, so the commit is the one compact mode makes for that window, while the
+    acceptance the whole block would have reached -- the ceiling the trimming gave up -- is
+    recorded as well.
+
+    ``target_rows`` [w, V] are the target logits of the whole verified block (w rows,
+    anchor included), ``draft_rows`` [w-1, V]; ``cap`` in [1, w] is the window.
+
+    * n_full: accepted drafts over the whole block (first rejection among drafts 1..w-1);
+    * committed drafts n = min(n_full, cap - 1);
+    * y: when the block rejects inside the window (n_full < cap - 1) the residual draw of
+      that rejection, otherwise the bonus draw from p_t of row cap - 1 -- compact mode's
+      draw for the window cap;
+    * labels, p_t(x), p_d(x) for every draft of the block.
+    Returns the ``accept_request`` fields plus ``n_full``.
+    """
+    w = len(target_rows)
+    cap = int(cap)
+    assert 1 <= cap <= w
+    p_t = [softmax64(r) for r in target_rows]
+    p_d = [softmax64(r) for r in draft_rows]
+    pt_at = [float(p_t[k - 1][int(tokens[k - 1])]) for k in range(1, w)]
+    pd_at = [float(p_d[k - 1][int(tokens[k - 1])]) for k in range(1, w)]
+    labels = [tv_label(p_d[k - 1], p_t[k - 1]) for k in range(1, w)]
+    margins = []
+    n_full = w - 1
+    for k in range(1, w):  # the whole block, as the full verify sees it
+        pt, pd = pt_at[k - 1], pd_at[k - 1]
+        r = np.inf if pd == 0.0 else pt / pd
+        u = float(np.float32(u_accept[k - 1]))
+        margins.append(abs(u - r))
+        if not u < min(1.0, r):
+            n_full = k - 1
+            break
+    n = min(n_full, cap - 1)
+    if n_full < cap - 1:  # rejected inside the window: residual of that pair
+        dist = np.maximum(0.0, p_t[n] - p_d[n])
+        if not np.sum(dist) > 0.0:
+            dist = p_t[n]
+    else:  # the window's drafts all survive: bonus from the window's last target row
+        dist = p_t[cap - 1]
+    y, draw_margin = inverse_cdf(dist, float(np.float32(u_resample)))
+    committed = [int(tokens[i]) for i in range(n)] + [y]
+    return {"n": n, "n_full": n_full, "committed": committed, "margins": margins,
+            "draw_margin": draw_margin, "labels": labels, "pt_at": pt_at, "pd_at": pd_at}
+
+
 def accept_and_commit(target_logits, draft_logits, draft_tokens, u_accept, u_resample,
                       windows, cu_seqlens, context_lens):
     """Batch driver: one ``accept_request`` per request, then the commit bookkeeping.

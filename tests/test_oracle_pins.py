@@ -535,3 +535,40 @@ def test_batch_driver_layout():
     assert res["committed"][1, 0] == oracle.inverse_cdf(oracle.softmax64(tl[cu[1]]), ur[1])[0]
     lab = oracle.confidence_labels(tl, dl, windows, cu)
     assert np.allclose(lab, res["labels"], equal_nan=True)
+
+
+# ---------------------------------------------------------------- cap-accept verify mode
+
+
+def test_cap_accept_commits_what_compact_commits():
+    """Cap-accept ([SGL] "Confidence scheduler 与 verify 模式"; [CSDN] section 5) verifies the
+    whole block but commits only inside the window: its commit must equal compact mode's
+    commit for that window, and its ceiling must equal the whole block's (static mode's)
+    acceptance.  Checked over many seeded cases, with drafts close to the target (long
+    acceptances, so the cap binds) and far from it (early rejections)."""
+    rng = np.random.default_rng(21)
+    checked_binding = checked_free = 0
+    for case in range(300):
+        V, w = 12, int(rng.integers(1, 8))
+        t = rng.standard_normal((w, V)) * 1.5
+        noise = 0.05 if case % 2 == 0 else 1.5
+        d = t[: w - 1] + rng.standard_normal((w - 1, V)) * noise
+        tokens = np.array([int(np.argmax(d[k] + rng.gumbel(size=V))) for k in range(w - 1)], np.int64)
+        ua = rng.random(w - 1).astype(np.float32)
+        ur = np.float32(rng.random())
+        full = oracle.accept_request(t, d, tokens, ua, ur)
+        for cap in range(1, w + 1):
+            capped = oracle.accept_request_capped(t, d, tokens, ua, ur, cap)
+            compact = oracle.accept_request(t[:cap], d[: cap - 1], tokens[: cap - 1], ua[: cap - 1], ur)
+            assert capped["n"] == compact["n"]
+            assert capped["committed"] == compact["committed"]
+            assert capped["n_full"] == full["n"]
+            assert capped["n"] <= capped["n_full"]
+            if capped["n_full"] > capped["n"]:
+                checked_binding += 1
+            else:
+                checked_free += 1
+            if cap == w:  # no cap: the whole-block result
+                assert capped["committed"] == full["committed"]
+            np.testing.assert_allclose(capped["labels"], full["labels"], rtol=0, atol=0)
+    assert checked_binding > 50 and checked_free > 50
