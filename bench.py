@@ -119,7 +119,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="mixed-b64")
-    ap.add_argument("--mode", default="compact", choices=["compact", "static"])
+    ap.add_argument("--mode", default="compact", choices=["compact", "static", "cap-accept"],
+                    help="cap-accept: whole blocks verified, commits capped at the scheduled windows")
     ap.add_argument("--cpu-sample", type=int, default=24, help="requests in the oracle sample (0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 1 GiB device-to-device copy first (counter calibration)")
@@ -140,8 +141,13 @@ def main():
     torch.cuda.set_device(0)
     wl = get(args.workload)
     inp = Inputs(wl)
-    ds = DeviceStep(inp, mode=args.mode)
+    capped = args.mode == "cap-accept"
+    ds = DeviceStep(inp, mode="compact" if capped else args.mode)
     ds.prepare()
+    if capped:
+        from workloads.device import prepare_with_windows
+        caps = ds.windows.cpu().numpy()
+        prepare_with_windows(ds, np.full(inp.B, wl.gamma))
     torch.cuda.synchronize()
     windows = ds.windows.cpu().numpy()
     M, tier = (int(x) for x in ds.total_tier.cpu().numpy())
@@ -158,7 +164,10 @@ def main():
 
     def step():
         ds.restore()
-        ds.step()
+        if capped:
+            ds.step_capped()
+        else:
+            ds.step()
 
     for _ in range(args.warmup):
         step()
@@ -184,11 +193,17 @@ def main():
         ds.restore()
         ev[i][0].record(stream)
         ds.schedule()
+        if capped:
+            ds.cap_windows.copy_(ds.windows)
+            ds.windows.fill_(wl.gamma)
         ds.pack()
         ev[i][1].record(stream)
         ds.attention()
         ev[i][2].record(stream)
-        ds.accept(labels=True)
+        if capped:
+            ds.accept_capped(None)
+        else:
+            ds.accept(labels=True)
         ev[i][3].record(stream)
     torch.cuda.synchronize()
     t_front = np.mean([ev[i][0].elapsed_time(ev[i][1]) for i in range(n_ev)])
@@ -229,8 +244,15 @@ def main():
                      "frac": attn_gbs / PEAK_HBM_GBS, "traffic": counter_traffic(wl.name),
                      "algorithmic_bytes": attn_b},
         "device_status": status,
+        "committed_tokens_per_step": int(ds.accept_len.sum().item()) + inp.B,
         "host_wall_s": t_host,
     }
+    if capped:
+        acc = int(ds.accept_len.sum().item())
+        full = int(ds.accept_len_full.sum().item())
+        res["cap_accept"] = {"accepted_drafts_capped": acc, "accepted_drafts_uncapped": full,
+                             "utilisation": acc / max(1, full),
+                             "mean_cap_window": float(caps.mean())}
     if args.cpu_sample > 0:
         res["cpu_baseline"] = cpu_baseline(inp, windows, min(args.cpu_sample, inp.B))
     print(json.dumps(res))

@@ -1,7 +1,7 @@
 /*
  * rva.h -- C ABI of the ragged verify + acceptance library (librva.so, gfx950 / MI355X).
  *
- * One speculative-decoding step, verify side, as five calls that each only enqueue HIP
+ * One speculative-decoding step, verify side, as five calls (and a measurement variant) that each only enqueue HIP
  * kernels on the caller's stream:
  *
  *   rva_schedule_windows   stage 1  confidence head + temperature scaling, prefix
@@ -11,6 +11,8 @@
  *   rva_accept_and_commit  stage 4  speculative-sampling acceptance, draw, commit
  *                          (+ stage 5 TV labels when `labels` is given)
  *   rva_confidence_labels  stage 5  TV-distance confidence labels on their own
+ *   rva_accept_capped      stage 4 in cap-accept mode (whole block verified, commit capped
+ *                          at the window, uncapped acceptance reported)
  *
  * Sources, cited by page title and section:
  *   [SGL]   "DFlash 到 DSpark in SGLang：解码提速 4.3×，以及 DeepSeek-V4 支持"
@@ -246,6 +248,41 @@ rva_status rva_accept_and_commit(int B, int gamma, int V, int logit_dtype, int m
                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 size_t rva_accept_workspace_size(int B, int gamma, int V, int max_rows);
+
+/*
+ * Stage 4 in cap-accept mode -- rva_accept_capped
+ *
+ * [SGL] "Confidence scheduler 与 verify 模式" and [CSDN] section 5: the verify ran on the
+ * whole drafted block (as in static mode), but only positions inside the scheduler's window
+ * may be committed.  The commit is therefore the one compact mode makes for that window,
+ * and the acceptance the whole block would have reached -- the ceiling the trimming gave
+ * up -- is reported beside it (a measurement arm, not the production path).
+ *
+ * With w = cu[b+1]-cu[b] verified rows (normally gamma) and cap = cap_windows[b] in [1, w]:
+ *   n_full = drafts accepted over the whole block (the rule of rva_accept_and_commit over
+ *            all w-1 drafts)  -> accept_len_full[b];
+ *   n = min(n_full, cap - 1) -> accept_len[b];
+ *   y = the residual draw of the rejecting pair when n_full < cap - 1, else the bonus draw
+ *       from p_t of row cu[b] + cap - 1;
+ *   committed[b] = x_1..x_n, y, then -1;  context_lens[b] += n + 1.
+ * p_t_at_draft / p_d_at_draft / labels cover every draft of the verified block (k < w).
+ * The utilisation of the acceptance ceiling is sum(accept_len) / sum(accept_len_full).
+ *
+ * Arguments: as rva_accept_and_commit, plus
+ *   cap_windows     [B] int32 (device) windows of the commit cap, anchor included;
+ *                   outside [1, w] sets RVA_DEV_BAD_WINDOW and is clamped.
+ *   accept_len_full [B] int32 output.
+ * The workspace is the one of rva_accept_and_commit (rva_accept_workspace_size).
+ */
+rva_status rva_accept_capped(int B, int gamma, int V, int logit_dtype, int max_rows,
+                             const void* target_logits, const void* draft_logits,
+                             const int32_t* draft_tokens, const float* u_accept,
+                             const float* u_resample, const int32_t* cu_seqlens,
+                             const int32_t* cap_windows, int32_t* accept_len,
+                             int32_t* accept_len_full, int32_t* committed,
+                             int32_t* context_lens, float* p_t_at_draft, float* p_d_at_draft,
+                             float* labels, int32_t* device_status, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Stage 5 on its own -- rva_confidence_labels

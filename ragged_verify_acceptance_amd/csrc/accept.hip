@@ -436,17 +436,31 @@ __global__ __launch_bounds__(kDecideThreads) void decide_kernel(Ctx c, int commi
   }
   // first rejected draft (G1 <= 63: one lane per draft)
   const unsigned long long rej = __ballot(reject);
-  const int n = rej ? __ffsll(rej) - 1 : w - 1;
+  const int n_full = rej ? __ffsll(rej) - 1 : w - 1;
+  // cap-accept: the whole block was verified, but only drafts inside the window (cap - 1 of
+  // them) may be committed; a rejection inside the window draws its residual, otherwise the
+  // bonus comes from the window's last target row -- what compact mode does for that window
+  int cap = w;
+  if (c.a.cap) {
+    cap = c.a.cap[b];
+    if (cap < 1 || cap > w) {
+      if (lane == 0) flag(c.a.status, RVA_DEV_BAD_WINDOW);
+      cap = cap < 1 ? 1 : w;
+    }
+  }
+  const bool residual = n_full < cap - 1;
+  const int n = residual ? n_full : cap - 1;
   if (lane == 0) {
     Decision d;
     d.n = n;
     d.id_t = r0 + n;
-    d.id_d = n < w - 1 ? c.a.max_rows + b * G1 + n : -1;
+    d.id_d = residual ? c.a.max_rows + b * G1 + n : -1;
     d.pad = 0;
     d.Mt = sM[n];
-    d.Md = n < w - 1 ? sM[w + n] : 0.f;
-    d.rho32 = n < w - 1 ? sS[n] / sS[w + n] : 0.0;
+    d.Md = residual ? sM[w + n] : 0.f;
+    d.rho32 = residual ? sS[n] / sS[w + n] : 0.0;
     c.dec[b] = d;
+    if (c.a.accept_len_full) c.a.accept_len_full[b] = n_full;
   }
 }
 

@@ -217,7 +217,7 @@ rva_status rva_accept_and_commit(int B, int gamma, int V, int logit_dtype, int m
   if (s != RVA_OK) return s;
   REQUIRE(draft_tokens && u_accept && u_resample, "draft_tokens, u_accept and u_resample are required");
   REQUIRE(accept_len && committed && context_lens, "accept_len, committed and context_lens are required");
-  rva::AcceptArgs a;
+  rva::AcceptArgs a{};
   a.B = B;
   a.gamma = gamma;
   a.V = V;
@@ -237,6 +237,46 @@ rva_status rva_accept_and_commit(int B, int gamma, int V, int logit_dtype, int m
   a.status = device_status;
   a.ws = workspace;
   return hip_result(rva::launch_accept(a, logit_dtype, true, stream), "rva_accept_and_commit launch");
+}
+
+rva_status rva_accept_capped(int B, int gamma, int V, int logit_dtype, int max_rows,
+                             const void* target_logits, const void* draft_logits,
+                             const int32_t* draft_tokens, const float* u_accept,
+                             const float* u_resample, const int32_t* cu_seqlens,
+                             const int32_t* cap_windows, int32_t* accept_len,
+                             int32_t* accept_len_full, int32_t* committed, int32_t* context_lens,
+                             float* p_t_at_draft, float* p_d_at_draft, float* labels,
+                             int32_t* device_status, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+  rva_status s = accept_common("rva_accept_capped", B, gamma, V, logit_dtype, max_rows,
+                               target_logits, draft_logits, cu_seqlens, workspace, workspace_bytes);
+  if (s != RVA_OK) return s;
+  REQUIRE(draft_tokens && u_accept && u_resample, "draft_tokens, u_accept and u_resample are required");
+  REQUIRE(cap_windows != nullptr, "cap_windows is required");
+  REQUIRE(accept_len && accept_len_full && committed && context_lens,
+          "accept_len, accept_len_full, committed and context_lens are required");
+  rva::AcceptArgs a{};
+  a.B = B;
+  a.gamma = gamma;
+  a.V = V;
+  a.max_rows = max_rows;
+  a.target = target_logits;
+  a.draft = draft_logits;
+  a.tokens = draft_tokens;
+  a.u_acc = u_accept;
+  a.u_res = u_resample;
+  a.cu = cu_seqlens;
+  a.accept_len = accept_len;
+  a.committed = committed;
+  a.context_lens = context_lens;
+  a.pt_at = p_t_at_draft;
+  a.pd_at = p_d_at_draft;
+  a.labels = labels;
+  a.status = device_status;
+  a.ws = workspace;
+  a.cap = cap_windows;
+  a.accept_len_full = accept_len_full;
+  return hip_result(rva::launch_accept(a, logit_dtype, true, stream), "rva_accept_capped launch");
 }
 
 rva_status rva_confidence_labels(int B, int gamma, int V, int logit_dtype, int max_rows,

@@ -112,6 +112,8 @@ struct AcceptArgs {
   float* labels;
   int32_t* status;
   void* ws;
+  const int32_t* cap;        // cap-accept mode: commit cap (window) per request, else NULL
+  int32_t* accept_len_full;  // cap-accept mode: accepted drafts over the whole block
 };
 size_t accept_workspace_bytes(int B, int gamma, int V, int max_rows);
 hipError_t launch_accept(const AcceptArgs& a, int logit_dtype, bool commit, hipStream_t stream);

@@ -34,7 +34,8 @@ _STATUS = {0: "RVA_OK", 1: "RVA_ERR_INVALID_ARGUMENT", 2: "RVA_ERR_UNSUPPORTED",
 EXPORTED = [
     "rva_schedule_windows", "rva_pack_ragged", "rva_verify_attention",
     "rva_verify_attention_workspace_size", "rva_accept_and_commit",
-    "rva_accept_workspace_size", "rva_confidence_labels", "rva_last_error", "rva_version",
+    "rva_accept_workspace_size", "rva_confidence_labels", "rva_accept_capped", "rva_last_error",
+    "rva_version",
 ]
 
 
@@ -59,6 +60,8 @@ _SIGS = {
                               _p, _p, _p, _z, _p],
     "rva_accept_workspace_size": [_i, _i, _i, _i],
     "rva_confidence_labels": [_i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _z, _p],
+    "rva_accept_capped": [_i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p,
+                          _p, _p, _p, _z, _p],
     "rva_last_error": [],
     "rva_version": [],
 }
@@ -179,3 +182,16 @@ def confidence_labels(B, gamma, V, max_rows, target_logits, draft_logits, cu_seq
         B, gamma, V, dtype_code(target_logits), max_rows, _ptr(target_logits),
         _ptr(draft_logits), _ptr(cu_seqlens), _ptr(labels), _ptr(device_status),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def accept_capped(B, gamma, V, max_rows, target_logits, draft_logits, draft_tokens, u_accept,
+                  u_resample, cu_seqlens, cap_windows, accept_len, accept_len_full, committed,
+                  context_lens, p_t_at_draft, p_d_at_draft, labels, workspace,
+                  device_status=None, stream=None):
+    _check("rva_accept_capped", lib().rva_accept_capped(
+        B, gamma, V, dtype_code(target_logits), max_rows, _ptr(target_logits),
+        _ptr(draft_logits), _ptr(draft_tokens), _ptr(u_accept), _ptr(u_resample),
+        _ptr(cu_seqlens), _ptr(cap_windows), _ptr(accept_len), _ptr(accept_len_full),
+        _ptr(committed), _ptr(context_lens), _ptr(p_t_at_draft), _ptr(p_d_at_draft),
+        _ptr(labels), _ptr(device_status), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))

@@ -96,6 +96,18 @@ def oracle_accept(inp: Inputs, windows, reqs):
     return res
 
 
+def oracle_accept_capped(inp: Inputs, caps, reqs):
+    """Cap-accept results for `reqs`: the whole block verified, commit capped at caps[b]."""
+    ua, ur = inp.uniforms()
+    res = {}
+    w = inp.wl.gamma
+    for b in reqs:
+        tl, dl, toks = inp.request_logits(b)
+        res[b] = oracle.accept_request_capped(tl[:w].double().numpy(), dl[: w - 1].double().numpy(),
+                                              toks[: w - 1], ua[b, : w - 1], ur[b], int(caps[b]))
+    return res
+
+
 def attn_rel_err(out, ref):
     """max over (row, head) vectors of max|o - r| / max|r|."""
     out = np.asarray(out, np.float64)

@@ -29,7 +29,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     L = rva.lib()
     names = declared_functions()
-    assert "rva_verify_attention" in names and len(names) == 9
+    assert "rva_verify_attention" in names and len(names) == 10
     for n in names:
         assert hasattr(L, n), f"{n} declared in rva.h but not exported"
     assert set(names) == set(rva.EXPORTED)
@@ -126,3 +126,18 @@ def test_accept_validation():
     assert _accept(max_rows=70000) == INVALID   # grid rows beyond 65535
     big = rva.accept_workspace_size(256, 16, 151936, 4096)
     assert big > rva.accept_workspace_size(64, 8, 151936, 512) > 0
+
+
+def _capped(cap=FAKE, full=FAKE, B=2, gamma=6, V=1024, ws=FAKE):
+    ws_bytes = rva.accept_workspace_size(B, gamma, V, 16)
+    return rva.lib().rva_accept_capped(B, gamma, V, 1, 16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, cap,
+                                       FAKE, full, FAKE, FAKE, None, None, None, None, ws, ws_bytes,
+                                       None)
+
+
+def test_accept_capped_validation():
+    assert _capped(cap=None) == INVALID            # the commit cap is required
+    assert _capped(full=None) == INVALID           # so is the uncapped accept length
+    assert _capped(B=0) == INVALID
+    assert _capped(gamma=65) == INVALID
+    assert _capped(ws=None) == WS_SMALL

@@ -18,8 +18,8 @@ import numpy as np
 import pytest
 import torch
 
-from tests.reference import (attn_rel_err, oracle_accept, oracle_attention, oracle_schedule,
-                             to_np)
+from tests.reference import (attn_rel_err, oracle_accept, oracle_accept_capped,
+                             oracle_attention, oracle_schedule, to_np)
 import oracle
 from workloads import Inputs, get
 from workloads.device import DeviceStep, prepare_with_windows, upload_windows
@@ -192,6 +192,53 @@ def test_accept(ds, mode):
     assert _status(ds) == 0
     flips = _accept_compare(ds, name, windows, _sample(name, inp.B))
     assert flips <= 1
+
+
+def test_accept_capped(ds):
+    """Cap-accept: whole blocks verified, commits capped at the scheduled windows.  Against the
+    oracle, and against the GPU's own compact run on the same inputs (the commits must be
+    identical: that is what the mode is for)."""
+    name = ds.wl.name
+    if name in ("long-b32", "high-conc-b256"):
+        pytest.skip("covered on the three smaller workloads")
+    print(f"[accept-capped] {name}", flush=True)
+    inp, wl = ds.inp, ds.wl
+    caps = oracle_schedule(inp)["windows"]
+    prepare_with_windows(ds, np.full(inp.B, wl.gamma))
+    ds.restore()
+    ds.status.zero_()
+    ds.accept_capped(caps)
+    torch.cuda.synchronize()
+    assert _status(ds) == 0
+    acc, full = to_np(ds.accept_len).copy(), to_np(ds.accept_len_full).copy()
+    com, ctx = to_np(ds.committed).copy(), to_np(ds.context_lens).copy()
+    lab = to_np(ds.labels).copy()
+    reqs = _sample(name, inp.B)
+    ref = oracle_accept_capped(inp, caps, reqs)
+    flips = 0
+    G1 = wl.gamma - 1
+    for b in reqs:
+        r = ref[b]
+        band = any(m < 1e-6 for m in r["margins"]) or r["draw_margin"] < 1e-9
+        ok = acc[b] == r["n"] and full[b] == r["n_full"] and \
+            list(com[b, : r["n"] + 1]) == r["committed"] and np.all(com[b, r["n"] + 1:] == -1) and \
+            ctx[b] == inp.context_lens[b] + r["n"] + 1
+        if not ok:
+            assert band, f"request {b}: GPU {acc[b]}/{full[b]} {list(com[b])} vs {r['n']}/{r['n_full']} {r['committed']}"
+            flips += 1
+        assert np.all(np.abs(lab[b, :G1] - np.array(r["labels"])) <= PROB_TOL)
+    assert flips <= 1
+    assert np.all(acc <= full) and np.all(acc <= caps - 1)
+    util = acc.sum() / max(1, full.sum())
+    print(f"  cap-accept utilisation of the ceiling: {util:.3f} ({acc.sum()} / {full.sum()} drafts)")
+    # the GPU's compact run with windows = caps commits exactly the same tokens
+    prepare_with_windows(ds, caps)
+    ds.restore()
+    ds.accept()
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(ds.accept_len), acc)
+    assert np.array_equal(to_np(ds.committed), com)
+    assert np.array_equal(to_np(ds.context_lens), ctx)
 
 
 def test_labels_standalone(ds):

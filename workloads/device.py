@@ -103,6 +103,8 @@ class DeviceStep:
         self.pt_at = torch.empty((B, G1), **f32)
         self.pd_at = torch.empty((B, G1), **f32)
         self.labels = torch.empty((B, G1), **f32)
+        self.accept_len_full = torch.empty(B, **i32)  # cap-accept mode
+        self.cap_windows = torch.empty(B, **i32)
         self.acc_ws = torch.empty(rva.accept_workspace_size(B, gamma, wl.V, self.max_rows),
                                   dtype=torch.uint8, device=dev)
 
@@ -138,6 +140,18 @@ class DeviceStep:
                               self.pd_at if probs else None, self.labels if labels else None,
                               self.acc_ws, self.status)
 
+    def accept_capped(self, caps=None, labels=True):
+        """Cap-accept arm: the packed rows hold whole blocks; commits are capped at `caps`
+        (host array), or at the device windows already in `cap_windows` when None."""
+        wl = self.wl
+        if caps is not None:
+            self.cap_windows.copy_(torch.as_tensor(np.asarray(caps, np.int32)).to(self.dev))
+        rva.accept_capped(self.B, wl.gamma, wl.V, self.max_rows, self.target_logits,
+                          self.draft_logits, self.draft_tokens, self.u_accept, self.u_resample,
+                          self.cu, self.cap_windows, self.accept_len, self.accept_len_full,
+                          self.committed, self.context_lens, self.pt_at, self.pd_at,
+                          self.labels if labels else None, self.acc_ws, self.status)
+
     def labels_only(self, out):
         wl = self.wl
         rva.confidence_labels(self.B, wl.gamma, wl.V, self.max_rows, self.target_logits,
@@ -156,6 +170,17 @@ class DeviceStep:
 
     def restore(self):
         self.context_lens.copy_(self.context_lens0)
+
+    def step_capped(self, labels=True):
+        """One cap-accept step: schedule (compact) -> the windows become the commit cap ->
+        pack and verify whole blocks -> accept with the cap.  The packed inputs must be laid
+        out for whole blocks (prepare_with_windows with gamma everywhere)."""
+        self.schedule()
+        self.cap_windows.copy_(self.windows)
+        self.windows.fill_(self.wl.gamma)
+        self.pack()
+        self.attention()
+        self.accept_capped(None, labels=labels)
 
     def step(self, labels=True):
         """One pass of the whole path: stages 1, 2, 3 and 4 (+5)."""
