@@ -566,6 +566,64 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, SkShared<D, NBMAX
   __syncthreads();  // LDS merge buffers are reused by the next segment
 }
 
+// Appends request b's window K/V for kv head g at cache positions L .. L+w-1 (after the main
+// kernel, which took those keys from k_new / v_new).  A pass moves kThreads 4-element K
+// pieces (consecutive threads: consecutive pieces of one key row, a contiguous cache row) and
+// 4 kThreads V elements (consecutive threads: consecutive slots of one d, contiguous in the
+// transposed column blocks); every load of a pass is issued before its first store, so a
+// window of up to 8 rows at D = 128 costs one round trip.
+template <int D>
+__device__ __forceinline__ void append_window(const AttnArgs& a, int b, int g, int L, int r0, int w) {
+  const int Hkv = a.Hkv, P = a.page_size;
+  const uint16_t* kn = static_cast<const uint16_t*>(a.k_new);
+  const uint16_t* vn = static_cast<const uint16_t*>(a.v_new);
+  uint16_t* kcw = static_cast<uint16_t*>(a.k_cache);
+  uint16_t* vcw = static_cast<uint16_t*>(a.v_cache);
+  const int* bt = a.block_table + size_t(b) * a.max_pages;
+  const int tid = threadIdx.x, n = w * D;
+  for (int base = 0; base < n; base += 4 * kThreads) {
+    const int ik = base / 4 + tid;
+    const bool kok = ik < n / 4;
+    const int kj = kok ? ik / (D / 4) : 0, kd = (ik % (D / 4)) * 4;
+    const int kpg = kok ? bt[(L + kj) / P] : 0;
+    const uint2 kval =
+        kok ? *reinterpret_cast<const uint2*>(kn + (size_t(r0 + kj) * Hkv + g) * D + kd) : make_uint2(0, 0);
+    int vpg[4];
+    uint16_t vval[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int iv = base + e * kThreads + tid;
+      const int vj = iv % w, vd = iv / w;
+      vpg[e] = iv < n ? bt[(L + vj) / P] : -1;
+      vval[e] = iv < n ? vn[(size_t(r0 + vj) * Hkv + g) * D + vd] : 0;
+    }
+    if (kok) {
+      if (kpg < 0 || kpg >= a.num_pages) {
+        flag(a.status, RVA_DEV_BAD_PAGE);
+      } else {
+        const int p = L + kj;
+        *reinterpret_cast<uint2*>(kcw + ((size_t(kpg) * Hkv + g) * P + p % P) * D + kd) = kval;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int iv = base + e * kThreads + tid;
+      if (iv >= n || vpg[e] < 0 || vpg[e] >= a.num_pages) continue;  // a bad page is reported above
+      const int p = L + iv % w;
+      vcw[v_index(vpg[e], g, Hkv, P, D, p % P, iv / w)] = vval[e];
+    }
+  }
+}
+
+// Per-segment record for the merge kernel: the shares holding its tiles and the partial slot
+// of the first one (written every launch by the workgroup that holds the segment's tile 0).
+struct SegMeta {
+  int pa, pb, first_slot, pad;
+};
+__host__ __device__ inline size_t seg_meta_offset(int P, int nbmax, int D) {
+  return size_t(P) * 2 * size_t(nbmax * 16) * (D + 1) * sizeof(float);
+}
+
 template <int D, int NBMAX>
 __global__ __launch_bounds__(kThreads, 1) void attn_sk_kernel(AttnArgs a) {
   __shared__ SkShared<D, NBMAX> sh;
@@ -590,6 +648,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_sk_kernel(AttnArgs a) {
       if (NBMAX == 1 || cols <= 16) run_segment<D, 1, NBMAX>(a, sh, b, g, t0, n, full, slot);
       else if (NBMAX == 2 || cols <= 32) run_segment<D, (NBMAX >= 2 ? 2 : 1), NBMAX>(a, sh, b, g, t0, n, full, slot);
       else run_segment<D, NBMAX, NBMAX>(a, sh, b, g, t0, n, full, slot);
+      if (t0 == 0 && threadIdx.x == 0) {
+        SegMeta m;
+        m.pa = blockIdx.x;
+        m.pb = share_owner(W, P, seg_w1 - 1);
+        m.first_slot = slot;
+        m.pad = 0;
+        reinterpret_cast<SegMeta*>(static_cast<char*>(a.ws) + seg_meta_offset(P, NBMAX, D))[b * a.Hkv + g] = m;
+      }
     }
     x = min(x1, seg_w1);
   }
@@ -597,14 +663,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_sk_kernel(AttnArgs a) {
 
 // Appends each segment's window K/V to the cache, combines the partials of segments cut by
 // share boundaries, and zero-fills output rows [M, tier).  Blocks [0, B*Hkv) handle one
-// segment each, the rest zero-fill.  Every load of
-// a thread is independent of its others (partials are read four at a time), so a merge
-// costs about one memory round trip.
+// segment each (its record from the main kernel says whether it was cut), the rest
+// zero-fill.  Every load of a thread is independent of
+// its others (partials are read four at a time), so a merge costs about one memory round
+// trip after the record.
 template <int D, int NBMAX>
 __global__ __launch_bounds__(kThreads) void attn_merge_kernel(AttnArgs a, int P, int merge_blocks, int pad_blocks) {
   constexpr int ROWS = NBMAX * 16;
-  __shared__ int red[kThreads / kWave][2];
-  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int tid = threadIdx.x;
   if (int(blockIdx.x) >= merge_blocks) {
     const int M = max(a.total_tier[0], 0);
     const int tier = min(a.total_tier[1], a.max_rows);
@@ -616,80 +682,84 @@ __global__ __launch_bounds__(kThreads) void attn_merge_kernel(AttnArgs a, int P,
     return;
   }
   const int b = blockIdx.x / a.Hkv, g = blockIdx.x % a.Hkv;
-  // tile counts: this request's, all requests', and those before b (same rule as the main kernel)
-  int all = 0, before = 0;
-  for (int r = tid; r < a.B; r += kThreads) {
-    const ReqInfo ri = req_info(a, r, false);
-    const int span = seg_span(ri.ok ? (ri.L + ri.w + kTile - 1) / kTile : 0);
-    all += span;
-    before += r < b ? span : 0;
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    all += __shfl_xor(all, o);
-    before += __shfl_xor(before, o);
-  }
-  if (lane == 0) {
-    red[wave][0] = all;
-    red[wave][1] = before;
-  }
-  __syncthreads();
-  all = 0;
-  before = 0;
-#pragma unroll
-  for (int v = 0; v < kThreads / kWave; ++v) {
-    all += red[v][0];
-    before += red[v][1];
-  }
+  const SegMeta meta =
+      reinterpret_cast<const SegMeta*>(static_cast<const char*>(a.ws) + seg_meta_offset(P, NBMAX, D))[blockIdx.x];
   const ReqInfo ri = req_info(a, b, false);
-  if (!ri.ok) return;
-  // append the window's K/V to the cache at positions L .. L+w-1 (the attention kernel,
-  // which has finished, took these keys from k_new / v_new)
-  {
-    const int Hkv = a.Hkv, P = a.page_size;
-    const uint16_t* kn = static_cast<const uint16_t*>(a.k_new);
-    const uint16_t* vn = static_cast<const uint16_t*>(a.v_new);
-    uint16_t* kcw = static_cast<uint16_t*>(a.k_cache);
-    uint16_t* vcw = static_cast<uint16_t*>(a.v_cache);
-    for (int idx = tid; idx < ri.w * D; idx += kThreads) {
-      const int j = idx / D, d = idx % D, p = ri.L + j;
-      bool badp = false;
-      const int pg = page_of(a, b, p, badp);
-      if (pg < 0) {
-        flag(a.status, RVA_DEV_BAD_PAGE);
-        continue;
-      }
-      const size_t src = (size_t(ri.r0 + j) * Hkv + g) * D + d;
-      kcw[((size_t(pg) * Hkv + g) * P + p % P) * D + d] = kn[src];
-      vcw[v_index(pg, g, Hkv, P, D, p % P, d)] = vn[src];
-    }
-  }
-  const int span = seg_span((ri.L + ri.w + kTile - 1) / kTile);
-  const int W = all * a.Hkv;
-  const int seg_w0 = before * a.Hkv + g * span, seg_w1 = seg_w0 + span;
-  const int pa = share_owner(W, P, seg_w0 + kSegCost), pb = share_owner(W, P, seg_w1 - 1);
-  if (pa == pb) return;  // finished inside one share
+  if (!ri.ok) return;  // no tiles: the main kernel wrote no record for it
+  const int pa = meta.pa, pb = meta.pb, first_slot = meta.first_slot;  // then p * 2 for p > pa
+  const bool cut = pa != pb && pb - pa < 4;  // cut segments reach at most 3 shares in practice
   const int G = a.Hq / a.Hkv, nq = ri.w * G;
   const float* ws_o = static_cast<const float*>(a.ws);
   const float* ws_lse = ws_o + size_t(P) * 2 * ROWS * D;
-  const int first_slot = pa * 2 + (share_lo(W, P, pa) < seg_w0 ? 1 : 0);  // then p * 2 for p > pa
+  // Every load is issued before any store, so the whole merge costs about one round trip:
+  // the partials of a cut segment (kItems output items of 4 d per thread, up to 4 shares)...
+  constexpr int kItems = (ROWS * D / 4 + kThreads - 1) / kThreads;
+  float lse[kItems][4];
+  float4 po[kItems][4];
+  if (cut) {
+#pragma unroll
+    for (int i = 0; i < kItems; ++i) {
+      const int it = tid + i * kThreads;
+      const int col = min(it / (D / 4), nq - 1), c4 = it % (D / 4);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int p = min(pa + u, pb);
+        const size_t sl = p == pa ? first_slot : size_t(p) * 2;
+        const bool live = pa + u <= pb && it < nq * (D / 4);
+        lse[i][u] = live ? ws_lse[sl * ROWS + col] : -INFINITY;
+        po[i][u] = live ? reinterpret_cast<const float4*>(ws_o + (sl * ROWS + col) * D)[c4]
+                        : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+  }
+  // ...and the window K/V with its page numbers (appended at positions L .. L+w-1)
+  append_window<D>(a, b, g, ri.L, ri.r0, ri.w);
+  if (pa == pb) return;  // finished inside one share
+  if (cut) {
+#pragma unroll
+    for (int i = 0; i < kItems; ++i) {
+      const int it = tid + i * kThreads;
+      if (it >= nq * (D / 4)) break;
+      const int col = it / (D / 4), c4 = it % (D / 4);
+      float M = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) M = fmaxf(M, lse[i][u]);
+      float sum = 0.f;
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float e = lse[i][u] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(lse[i][u] - M);
+          sum += e;
+          acc.x += e * po[i][u].x; acc.y += e * po[i][u].y; acc.z += e * po[i][u].z; acc.w += e * po[i][u].w;
+        }
+      }
+      const float inv = sum > 0.f ? 1.f / sum : 0.f;
+      uint16_t* out = static_cast<uint16_t*>(a.out) + (size_t(ri.r0 + col / G) * a.Hq + g * G + col % G) * D + c4 * 4;
+      const uint32_t lo16 = f32_to_bf16(acc.x * inv) | (uint32_t(f32_to_bf16(acc.y * inv)) << 16);
+      const uint32_t hi16 = f32_to_bf16(acc.z * inv) | (uint32_t(f32_to_bf16(acc.w * inv)) << 16);
+      *reinterpret_cast<uint2*>(out) = make_uint2(lo16, hi16);
+    }
+    return;
+  }
+  // a segment spread over more than 4 shares: the general loop, 4 shares at a time
   for (int it = tid; it < nq * (D / 4); it += kThreads) {
     const int col = it / (D / 4), c4 = it % (D / 4);
     float M = -INFINITY, sum = 0.f;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int p0 = pa; p0 <= pb; p0 += 4) {
-      float lse[4];
+      float l4[4];
       float4 o[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int p = min(p0 + u, pb);
         const size_t sl = p == pa ? first_slot : size_t(p) * 2;
-        lse[u] = p0 + u <= pb ? ws_lse[sl * ROWS + col] : -INFINITY;
+        l4[u] = p0 + u <= pb ? ws_lse[sl * ROWS + col] : -INFINITY;
         o[u] = reinterpret_cast<const float4*>(ws_o + (sl * ROWS + col) * D)[c4];
       }
       float m4 = M;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) m4 = fmaxf(m4, lse[u]);
+      for (int u = 0; u < 4; ++u) m4 = fmaxf(m4, l4[u]);
       if (m4 != -INFINITY) {
         const float r = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - m4);
         sum *= r;
@@ -697,7 +767,7 @@ __global__ __launch_bounds__(kThreads) void attn_merge_kernel(AttnArgs a, int P,
         M = m4;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const float e = lse[u] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(lse[u] - M);
+          const float e = l4[u] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(l4[u] - M);
           sum += e;
           acc.x += e * o[u].x; acc.y += e * o[u].y; acc.z += e * o[u].z; acc.w += e * o[u].w;
         }
@@ -873,7 +943,7 @@ size_t attention_workspace_bytes(int B, int max_window, int Hq, int Hkv, int D, 
   if (!use_sk(kv_dtype, D, page_size, max_window, G, B)) return 0;
   const int nbmax = nbmax_for(max_window, G);
   const size_t P = sk_grid_for(D, nbmax);
-  return P * 2 * size_t(nbmax * 16) * (D + 1) * sizeof(float);
+  return seg_meta_offset(int(P), nbmax, D) + size_t(B) * Hkv * sizeof(SegMeta);
 }
 
 hipError_t launch_attention(const AttnArgs& a, int kv_dtype, hipStream_t stream) {
