@@ -113,14 +113,66 @@ def cpu_baseline(inp, windows, n_req):
                       f"sample, float64 NumPy, 1 thread, {dt:.1f} s on {platform.processor() or platform.machine()}"}
 
 
+def cost_table(inp, reps, warm):
+    """T(bs, M) of the verify calls measured by graph replay on the first bs requests, the
+    additive fit, and the windows the scheduler picks on the fitted tier-aware tables."""
+    import torch
+
+    from ragged_verify_acceptance_amd.costmodel import (fit_additive, fit_linear,
+                                                        scheduler_tables)
+    from workloads.costgrid import measure
+    from workloads.device import DeviceStep
+
+    wl = inp.wl
+    ds = DeviceStep(inp)
+    ds.prepare()
+    bs_list = sorted({b for b in (1, 2, 4, 8, 16, 32, 48, 64, 128, 256) if b <= inp.B} | {inp.B})
+    samples, sched = measure(ds, bs_list, reps=reps, warm=warm)
+    fit = fit_additive(samples, ds.tiers)
+    _, alpha_lin, theta1, rms_lin = fit_linear(samples)
+    bias, alpha, theta = scheduler_tables(fit, inp.B, wl.gamma, ds.tiers)
+    # the whole step's floor adds the scheduling call at the full batch
+    alpha = (alpha + np.float32(np.interp(np.arange(inp.B + 1), list(sched), list(sched.values()))))
+    windows_pages = ds.windows.cpu().numpy()  # scheduled on the pages' cost line at prepare()
+    ds.bias = float(bias)
+    ds.alpha = torch.from_numpy((alpha * 1e-3).astype(np.float32)).cuda()
+    ds.theta = torch.from_numpy((theta * 1e-3).astype(np.float32)).cuda()
+    ds.restore()
+    ds.schedule()
+    ds.pack()
+    torch.cuda.synchronize()
+    w = ds.windows.cpu().numpy()
+    M, tier = (int(x) for x in ds.total_tier.cpu().numpy())
+    return {
+        "metric": "verify step cost T(bs, M) by graph replay (us) and the scheduler on it",
+        "unit": "us", "n_gpus": 1, "data": "synthetic", "workload": wl.name,
+        "reps_per_point": reps,
+        "grid": [[b, m, round(t, 2)] for b, m, t in samples],
+        "schedule_us": {str(b): round(t, 2) for b, t in sched.items()},
+        "fit_tier_aware": {"bs": fit.bs.tolist(), "alpha_us": np.round(fit.alpha, 2).tolist(),
+                           "tiers": fit.tiers.tolist(), "theta_us": np.round(fit.theta, 2).tolist(),
+                           "rms_us": fit.rms, "max_abs_us": fit.max_abs},
+        "fit_linear": {"alpha_us": np.round(alpha_lin, 2).tolist(), "theta_us_per_token": theta1,
+                       "rms_us": rms_lin},
+        "scheduler_on_measured_tables": {"mean_window": float(w.mean()), "M": M, "tier": tier,
+                                         "K": int(ds.K_out.item())},
+        "scheduler_on_pages_cost_line": {"mean_window": float(windows_pages.mean()),
+                                         "M": int(windows_pages.sum())},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="mixed-b64")
-    ap.add_argument("--mode", default="compact", choices=["compact", "static", "cap-accept"],
-                    help="cap-accept: whole blocks verified, commits capped at the scheduled windows")
+    ap.add_argument("--mode", default="compact",
+                    choices=["compact", "static", "cap-accept", "cost-table"],
+                    help="cap-accept: whole blocks verified, commits capped at the scheduled windows; "
+                         "cost-table: measure T(bs, M) by graph replay and fit the scheduler's tables")
+    ap.add_argument("--graph", action="store_true",
+                    help="time each step as one replay of the captured step graph")
     ap.add_argument("--cpu-sample", type=int, default=24, help="requests in the oracle sample (0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 1 GiB device-to-device copy first (counter calibration)")
@@ -141,6 +193,9 @@ def main():
     torch.cuda.set_device(0)
     wl = get(args.workload)
     inp = Inputs(wl)
+    if args.mode == "cost-table":
+        print(json.dumps(cost_table(inp, reps=max(5, args.steps), warm=max(1, args.warmup))))
+        return
     capped = args.mode == "cap-accept"
     ds = DeviceStep(inp, mode="compact" if capped else args.mode)
     ds.prepare()
@@ -162,10 +217,20 @@ def main():
 
     stream = torch.cuda.current_stream()
 
+    graph = None
+    if args.graph:
+        if capped:
+            sys.exit("bench.py: --graph times the compact and static steps only")
+        from ragged_verify_acceptance_amd.graph import CallGraph
+        ds.restore()
+        graph = CallGraph(ds.step)
+
     def step():
         ds.restore()
         if capped:
             ds.step_capped()
+        elif graph is not None:
+            graph.replay()
         else:
             ds.step()
 
@@ -230,7 +295,7 @@ def main():
         "config": {"workload": wl.name, "mode": args.mode, "B": wl.B, "gamma": wl.gamma,
                    "Hq": wl.Hq, "Hkv": wl.Hkv, "D": wl.D, "page": wl.page, "V": wl.V,
                    "packed_rows_M": M, "tier": tier, "mean_window": float(windows.mean()),
-                   "mean_context": float(inp.context_lens.mean())},
+                   "mean_context": float(inp.context_lens.mean()), "graph": bool(args.graph)},
         "verify_attn_accept": {
             "achieved_GBps": path_gbs, "pct_peak": 100.0 * path_gbs / PEAK_HBM_GBS,
             "tokens_per_s": M / ((t_attn + t_acc) * 1e-3),

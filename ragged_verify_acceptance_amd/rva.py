@@ -137,7 +137,14 @@ def pack_ragged(B, gamma, windows, context_lens, tiers, src, dst, max_rows, cu_s
     t = (ctypes.c_int32 * len(tiers))(*[int(x) for x in tiers])
     row_bytes = 0
     if src is not None:
-        row_bytes = src.element_size() * (src.numel() // (B * gamma))
+        # src is [>= B, gamma, ...] (only the first B blocks are read); a row is one block
+        # position's trailing elements
+        if src.dim() < 2 or src.shape[0] < B or src.shape[1] != gamma or not src.is_contiguous():
+            raise ValueError(f"pack source must be contiguous [>= {B}, {gamma}, ...], "
+                             f"got {tuple(src.shape)}")
+        row_bytes = src.element_size() * (src.numel() // (src.shape[0] * gamma))
+        if dst is None or dst.element_size() * (dst.numel() // max(1, dst.shape[0])) != row_bytes:
+            raise ValueError("pack destination rows must have the source's row size")
     _check("rva_pack_ragged", lib().rva_pack_ragged(
         B, gamma, _ptr(windows), _ptr(context_lens), ctypes.cast(t, ctypes.c_void_p), len(tiers),
         _ptr(src), row_bytes, _ptr(dst), max_rows, _ptr(cu_seqlens), _ptr(row_req),

@@ -141,3 +141,39 @@ def test_accept_capped_validation():
     assert _capped(B=0) == INVALID
     assert _capped(gamma=65) == INVALID
     assert _capped(ws=None) == WS_SMALL
+
+
+def test_pack_binding_row_bytes(monkeypatch):
+    """The binding derives the packed row size from the source's trailing shape, also when
+    only the first B blocks of a larger source are packed."""
+    import types
+
+    import torch
+
+    seen = {}
+
+    class FakeLib:
+        def rva_pack_ragged(self, *args):
+            seen["row_bytes"] = args[7]
+            return 0
+
+        def rva_last_error(self):
+            return b""
+
+    monkeypatch.setattr(rva, "lib", lambda: FakeLib())
+    # host tensors stand in for device ones: nothing is dereferenced
+    monkeypatch.setattr(rva, "_ptr", lambda t: None if t is None else ctypes.c_void_p(t.data_ptr()))
+    st = types.SimpleNamespace(cuda_stream=0)
+    i32 = torch.zeros(64, dtype=torch.int32)
+    src = torch.zeros((64, 8, 4096), dtype=torch.bfloat16)
+    dst = torch.zeros((512, 4096), dtype=torch.bfloat16)
+    for B in (1, 48, 64):
+        rva.pack_ragged(B, 8, i32, i32, [8, 512], src, dst, 512, i32, i32, i32, i32, stream=st)
+        assert seen["row_bytes"] == 8192
+    with pytest.raises(ValueError):
+        rva.pack_ragged(65, 8, i32, i32, [8, 520], src, dst, 512, i32, i32, i32, i32, stream=st)
+    with pytest.raises(ValueError):   # destination rows of another size
+        rva.pack_ragged(4, 8, i32, i32, [8, 32], src, dst[:, :100], 512, i32, i32, i32, i32,
+                        stream=st)
+    with pytest.raises(ValueError):   # block length mismatch
+        rva.pack_ragged(4, 6, i32, i32, [8, 32], src, dst, 512, i32, i32, i32, i32, stream=st)

@@ -192,7 +192,8 @@ class DeviceStep:
 
 def upload_windows(ds: DeviceStep, windows) -> None:
     """Overwrite the device windows (used by tests that feed a stage its inputs directly)."""
-    ds.windows.copy_(torch.as_tensor(np.asarray(windows, np.int32)).to(ds.dev))
+    w = torch.as_tensor(np.asarray(windows, np.int32))
+    ds.windows[: w.numel()].copy_(w.to(ds.dev))
 
 
 def prepare_with_windows(ds: DeviceStep, windows) -> None:
