@@ -24,16 +24,19 @@ Sources (web pages; cited by title and section, never by a line of any copy):
           sections "02 · Speculative Decoding", "07 · Confidence Head",
           "08 · Core Innovation B", "09 · End-to-End Cycle".
 
-Pins: each function is checked in ``tests/test_oracle_pins.py`` against values the
-pages print (``tests/golden/``), closed forms, special cases that reduce to a library
-routine, and brute force on tiny inputs.  Parity unpinned: the semantics of fitted
-Sequential Temperature Scaling temperatures (no page prints a worked example; only the
-identity T = 1 and the limits are pinned).
+Pins: each function is checked in ``tests/test_oracle_pins.py`` and
+``tests/test_oracle_calibration.py`` against values the pages print (``tests/golden/``),
+closed forms, special cases that reduce to a library routine, and brute force on tiny
+inputs.  Parity unpinned: that the Sequential Temperature Scaling fit in
+``calibration.py`` is the one the pages' authors ran (no page prints fitted temperatures;
+the estimator itself is pinned by its single-position special case, by recovery of known
+temperatures and by optimality).
 """
 
 from .scheduling import confidence_from_head, survival, schedule_windows
 from .packing import pack_ragged
 from .attention import verify_attention
+from .calibration import sts_fit, ece, log_prefix_survival
 from .acceptance import (softmax64, inverse_cdf, accept_request, accept_request_capped,
                          accept_and_commit, confidence_labels)
 
@@ -49,4 +52,7 @@ __all__ = [
     "accept_request_capped",
     "accept_and_commit",
     "confidence_labels",
+    "sts_fit",
+    "ece",
+    "log_prefix_survival",
 ]

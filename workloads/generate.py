@@ -23,6 +23,12 @@ any request can be regenerated alone and arrays are independent of each other):
 * packed-buffer source rows (stage 2): N(0, 1) bf16, [gamma, pack_hidden] per request.
 * page table: request b owns ceil((L_b + gamma) / page) pages; the physical page numbers
   are a seeded permutation of all pages (a fragmented pool).
+* calibration traces (``calibration_trace``): per sample and draft position a true
+  conditional acceptance probability q ~ Beta(a, b) (float64); the head logit is
+  z = T_k * log(q / (1 - q)) + noise * N(0, 1), rounded to float32 (T_k > 1: an
+  over-confident head); draft k is accepted iff U[0, 1) < q, and the accept length is the
+  number of leading accepted drafts; the observed length is gamma - 1 (full-block runs) or,
+  censored, U{0 .. gamma-1} (compact runs, which verify only the window).
 """
 
 from __future__ import annotations
@@ -199,3 +205,19 @@ def paged_cache(inp: Inputs, fill_unused=float("nan"), requests=None):
                 s1 = min(hi, s0 + VB)
                 v_pool[pg, :, (s0 - lo) // VB, :, : s1 - s0] = V[s0:s1].permute(1, 2, 0)
     return k_pool, v_pool
+
+
+def calibration_trace(seed: int, N: int, G1: int, T_true, beta=(6.0, 1.5), noise: float = 0.0,
+                      censor: bool = False):
+    """Synthetic acceptance trace with a known head temperature (recipe in the module
+    docstring).  Returns (z float32 [N, G1], accept_len int32 [N], observed_len int32 [N])."""
+    ss = np.random.SeedSequence([seed, 0xCA1])
+    r_q, r_z, r_u, r_o = (np.random.Generator(np.random.PCG64(s)) for s in ss.spawn(4))
+    T = np.broadcast_to(np.asarray(T_true, dtype=np.float64), (G1,))
+    q = r_q.beta(beta[0], beta[1], size=(N, G1))
+    q = np.clip(q, 1e-12, 1 - 1e-12)
+    z = (T[None, :] * np.log(q / (1.0 - q)) + noise * r_z.standard_normal((N, G1))).astype(np.float32)
+    acc = r_u.random((N, G1)) < q
+    n = np.where(acc.all(axis=1), G1, np.argmin(acc, axis=1)).astype(np.int32)
+    obs = r_o.integers(0, G1 + 1, size=N).astype(np.int32) if censor else np.full(N, G1, np.int32)
+    return z, n, obs
