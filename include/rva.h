@@ -13,11 +13,14 @@
  *   rva_confidence_labels  stage 5  TV-distance confidence labels on their own
  *   rva_accept_capped      stage 4 in cap-accept mode (whole block verified, commit capped
  *                          at the window, uncapped acceptance reported)
+ *   rva_sts_fit            calibration: per-position temperatures of the confidence head
+ *                          fitted to acceptance traces (input of stage 1)
+ *   rva_calibration_ece    calibration: expected calibration error of the survival
  *
  * Sources, cited by page title and section:
  *   [SGL]   "DFlash 到 DSpark in SGLang：解码提速 4.3×，以及 DeepSeek-V4 支持"
  *           (yichizhang.dev, AI-Infra-Visualized).
- *   [CSDN]  devpress.csdn.net (awstech) article on DSpark in SGLang, sections 2-4.
+ *   [CSDN]  devpress.csdn.net (awstech) article on DSpark in SGLang, sections 2-5.
  *   [NOTES] "DSpark：投机解码与生产级 Serving 学习笔记" (sorenprojections.com).
  *
  * Conventions shared by every call
@@ -297,6 +300,65 @@ rva_status rva_confidence_labels(int B, int gamma, int V, int logit_dtype, int m
                                  const int32_t* cu_seqlens, float* labels,
                                  int32_t* device_status, void* workspace,
                                  size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Calibration -- rva_sts_fit (Sequential Temperature Scaling)
+ *
+ * [NOTES] section 07 ("为什么还要做 Sequential Temperature Scaling？"): the head's scores
+ * are over-confident, so a temperature per draft position is fitted that makes the
+ * predicted prefix survival match the measured one; [SGL] "DSpark：sequential head 加验证
+ * 预算": STS calibrates the block's survival to the real acceptance rate.  The fitted
+ * temperatures are the `sts_T` argument of rva_schedule_windows.
+ *
+ * A trace holds N samples (one request at one step).  Sample i: head logits z[i, k] for
+ * the G1 = gamma-1 draft positions (the logit before the sigmoid), the accepted drafts
+ * accept_len[i] of a full-block verification, and the positions actually verified,
+ * observed_len[i] (NULL: all G1; a compact run observes only w_i - 1).  Position k
+ * (0-based) is observed iff k < observed_len[i]; its outcome is [accept_len[i] > k].
+ * Predicted survival: a[i, k] = exp(sum_{j <= k} log sigmoid(z[i, j] / T_j)), float64.
+ * Fit, in position order with the earlier temperatures fixed: T_k in [T_lo, T_hi]
+ * minimises the Bernoulli negative log-likelihood of position k's observed outcomes
+ * (global minimum located by iterated 64-point grid refinement in ln T, six rounds; final
+ * spacing ~1e-8 relative).  A position with no observed sample gets T_k = 1.
+ *
+ *   N               samples, 1 .. 2^26; G1 = gamma - 1 in [1, 63].
+ *   z               [N, G1] float32; accept_len [N] int32; observed_len [N] int32 or NULL.
+ *   T_lo, T_hi      bracket, 0 < T_lo < T_hi (float32; the search runs in float64).
+ *   T_out           [G1] float32 output; nll_out [G1] float64 output or NULL (the
+ *                   minimised negative log-likelihood of each position).
+ *   workspace       rva_sts_fit_workspace_size(N) bytes, 256-byte aligned; its contents on
+ *                   entry do not matter.
+ * Launches 1 + G1 * 13 small kernels (data-parallel passes and single-wave selections);
+ * nothing is read back to the host.
+ */
+rva_status rva_sts_fit(int N, int G1, const float* z, const int32_t* accept_len,
+                       const int32_t* observed_len, float T_lo, float T_hi, float* T_out,
+                       double* nll_out, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+size_t rva_sts_fit_workspace_size(int N);
+
+/*
+ * Calibration -- rva_calibration_ece (expected calibration error)
+ *
+ * [CSDN] section 5: per-request confidence and calibration metrics such as ECE for
+ * analysis after the fact.  The predicted survival a[i, k] (as in rva_sts_fit, with
+ * temperatures T, or T_k = 1 when T is NULL) of every observed (i, k) is put in one of
+ * n_bins equal bins of [0, 1]: bin = min(floor(a * n_bins), n_bins - 1).  Per bin: count,
+ * mean a, mean outcome; ECE = sum over bins of count/total * |mean a - mean outcome|.
+ *
+ *   N, G1, z, accept_len, observed_len   as rva_sts_fit.
+ *   T               [G1] float32 or NULL.
+ *   n_bins          1 .. 64, with G1 * n_bins <= 3840.
+ *   ece_out         [G1 + 1] float64 output: [0] pooled over every observed position,
+ *                   [1 + k] position k alone (0 when it has no observed sample).
+ *   bin_counts      [G1, n_bins] int32 output or NULL.
+ *   workspace       rva_calibration_ece_workspace_size(N, G1, n_bins) bytes, 256-aligned.
+ */
+rva_status rva_calibration_ece(int N, int G1, const float* z, const int32_t* accept_len,
+                               const int32_t* observed_len, const float* T, int n_bins,
+                               double* ece_out, int32_t* bin_counts, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream);
+size_t rva_calibration_ece_workspace_size(int N, int G1, int n_bins);
 
 /* Message for the last error returned on the calling thread ("" if none). */
 const char* rva_last_error(void);

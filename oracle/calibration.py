@@ -97,6 +97,8 @@ def sts_fit(z, accept_len, observed_len=None, T_lo=0.05, T_hi=20.0, grid=4097):
     z = np.asarray(z, dtype=np.float32)
     N, G1 = z.shape
     obs, E = observed_outcomes(accept_len, observed_len, G1)
+    # the bracket ends are float32 values (as a caller passes them to the library)
+    T_lo, T_hi = float(np.float32(T_lo)), float(np.float32(T_hi))
     u = np.linspace(np.log(T_lo), np.log(T_hi), grid)
     T_fit = np.ones(G1)
     nll = np.zeros(G1)

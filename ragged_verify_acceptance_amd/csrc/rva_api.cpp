@@ -1,6 +1,7 @@
 // extern "C" entry points of librva: host-side argument validation, workspace sizing, the
 // thread-local error text, and dispatch to the HIP launchers.  Nothing here touches device
 // memory or synchronises; a call that fails validation enqueues nothing.
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
@@ -299,6 +300,73 @@ rva_status rva_confidence_labels(int B, int gamma, int V, int logit_dtype, int m
   a.status = device_status;
   a.ws = workspace;
   return hip_result(rva::launch_accept(a, logit_dtype, false, stream), "rva_confidence_labels launch");
+}
+
+size_t rva_sts_fit_workspace_size(int N) {
+  if (N < 1 || N > (1 << 26)) return 0;
+  return rva::sts_workspace_bytes(N);
+}
+
+rva_status rva_sts_fit(int N, int G1, const float* z, const int32_t* accept_len,
+                       const int32_t* observed_len, float T_lo, float T_hi, float* T_out,
+                       double* nll_out, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+  REQUIRE(N >= 1 && N <= (1 << 26), "N must be in [1, 2^26] (got %d)", N);
+  REQUIRE(G1 >= 1 && G1 <= 63, "G1 must be in [1, 63] (got %d)", G1);
+  REQUIRE(z && accept_len && T_out, "z, accept_len and T_out are required");
+  REQUIRE(T_lo > 0.f && T_hi > T_lo && std::isfinite(T_hi), "need 0 < T_lo < T_hi (got %g, %g)",
+          double(T_lo), double(T_hi));
+  const size_t need = rva::sts_workspace_bytes(N);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(RVA_ERR_WORKSPACE_TOO_SMALL, "rva_sts_fit: workspace needs %zu bytes (got %zu)", need,
+                workspace_bytes);
+  REQUIRE(aligned(workspace, 256), "workspace must be 256-byte aligned");
+  rva::StsArgs a{};
+  a.N = N;
+  a.G1 = G1;
+  a.z = z;
+  a.accept_len = accept_len;
+  a.observed_len = observed_len;
+  a.T_lo = T_lo;
+  a.T_hi = T_hi;
+  a.T_out = T_out;
+  a.nll_out = nll_out;
+  a.ws = workspace;
+  return hip_result(rva::launch_sts_fit(a, stream), "rva_sts_fit launch");
+}
+
+size_t rva_calibration_ece_workspace_size(int N, int G1, int n_bins) {
+  if (N < 1 || N > (1 << 26) || G1 < 1 || G1 > 63 || n_bins < 1 || n_bins > 64 || G1 * n_bins > 3840)
+    return 0;
+  return rva::ece_workspace_bytes(N, G1, n_bins);
+}
+
+rva_status rva_calibration_ece(int N, int G1, const float* z, const int32_t* accept_len,
+                               const int32_t* observed_len, const float* T, int n_bins,
+                               double* ece_out, int32_t* bin_counts, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+  REQUIRE(N >= 1 && N <= (1 << 26), "N must be in [1, 2^26] (got %d)", N);
+  REQUIRE(G1 >= 1 && G1 <= 63, "G1 must be in [1, 63] (got %d)", G1);
+  REQUIRE(n_bins >= 1 && n_bins <= 64 && G1 * n_bins <= 3840,
+          "n_bins must be in [1, 64] with G1*n_bins <= 3840 (got %d)", n_bins);
+  REQUIRE(z && accept_len && ece_out, "z, accept_len and ece_out are required");
+  const size_t need = rva::ece_workspace_bytes(N, G1, n_bins);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(RVA_ERR_WORKSPACE_TOO_SMALL, "rva_calibration_ece: workspace needs %zu bytes (got %zu)",
+                need, workspace_bytes);
+  REQUIRE(aligned(workspace, 256), "workspace must be 256-byte aligned");
+  rva::EceArgs a{};
+  a.N = N;
+  a.G1 = G1;
+  a.n_bins = n_bins;
+  a.z = z;
+  a.accept_len = accept_len;
+  a.observed_len = observed_len;
+  a.T = T;
+  a.ece_out = ece_out;
+  a.bin_counts = bin_counts;
+  a.ws = workspace;
+  return hip_result(rva::launch_ece(a, stream), "rva_calibration_ece launch");
 }
 
 }  // extern "C"

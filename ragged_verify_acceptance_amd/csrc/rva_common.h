@@ -118,4 +118,30 @@ struct AcceptArgs {
 size_t accept_workspace_bytes(int B, int gamma, int V, int max_rows);
 hipError_t launch_accept(const AcceptArgs& a, int logit_dtype, bool commit, hipStream_t stream);
 
+struct StsArgs {
+  int N, G1;
+  const float* z;
+  const int32_t* accept_len;
+  const int32_t* observed_len;
+  float T_lo, T_hi;
+  float* T_out;
+  double* nll_out;
+  void* ws;
+};
+size_t sts_workspace_bytes(int N);
+hipError_t launch_sts_fit(const StsArgs& a, hipStream_t stream);
+
+struct EceArgs {
+  int N, G1, n_bins;
+  const float* z;
+  const int32_t* accept_len;
+  const int32_t* observed_len;
+  const float* T;
+  double* ece_out;
+  int32_t* bin_counts;
+  void* ws;
+};
+size_t ece_workspace_bytes(int N, int G1, int n_bins);
+hipError_t launch_ece(const EceArgs& a, hipStream_t stream);
+
 }  // namespace rva

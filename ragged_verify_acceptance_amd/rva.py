@@ -34,8 +34,9 @@ _STATUS = {0: "RVA_OK", 1: "RVA_ERR_INVALID_ARGUMENT", 2: "RVA_ERR_UNSUPPORTED",
 EXPORTED = [
     "rva_schedule_windows", "rva_pack_ragged", "rva_verify_attention",
     "rva_verify_attention_workspace_size", "rva_accept_and_commit",
-    "rva_accept_workspace_size", "rva_confidence_labels", "rva_accept_capped", "rva_last_error",
-    "rva_version",
+    "rva_accept_workspace_size", "rva_confidence_labels", "rva_accept_capped", "rva_sts_fit",
+    "rva_sts_fit_workspace_size", "rva_calibration_ece", "rva_calibration_ece_workspace_size",
+    "rva_last_error", "rva_version",
 ]
 
 
@@ -62,10 +63,15 @@ _SIGS = {
     "rva_confidence_labels": [_i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _z, _p],
     "rva_accept_capped": [_i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p,
                           _p, _p, _p, _z, _p],
+    "rva_sts_fit": [_i, _i, _p, _p, _p, _f, _f, _p, _p, _p, _z, _p],
+    "rva_sts_fit_workspace_size": [_i],
+    "rva_calibration_ece": [_i, _i, _p, _p, _p, _p, _i, _p, _p, _p, _z, _p],
+    "rva_calibration_ece_workspace_size": [_i, _i, _i],
     "rva_last_error": [],
     "rva_version": [],
 }
 _RESTYPES = {"rva_verify_attention_workspace_size": _z, "rva_accept_workspace_size": _z,
+             "rva_sts_fit_workspace_size": _z, "rva_calibration_ece_workspace_size": _z,
              "rva_last_error": ctypes.c_char_p}
 
 
@@ -202,3 +208,27 @@ def accept_capped(B, gamma, V, max_rows, target_logits, draft_logits, draft_toke
         _ptr(committed), _ptr(context_lens), _ptr(p_t_at_draft), _ptr(p_d_at_draft),
         _ptr(labels), _ptr(device_status), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def sts_fit_workspace_size(N):
+    return lib().rva_sts_fit_workspace_size(N)
+
+
+def sts_fit(N, G1, z, accept_len, observed_len, T_lo, T_hi, T_out, nll_out, workspace,
+            stream=None):
+    _check("rva_sts_fit", lib().rva_sts_fit(
+        N, G1, _ptr(z), _ptr(accept_len), _ptr(observed_len), float(T_lo), float(T_hi),
+        _ptr(T_out), _ptr(nll_out), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def calibration_ece_workspace_size(N, G1, n_bins):
+    return lib().rva_calibration_ece_workspace_size(N, G1, n_bins)
+
+
+def calibration_ece(N, G1, z, accept_len, observed_len, T, n_bins, ece_out, bin_counts,
+                    workspace, stream=None):
+    _check("rva_calibration_ece", lib().rva_calibration_ece(
+        N, G1, _ptr(z), _ptr(accept_len), _ptr(observed_len), _ptr(T), n_bins, _ptr(ece_out),
+        _ptr(bin_counts), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)))

@@ -29,7 +29,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     L = rva.lib()
     names = declared_functions()
-    assert "rva_verify_attention" in names and len(names) == 10
+    assert "rva_verify_attention" in names and len(names) == 14
     for n in names:
         assert hasattr(L, n), f"{n} declared in rva.h but not exported"
     assert set(names) == set(rva.EXPORTED)
@@ -177,3 +177,35 @@ def test_pack_binding_row_bytes(monkeypatch):
                         stream=st)
     with pytest.raises(ValueError):   # block length mismatch
         rva.pack_ragged(4, 6, i32, i32, [8, 32], src, dst, 512, i32, i32, i32, i32, stream=st)
+
+
+def test_calibration_validation():
+    L = rva.lib()
+    ws = rva.sts_fit_workspace_size(1000)
+    assert ws > 1000 * 8 and rva.sts_fit_workspace_size(0) == 0
+
+    def fit(N=1000, G1=7, z=FAKE, n=FAKE, T_out=FAKE, lo=0.05, hi=20.0, w=FAKE, wb=ws):
+        return L.rva_sts_fit(N, G1, z, n, None, lo, hi, T_out, None, w, wb, None)
+
+    assert fit(N=0) == INVALID
+    assert fit(G1=64) == INVALID
+    assert fit(z=None) == INVALID
+    assert fit(T_out=None) == INVALID
+    assert fit(lo=0.0) == INVALID
+    assert fit(lo=2.0, hi=1.0) == INVALID
+    assert fit(w=None) == WS_SMALL
+    assert fit(wb=ws - 1) == WS_SMALL
+    assert fit(w=ctypes.c_void_p(0x100010)) == INVALID   # not 256-byte aligned
+
+    we = rva.calibration_ece_workspace_size(1000, 7, 15)
+    assert we > 0 and rva.calibration_ece_workspace_size(1000, 63, 64) == 0  # 63*64 > 3840
+
+    def ece(N=1000, G1=7, nb=15, out=FAKE, w=FAKE, wb=we):
+        return L.rva_calibration_ece(N, G1, FAKE, FAKE, None, None, nb, out, None, w, wb, None)
+
+    assert ece(nb=0) == INVALID
+    assert ece(nb=65) == INVALID
+    assert ece(G1=63, nb=61) == INVALID
+    assert ece(out=None) == INVALID
+    assert ece(w=None) == WS_SMALL
+    assert ece(wb=we - 1) == WS_SMALL
