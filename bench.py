@@ -161,6 +161,104 @@ def cost_table(inp, reps, warm):
     }
 
 
+def sts_bench(wl, steps, reps, cpu):
+    """Acceptance trace from the acceptance call itself (full blocks, so every position is
+    observed), an over-confident head on it, then the STS fit and ECE calls, timed."""
+    import torch
+
+    from ragged_verify_acceptance_amd import rva
+
+    B, gamma, G1, V = wl.B, wl.gamma, wl.G1, 4096
+    dev = "cuda"
+    g = torch.Generator(device=dev)
+    g.manual_seed(wl.seed)
+    sig = torch.tensor([wl.classes[b % len(wl.classes)].sigma for b in range(B)], device=dev)
+    cu = torch.arange(0, B * gamma + 1, gamma, dtype=torch.int32, device=dev)
+    acc_ws = torch.empty(rva.accept_workspace_size(B, gamma, V, B * gamma), dtype=torch.uint8, device=dev)
+    accept_len = torch.empty(B, dtype=torch.int32, device=dev)
+    committed = torch.empty((B, gamma), dtype=torch.int32, device=dev)
+    ctx = torch.zeros(B, dtype=torch.int32, device=dev)
+    labels = torch.empty((steps, B, G1), dtype=torch.float32, device=dev)
+    n_all = torch.empty((steps, B), dtype=torch.int32, device=dev)
+    for s in range(steps):
+        # the drafter's side (outside the path): logits and tokens sampled from the draft
+        target = 2.0 * torch.randn((B * gamma, V), generator=g, device=dev)
+        draft = (target.view(B, gamma, V)[:, :G1]
+                 + sig[:, None, None] * torch.randn((B, G1, V), generator=g, device=dev)).contiguous()
+        gum = -torch.log(-torch.log(torch.rand((B, G1, V), generator=g, device=dev).clamp_min(1e-30)))
+        tokens = torch.argmax(draft + gum, dim=-1).to(torch.int32).contiguous()
+        u_acc = torch.rand((B, G1), generator=g, device=dev)
+        u_res = torch.rand(B, generator=g, device=dev)
+        rva.accept_and_commit(B, gamma, V, B * gamma, target, draft, tokens, u_acc, u_res, cu,
+                              accept_len, committed, ctx, None, None, labels[s], acc_ws)
+        n_all[s].copy_(accept_len)
+    # an over-confident head that tracks the label: z = T* logit(c*) + noise
+    T_star = torch.tensor([1.5 + 0.1 * k for k in range(G1)], device=dev)
+    q = labels.clamp(1e-6, 1 - 1e-6)
+    z = (T_star * torch.log(q / (1 - q))
+         + 0.3 * torch.randn(q.shape, generator=g, device=dev)).reshape(-1, G1).contiguous()
+    n = n_all.reshape(-1).contiguous()
+    N = z.shape[0]
+    T = torch.empty(G1, dtype=torch.float32, device=dev)
+    nll = torch.empty(G1, dtype=torch.float64, device=dev)
+    ws = torch.empty(rva.sts_fit_workspace_size(N), dtype=torch.uint8, device=dev)
+    ece_before = torch.empty(G1 + 1, dtype=torch.float64, device=dev)
+    ece_after = torch.empty(G1 + 1, dtype=torch.float64, device=dev)
+    ews = torch.empty(rva.calibration_ece_workspace_size(N, G1, 15), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    rva.sts_fit(N, G1, z, n, None, 0.05, 20.0, T, nll, ws)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    t_fit, t_ece = [], []
+    for _ in range(reps):
+        ev[0].record(stream)
+        rva.sts_fit(N, G1, z, n, None, 0.05, 20.0, T, nll, ws)
+        ev[1].record(stream)
+        rva.calibration_ece(N, G1, z, n, None, T, 15, ece_after, None, ews)
+        ev[2].record(stream)
+        torch.cuda.synchronize()
+        t_fit.append(ev[0].elapsed_time(ev[1]))
+        t_ece.append(ev[1].elapsed_time(ev[2]))
+    rva.calibration_ece(N, G1, z, n, None, None, 15, ece_before, None, ews)
+    torch.cuda.synchronize()
+    ms_fit, ms_ece = float(np.median(t_fit)), float(np.median(t_ece))
+    nn = n.cpu().numpy()
+    res = {
+        "metric": "STS fit + ECE on an acceptance trace from the acceptance call",
+        "value": N / ((ms_fit + ms_ece) * 1e-3), "unit": "trace samples/s", "n_gpus": 1,
+        "dtype": "f64", "data": "synthetic",
+        "config": {"workload": f"{wl.name} classes, V={V} f32 logits, full blocks",
+                   "B": B, "gamma": gamma, "trace_steps": steps, "N": N, "n_bins": 15,
+                   "T_bracket": [0.05, 20.0]},
+        "sts_fit_ms": ms_fit, "ece_ms": ms_ece,
+        "head_T_true": [round(float(x), 3) for x in T_star.cpu()],
+        "T_fit": [round(float(x), 4) for x in T.cpu()],
+        "ece_before": {"pooled": float(ece_before[0]), "per_position": ece_before[1:].cpu().tolist()},
+        "ece_after": {"pooled": float(ece_after[0]), "per_position": ece_after[1:].cpu().tolist()},
+        "mean_accept_len": float(nn.mean()),
+        "mean_tv_label": float(labels.mean()),
+    }
+    if cpu:
+        import time
+
+        from threadpoolctl import threadpool_limits
+
+        import oracle
+
+        zc, nc = z.cpu().numpy(), nn
+        with threadpool_limits(1):
+            t0 = time.perf_counter()
+            r = oracle.sts_fit(zc, nc, grid=513)
+            oracle.ece(zc, nc, T=r["T"], n_bins=15)
+            dt = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": N / dt, "unit": "trace samples/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"the whole trace ({N} samples x {G1} positions): "
+                                         f"sts_fit (513-point scan + bounded refinement) and ECE, "
+                                         f"float64 NumPy, 1 thread, {dt:.1f} s"}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -168,9 +266,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="mixed-b64")
     ap.add_argument("--mode", default="compact",
-                    choices=["compact", "static", "cap-accept", "cost-table"],
+                    choices=["compact", "static", "cap-accept", "cost-table", "sts"],
                     help="cap-accept: whole blocks verified, commits capped at the scheduled windows; "
                          "cost-table: measure T(bs, M) by graph replay and fit the scheduler's tables")
+    ap.add_argument("--trace-steps", type=int, default=200,
+                    help="sts mode: verify steps (of B requests) in the acceptance trace")
     ap.add_argument("--graph", action="store_true",
                     help="time each step as one replay of the captured step graph")
     ap.add_argument("--cpu-sample", type=int, default=24, help="requests in the oracle sample (0: skip)")
@@ -192,6 +292,10 @@ def main():
 
     torch.cuda.set_device(0)
     wl = get(args.workload)
+    if args.mode == "sts":
+        print(json.dumps(sts_bench(wl, args.trace_steps, reps=max(3, args.steps),
+                                   cpu=args.cpu_sample > 0)))
+        return
     inp = Inputs(wl)
     if args.mode == "cost-table":
         print(json.dumps(cost_table(inp, reps=max(5, args.steps), warm=max(1, args.warmup))))

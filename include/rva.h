@@ -328,8 +328,8 @@ rva_status rva_confidence_labels(int B, int gamma, int V, int logit_dtype, int m
  *                   minimised negative log-likelihood of each position).
  *   workspace       rva_sts_fit_workspace_size(N) bytes, 256-byte aligned; its contents on
  *                   entry do not matter.
- * Launches 1 + G1 * 13 small kernels (data-parallel passes and single-wave selections);
- * nothing is read back to the host.
+ * Launches 1 + 6 * G1 kernels (one per refinement round; the last workgroup of a round
+ * makes its selection); nothing is read back to the host.
  */
 rva_status rva_sts_fit(int N, int G1, const float* z, const int32_t* accept_len,
                        const int32_t* observed_len, float T_lo, float T_hi, float* T_out,

@@ -16,10 +16,10 @@
 // negative log-likelihood of the observed outcomes of position k over [T_lo, T_hi].  The
 // minimum is located by iterated grid refinement in u = ln T: 64 log-spaced temperatures,
 // the best one's two neighbouring cells become the next round's bracket, six rounds (final
-// spacing about 1e-8 in u).  Every round is one data-parallel pass (each workgroup writes
-// per-temperature partial sums of its samples) and one single-wave selection that sums the
-// partials in a fixed order, so the result is reproducible run to run and the bracket stays
-// on the device (no host round trip between rounds).
+// spacing about 1e-8 in u).  Every round is one launch: a data-parallel pass over (sample
+// chunk, group of 8 temperatures) whose workgroups write partial sums, and a selection by
+// the last workgroup to finish that sums the partials in chunk order, so the result is
+// reproducible run to run and the bracket stays on the device (no host round trip).
 //
 // ECE: the observed (a, E) pairs are binned by a into n_bins equal bins of [0, 1]
 // (bin = min(floor(a n_bins), n_bins - 1)); per workgroup the bins live in LDS, partial bins
@@ -35,12 +35,13 @@ namespace {
 constexpr int kCalThreads = 256;
 constexpr int kGrid = 64;     // temperatures per refinement round
 constexpr int kRounds = 6;
-constexpr int kGroup = 8;     // temperatures evaluated per pass over a thread's samples
+constexpr int kGroup = 8;     // temperatures per workgroup (grid.y = kGrid / kGroup)
 constexpr int kMaxChunks = 512;
 constexpr int kMaxEceChunks = 256;
 
 struct StsState {
-  double u_lo, du, T, pad;
+  double u_lo, du, T, pad;  // bracket of the current round; the last fitted temperature
+  unsigned int done;        // workgroups of the current round that have finished
 };
 
 __device__ __forceinline__ double log_sigmoid(double x) { return fmin(x, 0.0) - log1p(exp(-fabs(x))); }
@@ -61,8 +62,10 @@ __device__ __forceinline__ double block_sum_f64(double v, double* red) {
   return s;
 }
 
+// Workspace: two running log-survival buffers (position k's prefix lives in L[k & 1]), the
+// per-workgroup partial sums of one round, and the round state.
 struct StsLayout {
-  size_t off_L, off_part, off_state, total;
+  size_t off_L0, off_L1, off_part, off_state, total;
   int chunks;
 };
 
@@ -70,15 +73,16 @@ StsLayout sts_layout(int N) {
   StsLayout l;
   l.chunks = std::min(kMaxChunks, (N + kCalThreads - 1) / kCalThreads);
   auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
-  l.off_L = 0;
-  l.off_part = up(size_t(N) * sizeof(double));
+  l.off_L0 = 0;
+  l.off_L1 = up(size_t(N) * sizeof(double));
+  l.off_part = l.off_L1 + up(size_t(N) * sizeof(double));
   l.off_state = l.off_part + up(size_t(kMaxChunks) * (kGrid + 1) * sizeof(double));
   l.total = l.off_state + 256;
   return l;
 }
 
 __global__ __launch_bounds__(kCalThreads) void sts_init_kernel(StsArgs a, StsLayout l) {
-  double* L = reinterpret_cast<double*>(static_cast<char*>(a.ws) + l.off_L);
+  double* L = reinterpret_cast<double*>(static_cast<char*>(a.ws) + l.off_L0);
   for (int i = blockIdx.x * kCalThreads + threadIdx.x; i < a.N; i += gridDim.x * kCalThreads) L[i] = 0.0;
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     StsState* st = reinterpret_cast<StsState*>(static_cast<char*>(a.ws) + l.off_state);
@@ -86,61 +90,79 @@ __global__ __launch_bounds__(kCalThreads) void sts_init_kernel(StsArgs a, StsLay
     st->u_lo = lo;
     st->du = (hi - lo) / (kGrid - 1);
     st->T = 1.0;
+    st->done = 0u;
   }
 }
 
-// Partial negative log-likelihoods of position k at the round's 64 temperatures (and the
-// number of observed samples) over this workgroup's samples.
-__global__ __launch_bounds__(kCalThreads) void sts_eval_kernel(StsArgs a, StsLayout l, int k) {
-  __shared__ double s_T[kGrid];
+// One refinement round of position k.  Workgroup (x, y) sums the negative log-likelihood of
+// its chunk x of samples at the round's temperatures 8y .. 8y+7 (and, for y = 0, counts the
+// observed samples).  In round 0 of a position k > 0 each thread first extends its samples'
+// log survival by position k-1 at the temperature just fitted (workgroups y = 0 store it for
+// the later rounds, in the other buffer, so no workgroup reads a value another one is
+// rewriting).  The last workgroup to finish (a device-scope counter) sums the partials in
+// chunk order with one wave, picks the best temperature (first on a tie), and narrows the
+// bracket or, after the last round, publishes T_k.
+__global__ __launch_bounds__(kCalThreads) void sts_round_kernel(StsArgs a, StsLayout l, int k, int round,
+                                                                int last) {
+  __shared__ double s_T[kGroup];
   __shared__ double red[kCalThreads / kWave];
-  const char* ws = static_cast<const char*>(a.ws);
-  const double* L = reinterpret_cast<const double*>(ws + l.off_L);
-  const StsState st = *reinterpret_cast<const StsState*>(ws + l.off_state);
-  double* part = reinterpret_cast<double*>(static_cast<char*>(a.ws) + l.off_part) + size_t(blockIdx.x) * (kGrid + 1);
-  const int tid = threadIdx.x;
-  if (tid < kGrid) s_T[tid] = exp(st.u_lo + tid * st.du);
+  __shared__ int s_last;
+  char* ws = static_cast<char*>(a.ws);
+  StsState* stp = reinterpret_cast<StsState*>(ws + l.off_state);
+  const StsState st = *stp;
+  double* Lcur = reinterpret_cast<double*>(ws + ((k & 1) ? l.off_L1 : l.off_L0));
+  const double* Lprev = reinterpret_cast<const double*>(ws + ((k & 1) ? l.off_L0 : l.off_L1));
+  double* part = reinterpret_cast<double*>(ws + l.off_part);
+  const int tid = threadIdx.x, g0 = blockIdx.y * kGroup;
+  if (tid < kGroup) s_T[tid] = exp(st.u_lo + (g0 + tid) * st.du);
   __syncthreads();
-  const int stride = gridDim.x * kCalThreads;
+  const bool extend = round == 0 && k > 0;
+  double acc[kGroup];
+#pragma unroll
+  for (int p = 0; p < kGroup; ++p) acc[p] = 0.0;
   double cnt = 0.0;
-  for (int g0 = 0; g0 < kGrid; g0 += kGroup) {
-    double acc[kGroup];
-#pragma unroll
-    for (int p = 0; p < kGroup; ++p) acc[p] = 0.0;
-    for (int i = blockIdx.x * kCalThreads + tid; i < a.N; i += stride) {
-      const int o = a.observed_len ? a.observed_len[i] : a.G1;
-      if (k >= o) continue;
-      const double z = a.z[size_t(i) * a.G1 + k];
-      const double Lp = L[i];
-      const bool E = a.accept_len[i] > k;
-      if (g0 == 0) cnt += 1.0;
-#pragma unroll
-      for (int p = 0; p < kGroup; ++p) {
-        const double la = Lp + log_sigmoid(z / s_T[g0 + p]);
-        acc[p] += E ? -la : -log1mexp(la);
-      }
+  for (int i = blockIdx.x * kCalThreads + tid; i < a.N; i += gridDim.x * kCalThreads) {
+    const int o = a.observed_len ? a.observed_len[i] : a.G1;
+    if (k >= o) continue;  // unobserved here, and so at every later position
+    double Lp;
+    if (extend) {
+      Lp = Lprev[i] + log_sigmoid(double(a.z[size_t(i) * a.G1 + k - 1]) / st.T);
+      if (blockIdx.y == 0) Lcur[i] = Lp;
+    } else {
+      Lp = k == 0 ? 0.0 : Lcur[i];
     }
+    const double z = a.z[size_t(i) * a.G1 + k];
+    const bool E = a.accept_len[i] > k;
+    cnt += 1.0;
 #pragma unroll
     for (int p = 0; p < kGroup; ++p) {
-      const double s = block_sum_f64(acc[p], red);
-      if (tid == 0) part[g0 + p] = s;
+      const double la = Lp + log_sigmoid(z / s_T[p]);
+      acc[p] += E ? -la : -log1mexp(la);
     }
   }
+  double* my = part + size_t(blockIdx.x) * (kGrid + 1);
+#pragma unroll
+  for (int p = 0; p < kGroup; ++p) {
+    const double sp = block_sum_f64(acc[p], red);
+    if (tid == 0) my[g0 + p] = sp;
+  }
   const double c = block_sum_f64(cnt, red);
-  if (tid == 0) part[kGrid] = c;
-}
+  if (tid == 0 && blockIdx.y == 0) my[kGrid] = c;
 
-// One wave: sums the partials in chunk order, picks the best temperature (first on a tie)
-// and narrows the bracket, or, after the last round, publishes T_k.
-__global__ __launch_bounds__(kGrid) void sts_select_kernel(StsArgs a, StsLayout l, int k, int last) {
-  char* ws = static_cast<char*>(a.ws);
-  const double* part = reinterpret_cast<const double*>(ws + l.off_part);
-  StsState* stp = reinterpret_cast<StsState*>(ws + l.off_state);
-  const int p = threadIdx.x;
-  double f = 0.0, cnt = 0.0;
-  for (int c = 0; c < l.chunks; ++c) {
-    f += part[size_t(c) * (kGrid + 1) + p];
-    cnt += part[size_t(c) * (kGrid + 1) + kGrid];
+  // the last workgroup of the round selects
+  __threadfence();
+  if (tid == 0) {
+    const unsigned total = gridDim.x * gridDim.y;
+    s_last = atomicAdd(&stp->done, 1u) == total - 1;
+  }
+  __syncthreads();
+  if (!s_last || tid >= kGrid) return;
+  __threadfence();
+  const int p = tid;
+  double f = 0.0, n_obs = 0.0;
+  for (int ch = 0; ch < int(gridDim.x); ++ch) {
+    f += part[size_t(ch) * (kGrid + 1) + p];
+    n_obs += part[size_t(ch) * (kGrid + 1) + kGrid];
   }
   double bf = f;
   int bp = p;
@@ -154,30 +176,22 @@ __global__ __launch_bounds__(kGrid) void sts_select_kernel(StsArgs a, StsLayout 
     }
   }
   if (p != 0) return;
-  StsState st = *stp;
+  StsState nx = st;
+  nx.done = 0u;
   const double lo0 = log(double(a.T_lo)), hi0 = log(double(a.T_hi));
-  if (cnt == 0.0 || last) {
-    const double T = cnt == 0.0 ? 1.0 : exp(st.u_lo + bp * st.du);
+  if (n_obs == 0.0 || last) {
+    const double T = n_obs == 0.0 ? 1.0 : exp(st.u_lo + bp * st.du);
     a.T_out[k] = float(T);
-    if (a.nll_out) a.nll_out[k] = cnt == 0.0 ? 0.0 : bf;
-    st.T = T;
-    st.u_lo = lo0;  // the next position starts from the whole bracket
-    st.du = (hi0 - lo0) / (kGrid - 1);
+    if (a.nll_out) a.nll_out[k] = n_obs == 0.0 ? 0.0 : bf;
+    nx.T = T;
+    nx.u_lo = lo0;  // the next position starts from the whole bracket
+    nx.du = (hi0 - lo0) / (kGrid - 1);
   } else {
     const int lo = bp > 0 ? bp - 1 : 0, hi = bp < kGrid - 1 ? bp + 1 : kGrid - 1;
-    st.u_lo = st.u_lo + lo * st.du;
-    st.du = (hi - lo) * st.du / (kGrid - 1);
+    nx.u_lo = st.u_lo + lo * st.du;
+    nx.du = (hi - lo) * st.du / (kGrid - 1);
   }
-  *stp = st;
-}
-
-// Adds position k's calibrated log-sigmoid to every sample's running log survival.
-__global__ __launch_bounds__(kCalThreads) void sts_advance_kernel(StsArgs a, StsLayout l, int k) {
-  char* ws = static_cast<char*>(a.ws);
-  double* L = reinterpret_cast<double*>(ws + l.off_L);
-  const double T = reinterpret_cast<const StsState*>(ws + l.off_state)->T;
-  for (int i = blockIdx.x * kCalThreads + threadIdx.x; i < a.N; i += gridDim.x * kCalThreads)
-    L[i] += log_sigmoid(double(a.z[size_t(i) * a.G1 + k]) / T);
+  *stp = nx;
 }
 
 // ---------------------------------------------------------------- ECE
@@ -297,13 +311,10 @@ size_t sts_workspace_bytes(int N) { return sts_layout(N).total; }
 hipError_t launch_sts_fit(const StsArgs& a, hipStream_t stream) {
   const StsLayout l = sts_layout(a.N);
   hipLaunchKernelGGL(sts_init_kernel, dim3(l.chunks), dim3(kCalThreads), 0, stream, a, l);
-  for (int k = 0; k < a.G1; ++k) {
-    for (int r = 0; r < kRounds; ++r) {
-      hipLaunchKernelGGL(sts_eval_kernel, dim3(l.chunks), dim3(kCalThreads), 0, stream, a, l, k);
-      hipLaunchKernelGGL(sts_select_kernel, dim3(1), dim3(kGrid), 0, stream, a, l, k, int(r == kRounds - 1));
-    }
-    hipLaunchKernelGGL(sts_advance_kernel, dim3(l.chunks), dim3(kCalThreads), 0, stream, a, l, k);
-  }
+  for (int k = 0; k < a.G1; ++k)
+    for (int r = 0; r < kRounds; ++r)
+      hipLaunchKernelGGL(sts_round_kernel, dim3(l.chunks, kGrid / kGroup), dim3(kCalThreads), 0, stream, a,
+                         l, k, r, int(r == kRounds - 1));
   return hipGetLastError();
 }
 
