@@ -21,7 +21,8 @@ Sources (web pages; cited by title and section, never by a line of any copy):
           "4. 零开销调度如何隐藏计算成本" (the additive step-cost model T(bs, K)),
           "5. 可观测性：理解修剪下的真实性能" (the cap-accept verify mode).
 * [NOTES] "DSpark：投机解码与生产级 Serving 学习笔记" (sorenprojections.com),
-          sections "02 · Speculative Decoding", "07 · Confidence Head",
+          sections "02 · Speculative Decoding", "05 · Core Innovation A"
+          (semi-autoregressive generation, the Markov head), "07 · Confidence Head",
           "08 · Core Innovation B", "09 · End-to-End Cycle".
 
 Pins: each function is checked in ``tests/test_oracle_pins.py`` and
@@ -37,6 +38,7 @@ from .scheduling import confidence_from_head, survival, schedule_windows
 from .packing import pack_ragged
 from .attention import verify_attention
 from .calibration import sts_fit, ece, log_prefix_survival
+from .markov import markov_sample
 from .acceptance import (softmax64, inverse_cdf, accept_request, accept_request_capped,
                          accept_and_commit, confidence_labels)
 
@@ -55,4 +57,5 @@ __all__ = [
     "sts_fit",
     "ece",
     "log_prefix_survival",
+    "markov_sample",
 ]

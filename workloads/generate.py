@@ -29,6 +29,11 @@ any request can be regenerated alone and arrays are independent of each other):
   over-confident head); draft k is accepted iff U[0, 1) < q, and the accept length is the
   number of leading accepted drafts; the observed length is gamma - 1 (full-block runs) or,
   censored, U{0 .. gamma-1} (compact runs, which verify only the window).
+* Markov-head inputs (``markov_inputs``): base logits U [B, gamma-1, V] ~ N(0, 2^2) in the
+  logit dtype; anchors uniform over the vocabulary; uniforms U[0, 1) float32; the rank-r
+  factors as int8 uniform on [-127, 127] ([V, r] each: embedding rows and vocabulary rows)
+  with float32 scales 4.2e-3 * U[0.5, 1.5] per row (a bias of standard deviation about
+  1.5 at r = 256).
 """
 
 from __future__ import annotations
@@ -221,3 +226,19 @@ def calibration_trace(seed: int, N: int, G1: int, T_true, beta=(6.0, 1.5), noise
     n = np.where(acc.all(axis=1), G1, np.argmin(acc, axis=1)).astype(np.int32)
     obs = r_o.integers(0, G1 + 1, size=N).astype(np.int32) if censor else np.full(N, G1, np.int32)
     return z, n, obs
+
+
+def markov_inputs(seed: int, B: int, G1: int, V: int, r: int = 256, dtype: str = "bf16"):
+    """Inputs of the Markov sequential head (recipe in the module docstring).  Returns dict
+    U (torch [B, G1, V]), anchor int32 [B], u float32 [B, G1], q1, q2 int8 [V, r],
+    s1, s2 float32 [V]."""
+    ss = np.random.SeedSequence([seed, 0x3A4])
+    rU, rA, rW, rS = (np.random.Generator(np.random.PCG64(s)) for s in ss.spawn(4))
+    U = _round(2.0 * rU.standard_normal((B, G1, V), dtype=np.float32), dtype)
+    anchor = rA.integers(0, V, size=B).astype(np.int32)
+    u = rA.random((B, G1), dtype=np.float32)
+    q1 = rW.integers(-127, 128, size=(V, r), dtype=np.int8)
+    q2 = rW.integers(-127, 128, size=(V, r), dtype=np.int8)
+    s1 = (4.2e-3 * rS.uniform(0.5, 1.5, size=V)).astype(np.float32)
+    s2 = (4.2e-3 * rS.uniform(0.5, 1.5, size=V)).astype(np.float32)
+    return {"U": U, "anchor": anchor, "u": u, "q1": q1, "q2": q2, "s1": s1, "s2": s2}
