@@ -16,6 +16,8 @@
  *   rva_sts_fit            calibration: per-position temperatures of the confidence head
  *                          fitted to acceptance traces (input of stage 1)
  *   rva_calibration_ece    calibration: expected calibration error of the survival
+ *   rva_markov_sample      drafter side: Markov sequential head, per-position logits and
+ *                          draws in order (produces the draft tokens and logits of stage 4)
  *
  * Sources, cited by page title and section:
  *   [SGL]   "DFlash 到 DSpark in SGLang：解码提速 4.3×，以及 DeepSeek-V4 支持"
@@ -359,6 +361,44 @@ rva_status rva_calibration_ece(int N, int G1, const float* z, const int32_t* acc
                                double* ece_out, int32_t* bin_counts, void* workspace,
                                size_t workspace_bytes, hipStream_t stream);
 size_t rva_calibration_ece_workspace_size(int N, int G1, int n_bins);
+
+/*
+ * Drafter side -- rva_markov_sample (Markov sequential head)
+ *
+ * [NOTES] "05 · Core Innovation A", 5.1-5.3: the parallel backbone gives base logits U_k
+ * for every draft position in one pass; the sequential head adds a bias that depends on
+ * the previous token, B(x_{k-1}, v), a rank-r product W1 W2 (r = 256 by default), and the
+ * positions are sampled in order ("09 · End-to-End Cycle").  Output: the draft tokens and
+ * the final draft logits that rva_accept_and_commit consumes as the draft distribution.
+ *
+ * For each request b and k = 1 .. G1 (x_0 = anchor[b]):
+ *   l_k(v) = U[b, k-1, v] + (w1_scale[x] * w2_scale[v]) * sum_j w1[x, j] * w2[v, j],
+ *            x = x_{k-1}; the int8 dot is exact, the rest is float64 with one rounded
+ *            multiply and one rounded add; stored in logit_dtype (bf16: via float32, RNE);
+ *   x_k = the smallest v whose cumulative exp(l_k - max) in ascending token order exceeds
+ *         u[b, k-1] * (total), computed from the STORED logits in float64.
+ *
+ *   B in [1, 4096]; G1 = gamma - 1 in [1, 63]; V >= 1; r in {64, 128, 256}.
+ *   logit_dtype     RVA_BF16 or RVA_F32 for base_logits and draft_logits.
+ *   base_logits     [B, G1, V]; draft_logits [B, G1, V] output (must not alias).
+ *   anchor          [B] int32; u [B, G1] float32 in [0, 1).
+ *   w1, w2          [V, r] int8 (16-byte aligned): embedding rows of the previous token and
+ *                   projection rows of the next; w1_scale, w2_scale [V] float32.
+ *   draft_tokens    [B, G1] int32 output; p_at [B, G1] float32 output (probability of
+ *                   each drawn token) or NULL.
+ *   workspace       rva_markov_workspace_size(B, V) bytes, 256-byte aligned.
+ *   device_status   optional: RVA_DEV_BAD_TOKEN for an anchor outside [0, V) (token 0 is
+ *                   used in its place).
+ * Launches 2 * G1 kernels (a tile-parallel logits pass with int8 MFMA and a per-request
+ * draw, per position).
+ */
+rva_status rva_markov_sample(int B, int G1, int V, int r, int logit_dtype,
+                             const void* base_logits, const int32_t* anchor, const float* u,
+                             const int8_t* w1, const float* w1_scale, const int8_t* w2,
+                             const float* w2_scale, void* draft_logits, int32_t* draft_tokens,
+                             float* p_at, int32_t* device_status, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+size_t rva_markov_workspace_size(int B, int V);
 
 /* Message for the last error returned on the calling thread ("" if none). */
 const char* rva_last_error(void);

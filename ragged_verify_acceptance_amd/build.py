@@ -20,7 +20,7 @@ INCLUDE = os.path.join(os.path.dirname(PKG_DIR), "include")
 
 ARCH = "gfx950"
 SOURCES = ["rva_api.cpp", "schedule.hip", "pack.hip", "attention.hip", "accept.hip",
-           "calibrate.hip"]
+           "calibrate.hip", "markov.hip"]
 # Packed-FP32 instructions are disabled for every device compile.
 CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result",

@@ -1,0 +1,349 @@
+// Markov sequential head of the block drafter: per draft position, the base logits of the
+// parallel backbone plus a previous-token bias from rank-r factors, then one draw; the
+// positions run in order because each bias needs the token drawn before it.
+//
+// Source: "DSpark：投机解码与生产级 Serving 学习笔记" (sorenprojections.com), section
+// "05 · Core Innovation A", 5.1-5.3: the backbone emits U_1 .. U_gamma in one pass; the
+// sequential head adds B(x_{k-1}, v) = (W1 W2)[x_{k-1}, v] of rank r = 256 (an embedding
+// lookup and a projection per step); section "09 · End-to-End Cycle": the light module
+// samples the positions one after another.
+//
+// Weights are int8 with float32 scales, both factors stored as [V, r] rows (q1[x] is the
+// embedding of the previous token, q2[v] the projection row of token v), so the dot
+// product is exact in int32 and the logit U_k(v) + (s1[x] s2[v]) dot is formed in float64
+// with explicitly rounded operations (no contraction) and stored in the dtype of U.  The
+// draw uses the stored logits (the draft distribution the acceptance step sees).
+//
+// Per position, two launches:
+//  * markov_logits_kernel: one workgroup per 128-token vocabulary tile.  Its four waves
+//    hold the tile's q2 rows in registers (64 contiguous bytes per lane: lane group g
+//    takes the g-th quarter of r, and the A operand walks r in the same order, so each
+//    MFMA pairs matching k -- an integer sum does not care about the order), gather
+//    q1[x_b] for 64 requests at a time into LDS, and run v_mfma_i32_16x16x32_i8.  The
+//    int32 dots go through LDS so the epilogue reads U and writes the logits as
+//    contiguous 8-token runs per thread, and each row's tile max and float64 sum of
+//    exp(l - max) are kept for the draw.
+//  * markov_sample_kernel: one workgroup per request combines the tile statistics into
+//    the row's maximum and total mass, finds the tile where the cumulative mass passes
+//    u * S (block scan of per-thread tile runs), and rescans that tile with one wave.
+#include <cmath>
+
+#include "rva_common.h"
+
+namespace rva {
+namespace {
+
+constexpr int kMkThreads = 256;
+constexpr int kTileV = 128;          // vocabulary entries per workgroup
+constexpr int kReqGroup = 64;        // requests per MFMA pass (4 row blocks of 16)
+constexpr int kDPitch = kTileV + 4;  // int32 pitch of the LDS dot tile
+constexpr int kSampleThreads = 256;
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+struct MkLayout {
+  size_t off_max, off_sum, total;
+  int ntiles;
+};
+
+MkLayout mk_layout(int B, int V) {
+  MkLayout l;
+  l.ntiles = (V + kTileV - 1) / kTileV;
+  auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
+  l.off_max = 0;
+  l.off_sum = up(size_t(B) * l.ntiles * sizeof(float));
+  l.total = l.off_sum + up(size_t(B) * l.ntiles * sizeof(double));
+  return l;
+}
+
+template <typename T> struct Out;
+template <> struct Out<uint16_t> {
+  __device__ static float load(const uint16_t* p, size_t i) { return bf16_to_f32(p[i]); }
+  __device__ static float round(double x) { return bf16_to_f32(f32_to_bf16(float(x))); }
+  __device__ static void store(uint16_t* p, size_t i, float v) { p[i] = f32_to_bf16(v); }
+};
+template <> struct Out<float> {
+  __device__ static float load(const float* p, size_t i) { return p[i]; }
+  __device__ static float round(double x) { return float(x); }
+  __device__ static void store(float* p, size_t i, float v) { p[i] = v; }
+};
+
+__device__ __forceinline__ int prev_token(const MarkovArgs& a, int b, int k) {
+  int x = k == 0 ? a.anchor[b] : a.tokens[size_t(b) * a.G1 + k - 1];
+  if (x < 0 || x >= a.V) {
+    flag(a.status, RVA_DEV_BAD_TOKEN);
+    x = 0;
+  }
+  return x;
+}
+
+template <typename T, int R>
+__global__ __launch_bounds__(kMkThreads) void markov_logits_kernel(MarkovArgs a, MkLayout l, int k) {
+  constexpr int kQ = R / 4;            // bytes of r per lane group
+  constexpr int kSteps = kQ / 8;       // MFMA k-steps (8 bytes per lane each)
+  constexpr int kEPitch = R + 16;      // LDS row pitch of the gathered embeddings
+  __shared__ __align__(16) int8_t sE[kReqGroup * kEPitch];
+  __shared__ __align__(16) int sD[kReqGroup * kDPitch];
+  __shared__ float sS1[kReqGroup];
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int g = lane / 16, c16 = lane % 16;
+  const int v0 = blockIdx.x * kTileV;
+  const int8_t* q1 = a.w1;
+  const int8_t* q2 = a.w2;
+
+  // this wave's two 16-token column blocks of q2, 64 bytes of r per lane (quarter g)
+  long bfrag[2][kSteps];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    const int v = min(v0 + (2 * wave + cb) * 16 + c16, a.V - 1);
+    const int8_t* row = q2 + size_t(v) * R + g * kQ;
+#pragma unroll
+    for (int s = 0; s < kSteps; s += 2) {
+      const uint4 w = *reinterpret_cast<const uint4*>(row + s * 8);
+      bfrag[cb][s] = (long(w.y) << 32) | long(uint32_t(w.x));
+      bfrag[cb][s + 1] = (long(w.w) << 32) | long(uint32_t(w.z));
+    }
+  }
+
+  const T* U = static_cast<const T*>(a.base);
+  T* O = static_cast<T*>(a.out);
+  float* tmax = reinterpret_cast<float*>(static_cast<char*>(a.ws) + l.off_max);
+  double* tsum = reinterpret_cast<double*>(static_cast<char*>(a.ws) + l.off_sum);
+  const bool vec = a.vec_ok;
+
+  for (int b0 = 0; b0 < a.B; b0 += kReqGroup) {
+    const int nb = min(kReqGroup, a.B - b0);
+    __syncthreads();  // the previous group's LDS is no longer read
+    // gather q1[x_b] rows (16 bytes per thread per step) and the scales
+    for (int it = tid; it < kReqGroup * (R / 16); it += kMkThreads) {
+      const int rl = it / (R / 16), c = it % (R / 16);
+      uint4 w = make_uint4(0, 0, 0, 0);
+      if (rl < nb) {
+        const int x = prev_token(a, b0 + rl, k);
+        w = *reinterpret_cast<const uint4*>(q1 + size_t(x) * R + c * 16);
+        if (c == 0) sS1[rl] = a.s1[x];
+      }
+      *reinterpret_cast<uint4*>(sE + rl * kEPitch + c * 16) = w;
+    }
+    __syncthreads();
+    // int8 MFMA: 4 row blocks x 2 column blocks per wave
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      v4i acc[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+      const int8_t* erow = sE + (rb * 16 + c16) * kEPitch + g * kQ;
+#pragma unroll
+      for (int s = 0; s < kSteps; ++s) {
+        const long av = *reinterpret_cast<const long*>(erow + s * 8);
+        acc[0] = __builtin_amdgcn_mfma_i32_16x16x32_i8(av, bfrag[0][s], acc[0], 0, 0, 0);
+        acc[1] = __builtin_amdgcn_mfma_i32_16x16x32_i8(av, bfrag[1][s], acc[1], 0, 0, 0);
+      }
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          sD[(rb * 16 + 4 * g + i) * kDPitch + (2 * wave + cb) * 16 + c16] = acc[cb][i];
+    }
+    __syncthreads();
+    // epilogue: thread item = (row, run of 8 tokens); 16 consecutive threads share a row
+    for (int it = tid; it < kReqGroup * (kTileV / 8); it += kMkThreads) {
+      const int rl = it / (kTileV / 8), c8 = it % (kTileV / 8);
+      const int b = b0 + rl;
+      const int vb = v0 + c8 * 8;
+      float lv[8];
+      float m = -INFINITY;
+      if (rl < nb) {
+        const size_t base = (size_t(b) * a.G1 + k) * a.V;
+        const double s1 = double(sS1[rl]);
+        float u8[8];
+        if (vec && vb + 8 <= a.V) {
+          if constexpr (sizeof(T) == 2) {
+            const uint4 w = *reinterpret_cast<const uint4*>(U + base + vb);
+            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              u8[2 * j] = bf16_to_f32(uint16_t(ww[j] & 0xffff));
+              u8[2 * j + 1] = bf16_to_f32(uint16_t(ww[j] >> 16));
+            }
+          } else {
+            const float4 w0 = *reinterpret_cast<const float4*>(U + base + vb);
+            const float4 w1 = *reinterpret_cast<const float4*>(U + base + vb + 4);
+            u8[0] = w0.x; u8[1] = w0.y; u8[2] = w0.z; u8[3] = w0.w;
+            u8[4] = w1.x; u8[5] = w1.y; u8[6] = w1.z; u8[7] = w1.w;
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) u8[j] = vb + j < a.V ? Out<T>::load(U, base + vb + j) : 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int v = vb + j;
+          if (v < a.V) {
+            const double t = s1 * double(a.s2[v]);  // exact: a product of two float32
+            const double lg = __dadd_rn(double(u8[j]), __dmul_rn(t, double(sD[rl * kDPitch + c8 * 8 + j])));
+            lv[j] = Out<T>::round(lg);
+            m = fmaxf(m, lv[j]);
+          } else {
+            lv[j] = -INFINITY;
+          }
+        }
+        if (vec && vb + 8 <= a.V) {
+          if constexpr (sizeof(T) == 2) {
+            uint4 w;
+            w.x = f32_to_bf16(lv[0]) | (uint32_t(f32_to_bf16(lv[1])) << 16);
+            w.y = f32_to_bf16(lv[2]) | (uint32_t(f32_to_bf16(lv[3])) << 16);
+            w.z = f32_to_bf16(lv[4]) | (uint32_t(f32_to_bf16(lv[5])) << 16);
+            w.w = f32_to_bf16(lv[6]) | (uint32_t(f32_to_bf16(lv[7])) << 16);
+            *reinterpret_cast<uint4*>(O + base + vb) = w;
+          } else {
+            *reinterpret_cast<float4*>(O + base + vb) = make_float4(lv[0], lv[1], lv[2], lv[3]);
+            *reinterpret_cast<float4*>(O + base + vb + 4) = make_float4(lv[4], lv[5], lv[6], lv[7]);
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            if (vb + j < a.V) Out<T>::store(O, base + vb + j, lv[j]);
+        }
+      }
+      // tile statistics of the row: max over 16 lanes, then the float64 mass below it
+#pragma unroll
+      for (int o = 8; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+      double sum = 0.0;
+      if (rl < nb) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (vb + j < a.V) sum += exp(double(lv[j]) - double(m));
+      }
+#pragma unroll
+      for (int o = 8; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
+      if (c8 == 0 && rl < nb) {
+        tmax[size_t(b) * l.ntiles + blockIdx.x] = m;
+        tsum[size_t(b) * l.ntiles + blockIdx.x] = sum;
+      }
+    }
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kSampleThreads) void markov_sample_kernel(MarkovArgs a, MkLayout l, int k) {
+  __shared__ double sc[kSampleThreads / kWave];
+  __shared__ float smax[kSampleThreads / kWave];
+  __shared__ int s_tile;
+  __shared__ double s_before, s_S;
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const float* tmax = reinterpret_cast<const float*>(static_cast<const char*>(a.ws) + l.off_max) + size_t(b) * l.ntiles;
+  const double* tsum = reinterpret_cast<const double*>(static_cast<const char*>(a.ws) + l.off_sum) + size_t(b) * l.ntiles;
+  const int nt = l.ntiles, per = (nt + kSampleThreads - 1) / kSampleThreads;
+  const int t0 = min(tid * per, nt), t1 = min(t0 + per, nt);
+  // row maximum
+  float m = -INFINITY;
+  for (int t = t0; t < t1; ++t) m = fmaxf(m, tmax[t]);
+  m = wave_max(m);
+  if (lane == 0) smax[wave] = m;
+  __syncthreads();
+  float M = smax[0];
+  for (int w = 1; w < kSampleThreads / kWave; ++w) M = fmaxf(M, smax[w]);
+  // this thread's run of tile masses, then a scan over threads (tile order).  Thread i
+  // owns [off + excl_i, off + inc_i); the next thread's lower end is the same expression,
+  // so the runs tile [0, S) without gaps or overlaps.
+  double part = 0.0;
+  for (int t = t0; t < t1; ++t) part += tsum[t] * exp(double(tmax[t]) - double(M));
+  double inc = part;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const double v = __shfl_up(inc, o);
+    if (lane >= o) inc += v;
+  }
+  const double excl_up = __shfl_up(inc, 1);
+  const double excl = lane == 0 ? 0.0 : excl_up;
+  if (lane == kWave - 1) sc[wave] = inc;
+  __syncthreads();
+  double off = 0.0;
+  for (int w = 0; w < wave; ++w) off += sc[w];
+  double S = 0.0;
+  for (int w = 0; w < kSampleThreads / kWave; ++w) S += sc[w];
+  const double before = off + excl, upper = off + inc;
+  const double target = double(a.u[size_t(b) * a.G1 + k]) * S;
+  if (tid == 0) {
+    s_tile = nt - 1;  // rounding can leave u * S at or past the last edge: the last tile
+    s_before = -1.0;
+    s_S = S;
+  }
+  __syncthreads();
+  if (t1 > t0 && before <= target && target < upper) {
+    double c = before;
+    int t = t0;
+    for (; t < t1 - 1; ++t) {
+      const double mt = tsum[t] * exp(double(tmax[t]) - double(M));
+      if (target < c + mt) break;
+      c += mt;
+    }
+    s_tile = t;
+    s_before = c;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  // rescan the tile: lane j takes tokens 2j, 2j+1
+  const int t = s_tile;
+  const T* O = static_cast<const T*>(a.out);
+  const size_t base = (size_t(b) * a.G1 + k) * a.V;
+  const int v = t * kTileV + 2 * lane;
+  const double e0 = v < a.V ? exp(double(Out<T>::load(O, base + v)) - double(M)) : 0.0;
+  const double e1 = v + 1 < a.V ? exp(double(Out<T>::load(O, base + v + 1)) - double(M)) : 0.0;
+  double c0;
+  if (s_before >= 0.0) {
+    c0 = s_before;
+  } else {
+    // the last tile after a rounding overshoot: its start is S minus its own mass
+    c0 = S - tsum[t] * exp(double(tmax[t]) - double(M));
+  }
+  double pinc = e0 + e1;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const double vv = __shfl_up(pinc, o);
+    if (lane >= o) pinc += vv;
+  }
+  const double cA = c0 + (pinc - e0 - e1) + e0;  // cumulative through token v
+  const double cB = c0 + pinc;                   // through token v + 1
+  int cand = a.V;                                 // smallest token whose cumulative passes
+  if (v < a.V && cA > target) cand = v;
+  else if (v + 1 < a.V && cB > target) cand = v + 1;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) cand = min(cand, __shfl_xor(cand, o));
+  if (cand == a.V) {
+    // nothing in the tile passes: past the last edge (u * S >= S after rounding) the inverse
+    // CDF clamps to the last token; otherwise the tile's recomputed mass fell short of its
+    // summary by a rounding step, and its last token is the edge within that rounding
+    cand = s_before >= 0.0 ? min(a.V - 1, t * kTileV + kTileV - 1) : a.V - 1;
+  }
+  if (lane == 0) {
+    a.tokens[size_t(b) * a.G1 + k] = cand;
+    if (a.p_at) a.p_at[size_t(b) * a.G1 + k] = float(exp(double(Out<T>::load(O, base + cand)) - double(M)) / s_S);
+  }
+}
+
+template <typename T, int R>
+hipError_t launch_markov_typed(const MarkovArgs& a, hipStream_t stream) {
+  const MkLayout l = mk_layout(a.B, a.V);
+  for (int k = 0; k < a.G1; ++k) {
+    hipLaunchKernelGGL((markov_logits_kernel<T, R>), dim3(l.ntiles), dim3(kMkThreads), 0, stream, a, l, k);
+    hipLaunchKernelGGL((markov_sample_kernel<T>), dim3(a.B), dim3(kSampleThreads), 0, stream, a, l, k);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t markov_workspace_bytes(int B, int V) { return mk_layout(B, V).total; }
+
+hipError_t launch_markov(const MarkovArgs& a, int dtype, hipStream_t stream) {
+  if (dtype == RVA_BF16) {
+    if (a.r == 256) return launch_markov_typed<uint16_t, 256>(a, stream);
+    if (a.r == 128) return launch_markov_typed<uint16_t, 128>(a, stream);
+    return launch_markov_typed<uint16_t, 64>(a, stream);
+  }
+  if (a.r == 256) return launch_markov_typed<float, 256>(a, stream);
+  if (a.r == 128) return launch_markov_typed<float, 128>(a, stream);
+  return launch_markov_typed<float, 64>(a, stream);
+}
+
+}  // namespace rva

@@ -369,4 +369,51 @@ rva_status rva_calibration_ece(int N, int G1, const float* z, const int32_t* acc
   return hip_result(rva::launch_ece(a, stream), "rva_calibration_ece launch");
 }
 
+size_t rva_markov_workspace_size(int B, int V) {
+  if (B < 1 || B > 4096 || V < 1) return 0;
+  return rva::markov_workspace_bytes(B, V);
+}
+
+rva_status rva_markov_sample(int B, int G1, int V, int r, int logit_dtype, const void* base_logits,
+                             const int32_t* anchor, const float* u, const int8_t* w1,
+                             const float* w1_scale, const int8_t* w2, const float* w2_scale,
+                             void* draft_logits, int32_t* draft_tokens, float* p_at,
+                             int32_t* device_status, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+  REQUIRE(B >= 1 && B <= 4096, "B must be in [1, 4096] (got %d)", B);
+  REQUIRE(G1 >= 1 && G1 <= 63, "G1 must be in [1, 63] (got %d)", G1);
+  REQUIRE(V >= 1 && (long long)V * r <= (1LL << 40), "V must be >= 1 (got %d)", V);
+  REQUIRE((long long)B * G1 * V <= (1LL << 40), "B*G1*V too large");
+  REQUIRE(r == 64 || r == 128 || r == 256, "r must be 64, 128 or 256 (got %d)", r);
+  REQUIRE(logit_dtype == RVA_BF16 || logit_dtype == RVA_F32, "unknown logit_dtype %d", logit_dtype);
+  REQUIRE(base_logits && anchor && u && w1 && w1_scale && w2 && w2_scale && draft_logits && draft_tokens,
+          "an input or output pointer is NULL");
+  REQUIRE(aligned(w1, 16) && aligned(w2, 16), "w1 and w2 must be 16-byte aligned");
+  REQUIRE(base_logits != draft_logits, "draft_logits must not alias base_logits");
+  const size_t need = rva::markov_workspace_bytes(B, V);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(RVA_ERR_WORKSPACE_TOO_SMALL, "rva_markov_sample: workspace needs %zu bytes (got %zu)",
+                need, workspace_bytes);
+  REQUIRE(aligned(workspace, 256), "workspace must be 256-byte aligned");
+  rva::MarkovArgs a{};
+  a.B = B;
+  a.G1 = G1;
+  a.V = V;
+  a.r = r;
+  a.base = base_logits;
+  a.anchor = anchor;
+  a.u = u;
+  a.w1 = w1;
+  a.s1 = w1_scale;
+  a.w2 = w2;
+  a.s2 = w2_scale;
+  a.out = draft_logits;
+  a.tokens = draft_tokens;
+  a.p_at = p_at;
+  a.status = device_status;
+  a.ws = workspace;
+  a.vec_ok = V % 8 == 0 && aligned(base_logits, 16) && aligned(draft_logits, 16);
+  return hip_result(rva::launch_markov(a, logit_dtype, stream), "rva_markov_sample launch");
+}
+
 }  // extern "C"

@@ -144,4 +144,23 @@ struct EceArgs {
 size_t ece_workspace_bytes(int N, int G1, int n_bins);
 hipError_t launch_ece(const EceArgs& a, hipStream_t stream);
 
+struct MarkovArgs {
+  int B, G1, V, r;
+  const void* base;        // [B, G1, V] base logits
+  const int32_t* anchor;   // [B]
+  const float* u;          // [B, G1]
+  const int8_t* w1;        // [V, r]
+  const float* s1;         // [V]
+  const int8_t* w2;        // [V, r]
+  const float* s2;         // [V]
+  void* out;               // [B, G1, V] logits (dtype of base)
+  int32_t* tokens;         // [B, G1]
+  float* p_at;             // [B, G1] or NULL
+  int32_t* status;
+  void* ws;
+  bool vec_ok;             // V a multiple of 8 and base / out 16-byte aligned
+};
+size_t markov_workspace_bytes(int B, int V);
+hipError_t launch_markov(const MarkovArgs& a, int dtype, hipStream_t stream);
+
 }  // namespace rva

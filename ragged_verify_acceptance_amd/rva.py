@@ -36,7 +36,7 @@ EXPORTED = [
     "rva_verify_attention_workspace_size", "rva_accept_and_commit",
     "rva_accept_workspace_size", "rva_confidence_labels", "rva_accept_capped", "rva_sts_fit",
     "rva_sts_fit_workspace_size", "rva_calibration_ece", "rva_calibration_ece_workspace_size",
-    "rva_last_error", "rva_version",
+    "rva_markov_sample", "rva_markov_workspace_size", "rva_last_error", "rva_version",
 ]
 
 
@@ -67,11 +67,14 @@ _SIGS = {
     "rva_sts_fit_workspace_size": [_i],
     "rva_calibration_ece": [_i, _i, _p, _p, _p, _p, _i, _p, _p, _p, _z, _p],
     "rva_calibration_ece_workspace_size": [_i, _i, _i],
+    "rva_markov_sample": [_i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _z, _p],
+    "rva_markov_workspace_size": [_i, _i],
     "rva_last_error": [],
     "rva_version": [],
 }
 _RESTYPES = {"rva_verify_attention_workspace_size": _z, "rva_accept_workspace_size": _z,
              "rva_sts_fit_workspace_size": _z, "rva_calibration_ece_workspace_size": _z,
+             "rva_markov_workspace_size": _z,
              "rva_last_error": ctypes.c_char_p}
 
 
@@ -232,3 +235,16 @@ def calibration_ece(N, G1, z, accept_len, observed_len, T, n_bins, ece_out, bin_
         N, G1, _ptr(z), _ptr(accept_len), _ptr(observed_len), _ptr(T), n_bins, _ptr(ece_out),
         _ptr(bin_counts), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(stream)))
+
+
+def markov_workspace_size(B, V):
+    return lib().rva_markov_workspace_size(B, V)
+
+
+def markov_sample(B, G1, V, r, base_logits, anchor, u, w1, w1_scale, w2, w2_scale, draft_logits,
+                  draft_tokens, p_at, workspace, device_status=None, stream=None):
+    _check("rva_markov_sample", lib().rva_markov_sample(
+        B, G1, V, r, dtype_code(base_logits), _ptr(base_logits), _ptr(anchor), _ptr(u), _ptr(w1),
+        _ptr(w1_scale), _ptr(w2), _ptr(w2_scale), _ptr(draft_logits), _ptr(draft_tokens),
+        _ptr(p_at), _ptr(device_status), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))

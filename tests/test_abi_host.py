@@ -29,7 +29,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     L = rva.lib()
     names = declared_functions()
-    assert "rva_verify_attention" in names and len(names) == 14
+    assert "rva_verify_attention" in names and len(names) == 16
     for n in names:
         assert hasattr(L, n), f"{n} declared in rva.h but not exported"
     assert set(names) == set(rva.EXPORTED)
@@ -209,3 +209,24 @@ def test_calibration_validation():
     assert ece(out=None) == INVALID
     assert ece(w=None) == WS_SMALL
     assert ece(wb=we - 1) == WS_SMALL
+
+
+def test_markov_validation():
+    L = rva.lib()
+    ws = rva.markov_workspace_size(64, 151936)
+    assert ws > 0 and rva.markov_workspace_size(0, 10) == 0
+
+    def mk(B=64, G1=7, V=151936, r=256, dt=1, base=FAKE, out=ctypes.c_void_p(0x200000), w1=FAKE,
+           w=FAKE, wb=ws):
+        return L.rva_markov_sample(B, G1, V, r, dt, base, FAKE, FAKE, w1, FAKE, FAKE, FAKE, out,
+                                   FAKE, None, None, w, wb, None)
+
+    assert mk(B=0) == INVALID
+    assert mk(G1=64) == INVALID
+    assert mk(r=96) == INVALID
+    assert mk(dt=4) == INVALID
+    assert mk(base=None) == INVALID
+    assert mk(out=FAKE) == INVALID                        # aliasing the base logits
+    assert mk(w1=ctypes.c_void_p(0x100008)) == INVALID    # not 16-byte aligned
+    assert mk(w=None) == WS_SMALL
+    assert mk(wb=ws - 1) == WS_SMALL
