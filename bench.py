@@ -161,6 +161,77 @@ def cost_table(inp, reps, warm):
     }
 
 
+def markov_bench(wl, steps, warmup, cpu):
+    """Markov sequential head over the workload's batch: G1 positions drawn in order, each
+    an int8-MFMA vocabulary pass and a per-request draw; HIP events on the launch stream."""
+    import torch
+
+    from ragged_verify_acceptance_amd import rva
+    from workloads.generate import markov_inputs
+
+    B, G1, V, r = wl.B, wl.G1, wl.V, 256
+    inp = markov_inputs(wl.seed, B, G1, V, r=r, dtype=wl.logit_dtype)
+    dev = "cuda"
+    t = lambda x, d: torch.as_tensor(np.ascontiguousarray(x)).to(d).to(dev)
+    U = inp["U"].to(dev)
+    anchor, u = t(inp["anchor"], torch.int32), t(inp["u"], torch.float32)
+    q1, s1 = t(inp["q1"], torch.int8), t(inp["s1"], torch.float32)
+    q2, s2 = t(inp["q2"], torch.int8), t(inp["s2"], torch.float32)
+    out = torch.empty_like(U)
+    tokens = torch.empty((B, G1), dtype=torch.int32, device=dev)
+    p_at = torch.empty((B, G1), dtype=torch.float32, device=dev)
+    ws = torch.empty(rva.markov_workspace_size(B, V), dtype=torch.uint8, device=dev)
+
+    def call():
+        rva.markov_sample(B, G1, V, r, U, anchor, u, q1, s1, q2, s2, out, tokens, p_at, ws)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    s_lg = 2 if wl.logit_dtype == "bf16" else 4
+    # per position: the q2 factor once, U in, logits out, the gathered q1 rows, the scales
+    per_pos = V * r + 2 * B * V * s_lg + B * r + 2 * V * 4
+    bytes_call = G1 * per_pos
+    gbs = bytes_call / (ms * 1e-3) / 1e9
+    res = {
+        "metric": "Markov sequential head: drafted tokens/s (B requests x gamma-1 positions)",
+        "value": B * G1 / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": ms, "higher_is_better": True, "dtype": "i8 x i8 -> i32, f64",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name} Markov head", "B": B, "G1": G1, "V": V, "r": r,
+                   "logit_dtype": wl.logit_dtype},
+        "roofline": {"kernel": "rva_markov_sample (markov_logits_kernel + markov_sample_kernel)",
+                     "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": gbs / PEAK_HBM_GBS, "traffic": None, "algorithmic_bytes": bytes_call},
+        "int8_TOPs": 2.0 * B * r * V * G1 / (ms * 1e-3) / 1e12,
+    }
+    if cpu:
+        import time
+
+        from threadpoolctl import threadpool_limits
+
+        import oracle
+
+        n = 2
+        with threadpool_limits(1):
+            t0 = time.perf_counter()
+            oracle.markov_sample(inp["U"][:n], inp["anchor"][:n], inp["u"][:n], inp["q1"],
+                                 inp["s1"], inp["q2"], inp["s2"])
+            dt = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": n * G1 / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                               "sample": f"{n} of {B} requests x {G1} positions, float64 NumPy, "
+                                         f"1 thread, {dt:.1f} s"}
+    return res
+
+
 def sts_bench(wl, steps, reps, cpu):
     """Acceptance trace from the acceptance call itself (full blocks, so every position is
     observed), an over-confident head on it, then the STS fit and ECE calls, timed."""
@@ -266,7 +337,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="mixed-b64")
     ap.add_argument("--mode", default="compact",
-                    choices=["compact", "static", "cap-accept", "cost-table", "sts"],
+                    choices=["compact", "static", "cap-accept", "cost-table", "sts", "markov"],
                     help="cap-accept: whole blocks verified, commits capped at the scheduled windows; "
                          "cost-table: measure T(bs, M) by graph replay and fit the scheduler's tables")
     ap.add_argument("--trace-steps", type=int, default=200,
@@ -292,6 +363,10 @@ def main():
 
     torch.cuda.set_device(0)
     wl = get(args.workload)
+    if args.mode == "markov":
+        print(json.dumps(markov_bench(wl, steps=args.steps, warmup=args.warmup,
+                                      cpu=args.cpu_sample > 0)))
+        return
     if args.mode == "sts":
         print(json.dumps(sts_bench(wl, args.trace_steps, reps=max(3, args.steps),
                                    cpu=args.cpu_sample > 0)))

@@ -16,18 +16,20 @@
 //
 // Per position, two launches:
 //  * markov_logits_kernel: one workgroup per 128-token vocabulary tile.  Its four waves
-//    hold the tile's q2 rows in registers (64 contiguous bytes per lane: lane group g
-//    takes the g-th quarter of r, and the A operand walks r in the same order, so each
-//    MFMA pairs matching k -- an integer sum does not care about the order), gather
-//    q1[x_b] for 64 requests at a time into LDS, and run v_mfma_i32_16x16x32_i8.  The
-//    int32 dots go through LDS so the epilogue reads U and writes the logits as
-//    contiguous 8-token runs per thread, and each row's tile max and float64 sum of
-//    exp(l - max) are kept for the draw.
+//    hold the tile's q2 rows in registers as the MFMA's A operand (64 contiguous bytes per
+//    lane: lane group g takes the g-th quarter of r, and the B operand -- q1[x_b] of 64
+//    requests at a time, gathered into LDS -- walks r in the same order, so each MFMA pairs
+//    matching k; an integer sum does not care about the order), and run
+//    v_mfma_i32_16x16x32_i8.  With tokens as the MFMA rows each lane ends with 4
+//    consecutive tokens of one request, so the epilogue reads U and writes the logits
+//    straight from the accumulators (U is requested before the MFMA), and each request's
+//    tile max and float64 mass below it are merged over lanes and waves for the draw.
 //  * markov_sample_kernel: one workgroup per request combines the tile statistics into
 //    the row's maximum and total mass, finds the tile where the cumulative mass passes
 //    u * S (block scan of per-thread tile runs), and rescans that tile with one wave.
 #include <cmath>
 
+#include "exp2_f64.h"
 #include "rva_common.h"
 
 namespace rva {
@@ -36,7 +38,6 @@ namespace {
 constexpr int kMkThreads = 256;
 constexpr int kTileV = 128;          // vocabulary entries per workgroup
 constexpr int kReqGroup = 64;        // requests per MFMA pass (4 row blocks of 16)
-constexpr int kDPitch = kTileV + 4;  // int32 pitch of the LDS dot tile
 constexpr int kSampleThreads = 256;
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -77,31 +78,38 @@ __device__ __forceinline__ int prev_token(const MarkovArgs& a, int b, int k) {
   return x;
 }
 
-template <typename T, int R>
-__global__ __launch_bounds__(kMkThreads) void markov_logits_kernel(MarkovArgs a, MkLayout l, int k) {
+// VEC: V is a multiple of 8 and U / out are 16-byte aligned, so a lane's 4 tokens are one
+// aligned vector access; its loads are then issued unconditionally from clamped addresses
+// (no branch between issue and use, so the compiler keeps them in flight together).
+template <typename T, int R, bool VEC>
+__global__ __launch_bounds__(kMkThreads) void markov_logits_kernel(MarkovArgs a, MkLayout l, int k,
+                                                                    Exp2Poly P) {
   constexpr int kQ = R / 4;            // bytes of r per lane group
   constexpr int kSteps = kQ / 8;       // MFMA k-steps (8 bytes per lane each)
-  constexpr int kEPitch = R + 16;      // LDS row pitch of the gathered embeddings
+  constexpr int kEPitch = R + 8;       // LDS row pitch of the gathered embeddings (8-aligned)
+  constexpr int kW = kMkThreads / kWave;
   __shared__ __align__(16) int8_t sE[kReqGroup * kEPitch];
-  __shared__ __align__(16) int sD[kReqGroup * kDPitch];
   __shared__ float sS1[kReqGroup];
+  __shared__ double tab[256];
+  __shared__ float wmax[kW][kReqGroup];
+  __shared__ double wsum[kW][kReqGroup];
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int g = lane / 16, c16 = lane % 16;
   const int v0 = blockIdx.x * kTileV;
-  const int8_t* q1 = a.w1;
-  const int8_t* q2 = a.w2;
+  if (tid < 256) tab[tid] = exp2_f64(P, double(tid) / 256.0);  // read after the barriers below
 
-  // this wave's two 16-token column blocks of q2, 64 bytes of r per lane (quarter g)
-  long bfrag[2][kSteps];
+  // this wave's two 16-token column blocks of q2 as the MFMA's A operand: lane row c16 is
+  // token v0 + 16 (2 wave + cb) + c16, 64 bytes of r per lane (quarter g)
+  long afrag[2][kSteps];
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
     const int v = min(v0 + (2 * wave + cb) * 16 + c16, a.V - 1);
-    const int8_t* row = q2 + size_t(v) * R + g * kQ;
+    const int8_t* row = a.w2 + size_t(v) * R + g * kQ;
 #pragma unroll
     for (int s = 0; s < kSteps; s += 2) {
       const uint4 w = *reinterpret_cast<const uint4*>(row + s * 8);
-      bfrag[cb][s] = (long(w.y) << 32) | long(uint32_t(w.x));
-      bfrag[cb][s + 1] = (long(w.w) << 32) | long(uint32_t(w.z));
+      afrag[cb][s] = (long(w.y) << 32) | long(uint32_t(w.x));
+      afrag[cb][s + 1] = (long(w.w) << 32) | long(uint32_t(w.z));
     }
   }
 
@@ -109,10 +117,50 @@ __global__ __launch_bounds__(kMkThreads) void markov_logits_kernel(MarkovArgs a,
   T* O = static_cast<T*>(a.out);
   float* tmax = reinterpret_cast<float*>(static_cast<char*>(a.ws) + l.off_max);
   double* tsum = reinterpret_cast<double*>(static_cast<char*>(a.ws) + l.off_sum);
-  const bool vec = a.vec_ok;
-
+  // the scales of this lane's 8 tokens (4 per column block)
+  float s2v[2][4];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    const int vb = v0 + (2 * wave + cb) * 16 + 4 * g;
+    if constexpr (VEC) {
+      const float4 w = *reinterpret_cast<const float4*>(a.s2 + min(vb, a.V - 4));
+      s2v[cb][0] = w.x; s2v[cb][1] = w.y; s2v[cb][2] = w.z; s2v[cb][3] = w.w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s2v[cb][i] = a.s2[min(vb + i, a.V - 1)];
+    }
+  }
+  // output element of (row block rb, column block cb, i): request rb*16 + c16, token
+  // v0 + 16 (2 wave + cb) + 4 g + i (the MFMA result layout: lane column c16, rows 4g + i)
   for (int b0 = 0; b0 < a.B; b0 += kReqGroup) {
     const int nb = min(kReqGroup, a.B - b0);
+    // the epilogue's base logits, requested before the gather and the MFMA
+    float uv[4][2][4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        const int rl = rb * 16 + c16, vb = v0 + (2 * wave + cb) * 16 + 4 * g;
+        if constexpr (VEC) {
+          // rows past the batch and tokens past V read a valid place; their values are unused
+          const size_t base = (size_t(b0 + min(rl, nb - 1)) * a.G1 + k) * a.V + min(vb, a.V - 4);
+          if constexpr (sizeof(T) == 2) {
+            const uint2 w = *reinterpret_cast<const uint2*>(U + base);
+            uv[rb][cb][0] = bf16_to_f32(uint16_t(w.x & 0xffff));
+            uv[rb][cb][1] = bf16_to_f32(uint16_t(w.x >> 16));
+            uv[rb][cb][2] = bf16_to_f32(uint16_t(w.y & 0xffff));
+            uv[rb][cb][3] = bf16_to_f32(uint16_t(w.y >> 16));
+          } else {
+            const float4 w = *reinterpret_cast<const float4*>(U + base);
+            uv[rb][cb][0] = w.x; uv[rb][cb][1] = w.y; uv[rb][cb][2] = w.z; uv[rb][cb][3] = w.w;
+          }
+        } else {
+          const size_t base = (size_t(b0 + rl) * a.G1 + k) * a.V;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            uv[rb][cb][i] = (rl < nb && vb + i < a.V) ? Out<T>::load(U, base + vb + i) : 0.f;
+        }
+      }
     __syncthreads();  // the previous group's LDS is no longer read
     // gather q1[x_b] rows (16 bytes per thread per step) and the scales
     for (int it = tid; it < kReqGroup * (R / 16); it += kMkThreads) {
@@ -120,116 +168,103 @@ __global__ __launch_bounds__(kMkThreads) void markov_logits_kernel(MarkovArgs a,
       uint4 w = make_uint4(0, 0, 0, 0);
       if (rl < nb) {
         const int x = prev_token(a, b0 + rl, k);
-        w = *reinterpret_cast<const uint4*>(q1 + size_t(x) * R + c * 16);
+        w = *reinterpret_cast<const uint4*>(a.w1 + size_t(x) * R + c * 16);
         if (c == 0) sS1[rl] = a.s1[x];
       }
-      *reinterpret_cast<uint4*>(sE + rl * kEPitch + c * 16) = w;
+      uint2* dst = reinterpret_cast<uint2*>(sE + rl * kEPitch + c * 16);
+      dst[0] = make_uint2(w.x, w.y);
+      dst[1] = make_uint2(w.z, w.w);
     }
     __syncthreads();
-    // int8 MFMA: 4 row blocks x 2 column blocks per wave
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
+      const int rl = rb * 16 + c16;
       v4i acc[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
-      const int8_t* erow = sE + (rb * 16 + c16) * kEPitch + g * kQ;
+      const int8_t* erow = sE + rl * kEPitch + g * kQ;
 #pragma unroll
       for (int s = 0; s < kSteps; ++s) {
-        const long av = *reinterpret_cast<const long*>(erow + s * 8);
-        acc[0] = __builtin_amdgcn_mfma_i32_16x16x32_i8(av, bfrag[0][s], acc[0], 0, 0, 0);
-        acc[1] = __builtin_amdgcn_mfma_i32_16x16x32_i8(av, bfrag[1][s], acc[1], 0, 0, 0);
+        const long bv = *reinterpret_cast<const long*>(erow + s * 8);
+        acc[0] = __builtin_amdgcn_mfma_i32_16x16x32_i8(afrag[0][s], bv, acc[0], 0, 0, 0);
+        acc[1] = __builtin_amdgcn_mfma_i32_16x16x32_i8(afrag[1][s], bv, acc[1], 0, 0, 0);
       }
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          sD[(rb * 16 + 4 * g + i) * kDPitch + (2 * wave + cb) * 16 + c16] = acc[cb][i];
-    }
-    __syncthreads();
-    // epilogue: thread item = (row, run of 8 tokens); 16 consecutive threads share a row
-    for (int it = tid; it < kReqGroup * (kTileV / 8); it += kMkThreads) {
-      const int rl = it / (kTileV / 8), c8 = it % (kTileV / 8);
-      const int b = b0 + rl;
-      const int vb = v0 + c8 * 8;
-      float lv[8];
+      // logits of request rl at this lane's 8 tokens, and their (max, mass) summary
+      const double s1 = double(sS1[rl]);
+      const size_t base = (size_t(b0 + rl) * a.G1 + k) * a.V;
+      float lv[2][4];
       float m = -INFINITY;
-      if (rl < nb) {
-        const size_t base = (size_t(b) * a.G1 + k) * a.V;
-        const double s1 = double(sS1[rl]);
-        float u8[8];
-        if (vec && vb + 8 <= a.V) {
-          if constexpr (sizeof(T) == 2) {
-            const uint4 w = *reinterpret_cast<const uint4*>(U + base + vb);
-            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              u8[2 * j] = bf16_to_f32(uint16_t(ww[j] & 0xffff));
-              u8[2 * j + 1] = bf16_to_f32(uint16_t(ww[j] >> 16));
+      for (int cb = 0; cb < 2; ++cb) {
+        const int vb = v0 + (2 * wave + cb) * 16 + 4 * g;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int v = vb + i;
+          lv[cb][i] = -INFINITY;
+          if (rl < nb && v < a.V) {
+            const double t = s1 * double(s2v[cb][i]);  // exact: a product of two float32
+            const double lg = __dadd_rn(double(uv[rb][cb][i]), __dmul_rn(t, double(acc[cb][i])));
+            lv[cb][i] = Out<T>::round(lg);
+            m = fmaxf(m, lv[cb][i]);
+          }
+        }
+        if (rl < nb) {
+          if (VEC && vb < a.V) {
+            if constexpr (sizeof(T) == 2) {
+              *reinterpret_cast<uint2*>(O + base + vb) =
+                  make_uint2(f32_to_bf16(lv[cb][0]) | (uint32_t(f32_to_bf16(lv[cb][1])) << 16),
+                             f32_to_bf16(lv[cb][2]) | (uint32_t(f32_to_bf16(lv[cb][3])) << 16));
+            } else {
+              *reinterpret_cast<float4*>(O + base + vb) = make_float4(lv[cb][0], lv[cb][1], lv[cb][2], lv[cb][3]);
             }
           } else {
-            const float4 w0 = *reinterpret_cast<const float4*>(U + base + vb);
-            const float4 w1 = *reinterpret_cast<const float4*>(U + base + vb + 4);
-            u8[0] = w0.x; u8[1] = w0.y; u8[2] = w0.z; u8[3] = w0.w;
-            u8[4] = w1.x; u8[5] = w1.y; u8[6] = w1.z; u8[7] = w1.w;
-          }
-        } else {
 #pragma unroll
-          for (int j = 0; j < 8; ++j) u8[j] = vb + j < a.V ? Out<T>::load(U, base + vb + j) : 0.f;
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int v = vb + j;
-          if (v < a.V) {
-            const double t = s1 * double(a.s2[v]);  // exact: a product of two float32
-            const double lg = __dadd_rn(double(u8[j]), __dmul_rn(t, double(sD[rl * kDPitch + c8 * 8 + j])));
-            lv[j] = Out<T>::round(lg);
-            m = fmaxf(m, lv[j]);
-          } else {
-            lv[j] = -INFINITY;
+            for (int i = 0; i < 4; ++i)
+              if (vb + i < a.V) Out<T>::store(O, base + vb + i, lv[cb][i]);
           }
-        }
-        if (vec && vb + 8 <= a.V) {
-          if constexpr (sizeof(T) == 2) {
-            uint4 w;
-            w.x = f32_to_bf16(lv[0]) | (uint32_t(f32_to_bf16(lv[1])) << 16);
-            w.y = f32_to_bf16(lv[2]) | (uint32_t(f32_to_bf16(lv[3])) << 16);
-            w.z = f32_to_bf16(lv[4]) | (uint32_t(f32_to_bf16(lv[5])) << 16);
-            w.w = f32_to_bf16(lv[6]) | (uint32_t(f32_to_bf16(lv[7])) << 16);
-            *reinterpret_cast<uint4*>(O + base + vb) = w;
-          } else {
-            *reinterpret_cast<float4*>(O + base + vb) = make_float4(lv[0], lv[1], lv[2], lv[3]);
-            *reinterpret_cast<float4*>(O + base + vb + 4) = make_float4(lv[4], lv[5], lv[6], lv[7]);
-          }
-        } else {
-#pragma unroll
-          for (int j = 0; j < 8; ++j)
-            if (vb + j < a.V) Out<T>::store(O, base + vb + j, lv[j]);
         }
       }
-      // tile statistics of the row: max over 16 lanes, then the float64 mass below it
-#pragma unroll
-      for (int o = 8; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+      // the wave's 32 tokens of this request sit in the 4 lanes c16, c16+16, +32, +48
+      m = fmaxf(m, __shfl_xor(m, 16));
+      m = fmaxf(m, __shfl_xor(m, 32));
       double sum = 0.0;
-      if (rl < nb) {
+      if (m != -INFINITY) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-          if (vb + j < a.V) sum += exp(double(lv[j]) - double(m));
-      }
+        for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-      for (int o = 8; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
-      if (c8 == 0 && rl < nb) {
-        tmax[size_t(b) * l.ntiles + blockIdx.x] = m;
-        tsum[size_t(b) * l.ntiles + blockIdx.x] = sum;
+          for (int i = 0; i < 4; ++i)
+            if (lv[cb][i] != -INFINITY) sum += exp2_tab(P, tab, (double(lv[cb][i]) - double(m)) * kLog2eF64);
       }
+      sum += __shfl_xor(sum, 16);
+      sum += __shfl_xor(sum, 32);
+      if (g == 0) {
+        wmax[wave][rl] = m;
+        wsum[wave][rl] = sum;
+      }
+    }
+    __syncthreads();
+    // tile summary per request: the four waves' (max, mass) merged in wave order
+    if (tid < nb) {
+      float M = wmax[0][tid];
+      for (int w = 1; w < kW; ++w) M = fmaxf(M, wmax[w][tid]);
+      double S = 0.0;
+      for (int w = 0; w < kW; ++w)
+        if (wmax[w][tid] != -INFINITY) S += wsum[w][tid] * exp2_tab(P, tab, (double(wmax[w][tid]) - double(M)) * kLog2eF64);
+      tmax[size_t(b0 + tid) * l.ntiles + blockIdx.x] = M;
+      tsum[size_t(b0 + tid) * l.ntiles + blockIdx.x] = S;
     }
   }
 }
 
 template <typename T>
-__global__ __launch_bounds__(kSampleThreads) void markov_sample_kernel(MarkovArgs a, MkLayout l, int k) {
+__global__ __launch_bounds__(kSampleThreads) void markov_sample_kernel(MarkovArgs a, MkLayout l, int k,
+                                                                       Exp2Poly P) {
+  __shared__ double tab[256];
   __shared__ double sc[kSampleThreads / kWave];
   __shared__ float smax[kSampleThreads / kWave];
   __shared__ int s_tile;
   __shared__ double s_before, s_S;
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  tab[tid] = exp2_f64(P, double(tid) / 256.0);  // read after the barriers below
+  auto ex = [&](float x, float m) { return exp2_tab(P, tab, (double(x) - double(m)) * kLog2eF64); };
   const float* tmax = reinterpret_cast<const float*>(static_cast<const char*>(a.ws) + l.off_max) + size_t(b) * l.ntiles;
   const double* tsum = reinterpret_cast<const double*>(static_cast<const char*>(a.ws) + l.off_sum) + size_t(b) * l.ntiles;
   const int nt = l.ntiles, per = (nt + kSampleThreads - 1) / kSampleThreads;
@@ -246,7 +281,7 @@ __global__ __launch_bounds__(kSampleThreads) void markov_sample_kernel(MarkovArg
   // owns [off + excl_i, off + inc_i); the next thread's lower end is the same expression,
   // so the runs tile [0, S) without gaps or overlaps.
   double part = 0.0;
-  for (int t = t0; t < t1; ++t) part += tsum[t] * exp(double(tmax[t]) - double(M));
+  for (int t = t0; t < t1; ++t) part += tsum[t] * ex(tmax[t], M);
   double inc = part;
 #pragma unroll
   for (int o = 1; o < kWave; o <<= 1) {
@@ -273,7 +308,7 @@ __global__ __launch_bounds__(kSampleThreads) void markov_sample_kernel(MarkovArg
     double c = before;
     int t = t0;
     for (; t < t1 - 1; ++t) {
-      const double mt = tsum[t] * exp(double(tmax[t]) - double(M));
+      const double mt = tsum[t] * ex(tmax[t], M);
       if (target < c + mt) break;
       c += mt;
     }
@@ -287,14 +322,14 @@ __global__ __launch_bounds__(kSampleThreads) void markov_sample_kernel(MarkovArg
   const T* O = static_cast<const T*>(a.out);
   const size_t base = (size_t(b) * a.G1 + k) * a.V;
   const int v = t * kTileV + 2 * lane;
-  const double e0 = v < a.V ? exp(double(Out<T>::load(O, base + v)) - double(M)) : 0.0;
-  const double e1 = v + 1 < a.V ? exp(double(Out<T>::load(O, base + v + 1)) - double(M)) : 0.0;
+  const double e0 = v < a.V ? ex(Out<T>::load(O, base + v), M) : 0.0;
+  const double e1 = v + 1 < a.V ? ex(Out<T>::load(O, base + v + 1), M) : 0.0;
   double c0;
   if (s_before >= 0.0) {
     c0 = s_before;
   } else {
     // the last tile after a rounding overshoot: its start is S minus its own mass
-    c0 = S - tsum[t] * exp(double(tmax[t]) - double(M));
+    c0 = S - tsum[t] * ex(tmax[t], M);
   }
   double pinc = e0 + e1;
 #pragma unroll
@@ -317,7 +352,7 @@ __global__ __launch_bounds__(kSampleThreads) void markov_sample_kernel(MarkovArg
   }
   if (lane == 0) {
     a.tokens[size_t(b) * a.G1 + k] = cand;
-    if (a.p_at) a.p_at[size_t(b) * a.G1 + k] = float(exp(double(Out<T>::load(O, base + cand)) - double(M)) / s_S);
+    if (a.p_at) a.p_at[size_t(b) * a.G1 + k] = float(ex(Out<T>::load(O, base + cand), M) / s_S);
   }
 }
 
@@ -325,8 +360,14 @@ template <typename T, int R>
 hipError_t launch_markov_typed(const MarkovArgs& a, hipStream_t stream) {
   const MkLayout l = mk_layout(a.B, a.V);
   for (int k = 0; k < a.G1; ++k) {
-    hipLaunchKernelGGL((markov_logits_kernel<T, R>), dim3(l.ntiles), dim3(kMkThreads), 0, stream, a, l, k);
-    hipLaunchKernelGGL((markov_sample_kernel<T>), dim3(a.B), dim3(kSampleThreads), 0, stream, a, l, k);
+    if (a.vec_ok)
+      hipLaunchKernelGGL((markov_logits_kernel<T, R, true>), dim3(l.ntiles), dim3(kMkThreads), 0, stream, a,
+                         l, k, kExp2Taylor);
+    else
+      hipLaunchKernelGGL((markov_logits_kernel<T, R, false>), dim3(l.ntiles), dim3(kMkThreads), 0, stream, a,
+                         l, k, kExp2Taylor);
+    hipLaunchKernelGGL((markov_sample_kernel<T>), dim3(a.B), dim3(kSampleThreads), 0, stream, a, l, k,
+                       kExp2Taylor);
   }
   return hipGetLastError();
 }

@@ -412,7 +412,7 @@ rva_status rva_markov_sample(int B, int G1, int V, int r, int logit_dtype, const
   a.p_at = p_at;
   a.status = device_status;
   a.ws = workspace;
-  a.vec_ok = V % 8 == 0 && aligned(base_logits, 16) && aligned(draft_logits, 16);
+  a.vec_ok = V % 8 == 0 && aligned(base_logits, 16) && aligned(draft_logits, 16) && aligned(w2_scale, 16);
   return hip_result(rva::launch_markov(a, logit_dtype, stream), "rva_markov_sample launch");
 }
 

@@ -158,7 +158,7 @@ struct MarkovArgs {
   float* p_at;             // [B, G1] or NULL
   int32_t* status;
   void* ws;
-  bool vec_ok;             // V a multiple of 8 and base / out 16-byte aligned
+  bool vec_ok;             // V a multiple of 8 and base / out / s2 16-byte aligned
 };
 size_t markov_workspace_bytes(int B, int V);
 hipError_t launch_markov(const MarkovArgs& a, int dtype, hipStream_t stream);
