@@ -350,7 +350,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the verify path is sharded by request across GPUs by the caller, see DESIGN.md)",
+              "(the verify path shards by request: each GPU runs its own batch with this library)",
               file=sys.stderr)
         sys.exit(2)
 
