@@ -112,20 +112,48 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(
     }
   }
   if (!src) return;
+  const bool vec16 = (row_bytes % 16 == 0) && ((reinterpret_cast<uintptr_t>(src) |
+                                                reinterpret_cast<uintptr_t>(dst)) % 16 == 0);
+  // source row of each of this block's rows (nullptr: a pad row, zero-filled)
+  const uint8_t* srow[kRowsPerBlock];
+  int nrows = 0;
+#pragma unroll
   for (int rr = 0; rr < kRowsPerBlock; ++rr) {
     const int r = blockIdx.x * kRowsPerBlock + rr;
-    if (r >= max_rows || r >= tier) break;
-    const int b = r < M ? owner(r) : -1;
-    const int i = b >= 0 ? r - cu[b] : 0;
-    uint8_t* d = dst + size_t(r) * row_bytes;
-    const uint8_t* s = b >= 0 ? src + (size_t(b) * gamma + i) * row_bytes : nullptr;
-    const bool vec16 = (row_bytes % 16 == 0) && ((reinterpret_cast<uintptr_t>(src) |
-                                                  reinterpret_cast<uintptr_t>(dst)) % 16 == 0);
-    if (vec16) {
-      const size_t n = row_bytes / 16;
-      for (size_t k = tid; k < n; k += kPackThreads)
-        reinterpret_cast<uint4*>(d)[k] = s ? reinterpret_cast<const uint4*>(s)[k] : make_uint4(0, 0, 0, 0);
-    } else {
+    srow[rr] = nullptr;
+    if (r < max_rows && r < tier) {
+      nrows = rr + 1;
+      const int b = r < M ? owner(r) : -1;
+      if (b >= 0) srow[rr] = src + (size_t(b) * gamma + (r - cu[b])) * row_bytes;
+    }
+  }
+  uint8_t* drow0 = dst + size_t(blockIdx.x) * kRowsPerBlock * row_bytes;
+  if (vec16) {
+    // rows of up to 8 KB: a pass loads 2 vectors of every row before storing any, so the
+    // block's copy costs about one round trip per pass
+    const size_t n = row_bytes / 16;
+    for (size_t k0 = 0; k0 < n; k0 += 2 * kPackThreads) {
+      uint4 v[kRowsPerBlock][2];
+#pragma unroll
+      for (int rr = 0; rr < kRowsPerBlock; ++rr)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const size_t k = k0 + h * kPackThreads + tid;
+          v[rr][h] = (rr < nrows && srow[rr] && k < n) ? reinterpret_cast<const uint4*>(srow[rr])[k]
+                                                      : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+      for (int rr = 0; rr < kRowsPerBlock; ++rr)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const size_t k = k0 + h * kPackThreads + tid;
+          if (rr < nrows && k < n) reinterpret_cast<uint4*>(drow0 + size_t(rr) * row_bytes)[k] = v[rr][h];
+        }
+    }
+  } else {
+    for (int rr = 0; rr < nrows; ++rr) {
+      uint8_t* d = drow0 + size_t(rr) * row_bytes;
+      const uint8_t* s = srow[rr];
       for (size_t k = tid; k < row_bytes; k += kPackThreads) d[k] = s ? s[k] : uint8_t(0);
     }
   }
