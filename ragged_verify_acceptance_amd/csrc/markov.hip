@@ -43,7 +43,7 @@ constexpr int kSampleThreads = 256;
 typedef int v4i __attribute__((ext_vector_type(4)));
 
 struct MkLayout {
-  size_t off_max, off_sum, total;
+  size_t off_max, off_sum, off_e, off_s1, total;
   int ntiles;
 };
 
@@ -53,7 +53,9 @@ MkLayout mk_layout(int B, int V) {
   auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
   l.off_max = 0;
   l.off_sum = up(size_t(B) * l.ntiles * sizeof(float));
-  l.total = l.off_sum + up(size_t(B) * l.ntiles * sizeof(double));
+  l.off_e = l.off_sum + up(size_t(B) * l.ntiles * sizeof(double));  // q1 row of x_b, [B][256]
+  l.off_s1 = l.off_e + up(size_t(B) * 256);                          // s1[x_b], [B]
+  l.total = l.off_s1 + up(size_t(B) * sizeof(float));
   return l;
 }
 
@@ -81,9 +83,27 @@ __device__ __forceinline__ int prev_token(const MarkovArgs& a, int b, int k) {
 // VEC: V is a multiple of 8 and U / out are 16-byte aligned, so a lane's 4 tokens are one
 // aligned vector access; its loads are then issued unconditionally from clamped addresses
 // (no branch between issue and use, so the compiler keeps them in flight together).
+// The rows the next logits pass multiplies by: q1[x] and s1[x] of request b's previous
+// token, copied to the workspace by one wave (R bytes), so the pass itself loads them
+// without a dependent lookup.
+template <int R>
+__device__ __forceinline__ void stage_row(const MarkovArgs& a, const MkLayout& l, int b, int x, int lane) {
+  int8_t* e = static_cast<int8_t*>(a.ws) + l.off_e + size_t(b) * R;
+  if (lane < R / 16) *reinterpret_cast<uint4*>(e + lane * 16) = *reinterpret_cast<const uint4*>(a.w1 + size_t(x) * R + lane * 16);
+  if (lane == 0) reinterpret_cast<float*>(static_cast<char*>(a.ws) + l.off_s1)[b] = a.s1[x];
+}
+
+// Stages the anchors' rows for the first position: one wave per request.
+template <int R>
+__global__ __launch_bounds__(256) void markov_stage_kernel(MarkovArgs a, MkLayout l) {
+  const int b = blockIdx.x * 4 + threadIdx.x / kWave;
+  if (b >= a.B) return;
+  stage_row<R>(a, l, b, prev_token(a, b, 0), threadIdx.x % kWave);
+}
+
 template <typename T, int R, bool VEC>
-__global__ __launch_bounds__(kMkThreads) void markov_logits_kernel(MarkovArgs a, MkLayout l, int k,
-                                                                    Exp2Poly P) {
+__global__ __launch_bounds__(kMkThreads, VEC ? 4 : 1) void markov_logits_kernel(MarkovArgs a, MkLayout l, int k,
+                                                                                  Exp2Poly P) {
   constexpr int kQ = R / 4;            // bytes of r per lane group
   constexpr int kSteps = kQ / 8;       // MFMA k-steps (8 bytes per lane each)
   constexpr int kEPitch = R + 8;       // LDS row pitch of the gathered embeddings (8-aligned)
@@ -134,8 +154,10 @@ __global__ __launch_bounds__(kMkThreads) void markov_logits_kernel(MarkovArgs a,
   // v0 + 16 (2 wave + cb) + 4 g + i (the MFMA result layout: lane column c16, rows 4g + i)
   for (int b0 = 0; b0 < a.B; b0 += kReqGroup) {
     const int nb = min(kReqGroup, a.B - b0);
-    // the epilogue's base logits, requested before the gather and the MFMA
-    float uv[4][2][4];
+    // the epilogue's base logits, requested before the MFMA and kept in their storage
+    // format (bf16 pairs stay packed: half the registers)
+    constexpr int kU = sizeof(T) == 2 ? 2 : 4;
+    uint32_t uv[4][2][kU];
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
@@ -146,35 +168,39 @@ __global__ __launch_bounds__(kMkThreads) void markov_logits_kernel(MarkovArgs a,
           const size_t base = (size_t(b0 + min(rl, nb - 1)) * a.G1 + k) * a.V + min(vb, a.V - 4);
           if constexpr (sizeof(T) == 2) {
             const uint2 w = *reinterpret_cast<const uint2*>(U + base);
-            uv[rb][cb][0] = bf16_to_f32(uint16_t(w.x & 0xffff));
-            uv[rb][cb][1] = bf16_to_f32(uint16_t(w.x >> 16));
-            uv[rb][cb][2] = bf16_to_f32(uint16_t(w.y & 0xffff));
-            uv[rb][cb][3] = bf16_to_f32(uint16_t(w.y >> 16));
+            uv[rb][cb][0] = w.x;
+            uv[rb][cb][1] = w.y;
           } else {
-            const float4 w = *reinterpret_cast<const float4*>(U + base);
+            const uint4 w = *reinterpret_cast<const uint4*>(U + base);
             uv[rb][cb][0] = w.x; uv[rb][cb][1] = w.y; uv[rb][cb][2] = w.z; uv[rb][cb][3] = w.w;
           }
         } else {
           const size_t base = (size_t(b0 + rl) * a.G1 + k) * a.V;
+          float x[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            uv[rb][cb][i] = (rl < nb && vb + i < a.V) ? Out<T>::load(U, base + vb + i) : 0.f;
+          for (int i = 0; i < 4; ++i) x[i] = (rl < nb && vb + i < a.V) ? Out<T>::load(U, base + vb + i) : 0.f;
+          if constexpr (sizeof(T) == 2) {
+            uv[rb][cb][0] = uint32_t(f32_to_bf16(x[0])) | (uint32_t(f32_to_bf16(x[1])) << 16);
+            uv[rb][cb][1] = uint32_t(f32_to_bf16(x[2])) | (uint32_t(f32_to_bf16(x[3])) << 16);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) uv[rb][cb][i] = __float_as_uint(x[i]);
+          }
         }
       }
     __syncthreads();  // the previous group's LDS is no longer read
-    // gather q1[x_b] rows (16 bytes per thread per step) and the scales
+    // the staged q1[x_b] rows (16 bytes per thread per step) and scales; no lookup chain
+    const int8_t* estage = static_cast<const int8_t*>(a.ws) + l.off_e;
+    const float* s1stage = reinterpret_cast<const float*>(static_cast<const char*>(a.ws) + l.off_s1);
     for (int it = tid; it < kReqGroup * (R / 16); it += kMkThreads) {
       const int rl = it / (R / 16), c = it % (R / 16);
-      uint4 w = make_uint4(0, 0, 0, 0);
-      if (rl < nb) {
-        const int x = prev_token(a, b0 + rl, k);
-        w = *reinterpret_cast<const uint4*>(a.w1 + size_t(x) * R + c * 16);
-        if (c == 0) sS1[rl] = a.s1[x];
-      }
+      uint4 w = *reinterpret_cast<const uint4*>(estage + size_t(b0 + min(rl, nb - 1)) * R + c * 16);
+      if (rl >= nb) w = make_uint4(0, 0, 0, 0);
       uint2* dst = reinterpret_cast<uint2*>(sE + rl * kEPitch + c * 16);
       dst[0] = make_uint2(w.x, w.y);
       dst[1] = make_uint2(w.z, w.w);
     }
+    if (tid < kReqGroup) sS1[tid] = s1stage[b0 + min(tid, nb - 1)];
     __syncthreads();
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
@@ -201,7 +227,10 @@ __global__ __launch_bounds__(kMkThreads) void markov_logits_kernel(MarkovArgs a,
           lv[cb][i] = -INFINITY;
           if (rl < nb && v < a.V) {
             const double t = s1 * double(s2v[cb][i]);  // exact: a product of two float32
-            const double lg = __dadd_rn(double(uv[rb][cb][i]), __dmul_rn(t, double(acc[cb][i])));
+            const float uf = sizeof(T) == 2 ? bf16_to_f32(uint16_t(i & 1 ? uv[rb][cb][i >> 1] >> 16
+                                                                            : uv[rb][cb][i >> 1] & 0xffff))
+                                            : __uint_as_float(uv[rb][cb][i % kU]);
+            const double lg = __dadd_rn(double(uf), __dmul_rn(t, double(acc[cb][i])));
             lv[cb][i] = Out<T>::round(lg);
             m = fmaxf(m, lv[cb][i]);
           }
@@ -354,11 +383,17 @@ __global__ __launch_bounds__(kSampleThreads) void markov_sample_kernel(MarkovArg
     a.tokens[size_t(b) * a.G1 + k] = cand;
     if (a.p_at) a.p_at[size_t(b) * a.G1 + k] = float(ex(Out<T>::load(O, base + cand), M) / s_S);
   }
+  if (k + 1 < a.G1) {
+    if (a.r == 256) stage_row<256>(a, l, b, cand, lane);
+    else if (a.r == 128) stage_row<128>(a, l, b, cand, lane);
+    else stage_row<64>(a, l, b, cand, lane);
+  }
 }
 
 template <typename T, int R>
 hipError_t launch_markov_typed(const MarkovArgs& a, hipStream_t stream) {
   const MkLayout l = mk_layout(a.B, a.V);
+  hipLaunchKernelGGL(markov_stage_kernel<R>, dim3((a.B + 3) / 4), dim3(256), 0, stream, a, l);
   for (int k = 0; k < a.G1; ++k) {
     if (a.vec_ok)
       hipLaunchKernelGGL((markov_logits_kernel<T, R, true>), dim3(l.ntiles), dim3(kMkThreads), 0, stream, a,
