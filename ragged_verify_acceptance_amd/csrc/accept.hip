@@ -18,10 +18,11 @@
 //                   residual draw) of e_t = exp(x_t - M_t), e_d = exp(x_d - M_d), and of the
 //                   unnormalised residual max(0, e_t - rho' e_d) with the draft entries it
 //                   keeps, at rho' = S_t / S_d from the float32-accurate stats; per segment
-//                   and per 512-entry sub-segment.  Pair slots: the segment's share of the TV
-//                   distance sum max(0, p_t - p_d) (float32 terms, float64 sum) of every
-//                   other draft pair.
-//   pick_kernel     one workgroup per request: labels = 1 - TV; the exact ratio
+//                   and per 512-entry sub-segment.  Pair slots: the segment's share of the
+//                   overlap sum min(p_t, p_d) = 1 - TV of every other draft pair, as
+//                   2^min(l_t, l_d) with l = (x - M) log2 e - log2 S (one float32
+//                   exponential per entry pair, float64 sum).
+//   pick_kernel     one workgroup per request: labels = the summed overlaps; the exact ratio
 //                   rho = S_t / S_d from the float64 sums corrects each residual mass to
 //                   first order, A(rho) = A(rho') - (rho - rho') D (exact up to the entries
 //                   whose sign differs between rho' and rho, a second-order term); u * Q
@@ -104,7 +105,7 @@ struct Ctx {
   float* st_m;    // [n_ids][nseg] segment maxima
   double* st_s;   // [n_ids][nseg] segment sums of exp(x - m_s)
   float2* nm;     // [n_ids] (row max, 1 / row sum) of the rows decide_kernel covered
-  double* tv;     // [B*G1][nseg] TV shares
+  double* tv;     // [B*G1][nseg] segment shares of the overlap sum min(p_t, p_d) = 1 - TV
   Decision* dec;  // [B]
   double* r1;     // [B][nseg][kDrawSums] float64 sums of the draw slots
   double* sub;    // [B][nseg][kSub][kSubSums] the same per sub-segment
@@ -439,7 +440,7 @@ __global__ __launch_bounds__(kWideThreads) void pair_kernel(Ctx c, int draw_slot
     const Decision d = c.dec[b];
     if (d.n < 0) return;
     const bool residual = d.id_d >= 0;
-    const bool lab = per_pair && residual;  // this pair's TV share is taken here too
+    const bool lab = per_pair && residual;  // this pair's overlap share is taken here too
     SegData<T, kWideThreads> xt, xd;
     xt.load(row_ptr<T>(c, d.id_t), c.a.V, seg);
     double v[kDrawSums + 1] = {0.0, 0.0, 0.0, 0.0, 0.0};
@@ -468,8 +469,7 @@ __global__ __launch_bounds__(kWideThreads) void pair_kernel(Ctx c, int draw_slot
             gs[1] += r;
             gs[2] += ed;
           }
-          const double q = et * it - ed * id;
-          v[4] += q > 0.0 ? q : 0.0;
+          v[4] += fmin(et * it, ed * id);  // overlap min(p_t, p_d)
         }
       }
       v[0] += gs[0];
@@ -504,15 +504,18 @@ __global__ __launch_bounds__(kWideThreads) void pair_kernel(Ctx c, int draw_slot
   xt.load(row_ptr<T>(c, id_t), c.a.V, seg);
   xd.load(row_ptr<T>(c, id_d), c.a.V, seg);
   const float2 nt = c.nm[id_t], nd = c.nm[id_d];
+  // min(p_t, p_d) = 2^min(lt, ld) with l = (x - M) log2 e - log2 S: one exponential per
+  // entry pair (the label is the segment sums of these overlaps)
+  const float lst = __log2f(nt.y), lsd = __log2f(nd.y);  // = -log2 S
   double acc = 0.0;
 #pragma unroll
   for (int i = 0; i < kWidePer; i += 8) {
     float run = 0.f;
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const float pt = exp_shift(xt[i + u], nt.x) * nt.y;
-      const float pd = exp_shift(xd[i + u], nd.x) * nd.y;
-      run += fmaxf(pt - pd, 0.f);
+      const float lt = fmaf(xt[i + u] - nt.x, kLog2e, lst);
+      const float ld = fmaf(xd[i + u] - nd.x, kLog2e, lsd);
+      run += __builtin_amdgcn_exp2f(fminf(lt, ld));
     }
     acc += double(run);
   }
@@ -575,14 +578,15 @@ __global__ __launch_bounds__(kPickThreads) void pick_kernel(Ctx c, int commit) {
   const int nseg = c.L.nseg;
   if (!req_ok(c, b)) return;
   const int w = c.a.cu[b + 1] - c.a.cu[b];
-  if (c.a.labels) {  // one wave per draft: lanes sum the segment shares of the TV distance
+  if (c.a.labels) {  // one wave per draft: lanes sum the segment shares of the overlap
     for (int k = wave; k < G1; k += kPickThreads / kWave) {
       const size_t o = size_t(b) * G1 + k;
-      double tv = 0.0;
+      double ov = 0.0;
       if (k < w - 1)
-        for (int s = lane; s < nseg; s += kWave) tv += c.tv[o * nseg + s];
-      tv = wave_sum_f64(tv);
-      if (lane == 0) c.a.labels[o] = k < w - 1 ? float(1.0 - tv) : __int_as_float(0x7fc00000);
+        for (int s = lane; s < nseg; s += kWave) ov += c.tv[o * nseg + s];
+      ov = wave_sum_f64(ov);
+      // c* = 1 - TV = sum_v min(p_d, p_t)
+      if (lane == 0) c.a.labels[o] = k < w - 1 ? float(ov) : __int_as_float(0x7fc00000);
     }
   }
   if (!commit) return;
