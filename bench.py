@@ -350,8 +350,11 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="time each step as one replay of the captured step graph")
     ap.add_argument("--cpu-sample", type=int, default=64, help="requests in the oracle sample (0: skip)")
+    ap.add_argument("--flush-mall", action="store_true",
+                    help="touch 1 GiB before every timed step (working sets under the 256 MB "
+                         "Infinity Cache); each step is then timed alone and the median reported")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="run one 1 GiB device-to-device copy first (counter calibration)")
+                    help="accepted for older profiling commands: the 1 GiB copy always runs")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
@@ -392,14 +395,23 @@ def main():
     M, tier = (int(x) for x in ds.total_tier.cpu().numpy())
     attn_b, acc_b, attn_flops = algorithmic_bytes(wl, inp.context_lens, windows)
 
-    if args.copy_calibration:
-        x = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-        y = torch.empty_like(x)
-        y.copy_(x)
-        torch.cuda.synchronize()
-        del x, y
-
     stream = torch.cuda.current_stream()
+    # a plain 1 GiB device-to-device copy on this GPU, for scale (and the counter calibration)
+    x = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(x)
+    y.copy_(x)
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(3):
+        y.copy_(x)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 3 * 2 * (1 << 30) / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    flush = x if args.flush_mall else None
+    del y
+    if flush is None:
+        del x
 
     graph = None
     if args.graph:
@@ -426,14 +438,28 @@ def main():
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    e0.record(stream)
-    t_host = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    t_host = time.perf_counter() - t_host
-    ms_step = e0.elapsed_time(e1) / args.steps
+    if flush is None:
+        e0.record(stream)
+        t_host = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t_host = time.perf_counter() - t_host
+        ms_step = e0.elapsed_time(e1) / args.steps
+    else:
+        # the cache is flushed before each step, outside its own event pair
+        per = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        t_host = time.perf_counter()
+        for a0, a1 in per:
+            flush.add_(1)
+            a0.record(stream)
+            step()
+            a1.record(stream)
+        torch.cuda.synchronize()
+        t_host = time.perf_counter() - t_host
+        ms_step = float(np.median([a0.elapsed_time(a1) for a0, a1 in per]))
 
     # ---- per-stage durations inside whole steps (HIP events on the launch stream)
     n_ev = max(10, args.steps // 2)
@@ -494,6 +520,9 @@ def main():
                      "algorithmic_bytes": attn_b},
         "device_status": status,
         "committed_tokens_per_step": int(ds.accept_len.sum().item()) + inp.B,
+        "goodput_committed_tokens_per_s": (int(ds.accept_len.sum().item()) + inp.B) / (ms_step * 1e-3),
+        "copy_1GiB_GBps": copy_gbs,
+        "flush_mall": bool(args.flush_mall),
         "host_wall_s": t_host,
     }
     if capped:
