@@ -3,7 +3,10 @@
 A step is one pass of the whole path over one batch: rva_schedule_windows ->
 rva_pack_ragged -> rva_verify_attention -> rva_accept_and_commit (with the TV labels
 fused), on the mixed-traffic workload (B = 64, gamma = 8, GQA 32/8 D = 128 bf16 paged KV,
-contexts U[512, 8K], V = 151936 bf16 logits), compact mode.  Inputs are resident in HBM
+contexts U[512, 8K], V = 151936 bf16 logits), compact mode.  With --overlap-schedule the
+scheduling call of each step is for the next step and runs on a second stream beside the
+acceptance kernels (zero-overhead scheduling, as the SGLang integration runs it), and the
+serial step is reported beside it.  Inputs are resident in HBM
 before the timed region; between steps context_lens is restored (a 256-byte device copy,
 inside the timed region) so every step redoes the same work.
 
@@ -347,6 +350,9 @@ def main():
                          "cost-table: measure T(bs, M) by graph replay and fit the scheduler's tables")
     ap.add_argument("--trace-steps", type=int, default=200,
                     help="sts mode: verify steps (of B requests) in the acceptance trace")
+    ap.add_argument("--overlap-schedule", action="store_true",
+                    help="run each step's scheduling call for the next step on a second stream, "
+                         "beside the acceptance kernels (the serial step is reported beside it)")
     ap.add_argument("--graph", action="store_true",
                     help="time each step as one replay of the captured step graph")
     ap.add_argument("--cpu-sample", type=int, default=64, help="requests in the oracle sample (0: skip)")
@@ -421,14 +427,25 @@ def main():
         ds.restore()
         graph = CallGraph(ds.step)
 
+    overlap = args.overlap_schedule and not (capped or graph is not None)
+    side = torch.cuda.Stream() if overlap else None  # default priority
+    ev_attn = torch.cuda.Event() if overlap else None
+    ev_sched = torch.cuda.Event() if overlap else None
+
     def step():
         ds.restore()
         if capped:
             ds.step_capped()
         elif graph is not None:
             graph.replay()
+        elif overlap:
+            ds.step_overlapped(side, ev_attn, ev_sched)
         else:
             ds.step()
+
+    def serial_step():
+        ds.restore()
+        ds.step()
 
     for _ in range(args.warmup):
         step()
@@ -460,6 +477,20 @@ def main():
         torch.cuda.synchronize()
         t_host = time.perf_counter() - t_host
         ms_step = float(np.median([a0.elapsed_time(a1) for a0, a1 in per]))
+
+    # the same number of steps with the scheduling call in line, for comparison
+    ms_serial = None
+    if overlap:
+        for _ in range(3):
+            serial_step()
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s0.record(stream)
+        for _ in range(args.steps):
+            serial_step()
+        s1.record(stream)
+        torch.cuda.synchronize()
+        ms_serial = s0.elapsed_time(s1) / args.steps
 
     # ---- per-stage durations inside whole steps (HIP events on the launch stream)
     n_ev = max(10, args.steps // 2)
@@ -505,7 +536,9 @@ def main():
         "config": {"workload": wl.name, "mode": args.mode, "B": wl.B, "gamma": wl.gamma,
                    "Hq": wl.Hq, "Hkv": wl.Hkv, "D": wl.D, "page": wl.page, "V": wl.V,
                    "packed_rows_M": M, "tier": tier, "mean_window": float(windows.mean()),
-                   "mean_context": float(inp.context_lens.mean()), "graph": bool(args.graph)},
+                   "mean_context": float(inp.context_lens.mean()), "graph": bool(args.graph),
+                   "schedule_overlapped": overlap},
+        "ms_per_step_serial_schedule": ms_serial,
         "verify_attn_accept": {
             "achieved_GBps": path_gbs, "pct_peak": 100.0 * path_gbs / PEAK_HBM_GBS,
             "tokens_per_s": M / ((t_attn + t_acc) * 1e-3),

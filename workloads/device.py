@@ -54,6 +54,7 @@ class DeviceStep:
         self.conf_out = torch.empty((B, G1), **f32)
         self.surv_out = torch.empty((B, G1), **f32)
         self.windows = torch.empty(B, **i32)
+        self.windows_next = torch.empty(B, **i32)  # written by the overlapped scheduler
         self.K_out = torch.empty(1, **i32)
         self.ratio_out = torch.empty(1, dtype=torch.float64, device=dev)
         self.status = torch.zeros(1, **i32)
@@ -109,11 +110,12 @@ class DeviceStep:
                                   dtype=torch.uint8, device=dev)
 
     # ------------------------------------------------------------------ calls
-    def schedule(self):
+    def schedule(self, windows=None):
         wl = self.wl
         rva.schedule_windows(self.B, wl.gamma, self.mode, self.hidden, wl.head_H, self.head_w,
                              self.head_b, self.conf_in, None, self.bias, self.alpha, self.theta,
-                             self.conf_out, self.surv_out, self.windows, self.K_out,
+                             self.conf_out, self.surv_out,
+                             self.windows if windows is None else windows, self.K_out,
                              self.ratio_out, self.status)
 
     def pack(self, src=None, dst=None):
@@ -181,6 +183,26 @@ class DeviceStep:
         self.pack()
         self.attention()
         self.accept_capped(None, labels=labels)
+
+    def step_overlapped(self, side, ev_attn, ev_sched, labels=True):
+        """One step with the scheduling call off the critical path, as the SGLang integration
+        runs it (the devpress.csdn.net article on DSpark in SGLang, section 4: the next
+        step's scheduling overlaps the current forward on a separate stream; the confidences
+        it reads are from an earlier step).  Pack, attention and acceptance use the windows
+        scheduled during the previous step; the scheduling call for the next step runs on
+        `side` once attention is done, beside the acceptance kernels.  Both buffers of
+        windows alternate, so no call reads a buffer another stream is writing."""
+        main = torch.cuda.current_stream()
+        self.pack()
+        self.attention()
+        ev_attn.record(main)
+        side.wait_event(ev_attn)
+        with torch.cuda.stream(side):
+            self.schedule(windows=self.windows_next)
+            ev_sched.record(side)
+        self.accept(labels=labels)
+        main.wait_event(ev_sched)
+        self.windows, self.windows_next = self.windows_next, self.windows
 
     def step(self, labels=True):
         """One pass of the whole path: stages 1, 2, 3 and 4 (+5)."""
