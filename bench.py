@@ -71,6 +71,16 @@ def counter_traffic(workload):
     return float(fields["traffic_bytes_per_launch"])
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
 def cpu_baseline(inp, windows, n_req):
     """The oracle, single-threaded, on the first n_req requests of the same workload."""
     from threadpoolctl import threadpool_limits
@@ -118,7 +128,7 @@ def cpu_baseline(inp, windows, n_req):
             "sample": f"first {n_req} of {inp.B} requests of {wl.name} ({R} packed verify rows): "
                       f"full-batch scheduling + pack, then attention and acceptance+labels of the "
                       f"sample, float64 NumPy, 1 thread, {reps} pass(es) in {dt:.1f} s on "
-                      f"{platform.processor() or platform.machine()}"}
+                      f"{cpu_model()} ({len(os.sched_getaffinity(0))} cores visible)"}
 
 
 def cost_table(inp, reps, warm):
@@ -555,6 +565,9 @@ def main():
         "committed_tokens_per_step": int(ds.accept_len.sum().item()) + inp.B,
         "goodput_committed_tokens_per_s": (int(ds.accept_len.sum().item()) + inp.B) / (ms_step * 1e-3),
         "copy_1GiB_GBps": copy_gbs,
+        "device": {"name": torch.cuda.get_device_name(0),
+                   "arch": getattr(torch.cuda.get_device_properties(0), "gcnArchName", ""),
+                   "cus": torch.cuda.get_device_properties(0).multi_processor_count},
         "flush_mall": bool(args.flush_mall),
         "host_wall_s": t_host,
     }
