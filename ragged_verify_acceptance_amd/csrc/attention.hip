@@ -18,10 +18,11 @@
 //     workgroup; a segment cut by share boundaries leaves at most one partial per workgroup
 //     side and attn_merge_kernel combines them.  No workgroup ever waits for another.
 //   * Inside a workgroup the 4 waves take the segment's tiles round-robin, one wave per
-//     SIMD.  Each wave rotates three register buffers, so two tiles (32 KB) are in flight
-//     while it computes a third.  Page numbers for 64 tiles at a time are preloaded into
-//     lanes and read back with readlane; operand addresses are a uniform SGPR base per
-//     tile plus lane-constant 32-bit offsets (global loads, no 64-bit lane arithmetic).
+//     SIMD.  Each wave alternates two register buffers, so the next tile (16 KB at
+//     D = 128) is in flight while it computes the current one (NB = 4 keeps one buffer: its
+//     accumulators take the registers).  Page numbers are scalar loads from the block
+//     table; operand addresses are a uniform SGPR base per tile plus lane-constant 32-bit
+//     offsets (global loads, no 64-bit lane arithmetic).
 //   * Scores are computed transposed, S^T = K Q^T, with mfma_f32_16x16x32_bf16 (K rows are
 //     the A operand, 16-byte loads from the (page, head) block, a contiguous
 //     [page_size, D] tile in this cache layout).  Row m of 16-key block mb holds key
@@ -410,10 +411,11 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, SkShared<D, NBMAX
     }
     return pg;
   };
-  // register ring: with three buffers tiles k+1 and k+2 are in flight while tile k is
-  // computed (two buffers for NB = 4, whose accumulators take the registers).  Loads are
-  // issued unconditionally (past the end they repeat the last tile), so every path has the
-  // same number of loads outstanding and each wait is exact.
+  // register ring of kStages buffers: with two, tile k+1 is in flight while tile k is
+  // computed; NB = 4 reloads one buffer (its accumulators take the registers).  A three-buffer
+  // ring (kStages = 3, two tiles in flight) spills at D = 128.  kC / vC hold the tail tile.
+  // Loads are issued unconditionally (past the end they repeat the last tile), so every
+  // path has the same number of loads outstanding and each wait is exact.
   constexpr int kStages = NB >= 4 ? 1 : 2;  // NB = 4's accumulators leave room for one buffer
   short8 kA[2][DS], vA[DB], kB[2][DS], vB[DB], kC[2][DS], vC[DB];
   int pg_next = 0;
