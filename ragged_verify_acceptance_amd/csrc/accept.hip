@@ -48,6 +48,7 @@ constexpr int kSubLen = 512;                // sub-segment: what one wave covers
 constexpr int kSub = kSeg / kSubLen;         // sub-segments per segment
 constexpr int kPickThreads = kSubLen;        // the pick rescans one sub-segment, an entry a thread
 static_assert(kSubLen == 8 * kWave, "a wave's group of 8 entries per lane is one sub-segment");
+static_assert(kSub <= kWave, "the pick holds one sub-segment per lane");
 constexpr float kLog2e = 1.44269504088896341f;
 
 // e^(x - m) in float32 (x = -inf gives 0; m must be finite)
@@ -428,8 +429,11 @@ __device__ __forceinline__ void block_sums_f64(double (&v)[N], double (*sm)[N]) 
 
 // blockIdx.y < draw_slots: the draw slot of request blockIdx.y (float64-heavy, dispatched
 // first); above: draft pair (blockIdx.y - draw_slots) = b*G1 + k for the labels (when per_pair).
+// 8 waves per SIMD (64 VGPRs): four workgroups per CU, so that one computing still leaves
+// three streaming (the draw slots' float64 path spills a few registers to scratch).
 template <typename T>
-__global__ __launch_bounds__(kWideThreads) void pair_kernel(Ctx c, int draw_slots, int per_pair) {
+__global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) void pair_kernel(
+    Ctx c, int draw_slots, int per_pair) {
   __shared__ double sm[kWideThreads / kWave][kDrawSums + 1];
   __shared__ double smd[kWideThreads / kWave];
   const int seg = blockIdx.x;
@@ -504,17 +508,21 @@ __global__ __launch_bounds__(kWideThreads) void pair_kernel(Ctx c, int draw_slot
   xt.load(row_ptr<T>(c, id_t), c.a.V, seg);
   xd.load(row_ptr<T>(c, id_d), c.a.V, seg);
   const float2 nt = c.nm[id_t], nd = c.nm[id_d];
-  // min(p_t, p_d) = 2^min(lt, ld) with l = (x - M) log2 e - log2 S: one exponential per
-  // entry pair (the label is the segment sums of these overlaps)
-  const float lst = __log2f(nt.y), lsd = __log2f(nd.y);  // = -log2 S
+  // min(p_t, p_d) = 2^min(lt, ld) with l = (x - M) log2 e - log2 S = x log2 e + c,
+  // c = -(M log2 e + log2 S): one FMA per entry and one exponential per entry pair (the label
+  // is the segment sums of these overlaps).  Forming l from x log2 e instead of (x - M) log2 e
+  // moves it by a few float32 ulp of |x log2 e| (< 30 for logits of magnitude < 20), a
+  // relative change of about 1e-6 in each term.
+  const float ct = -fmaf(nt.x, kLog2e, -__log2f(nt.y));  // nm.y = 1 / S
+  const float cd = -fmaf(nd.x, kLog2e, -__log2f(nd.y));
   double acc = 0.0;
 #pragma unroll
   for (int i = 0; i < kWidePer; i += 8) {
     float run = 0.f;
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const float lt = fmaf(xt[i + u] - nt.x, kLog2e, lst);
-      const float ld = fmaf(xd[i + u] - nd.x, kLog2e, lsd);
+      const float lt = fmaf(xt[i + u], kLog2e, ct);
+      const float ld = fmaf(xd[i + u], kLog2e, cd);
       run += __builtin_amdgcn_exp2f(fminf(lt, ld));
     }
     acc += double(run);
@@ -576,10 +584,30 @@ __global__ __launch_bounds__(kPickThreads) void pick_kernel(Ctx c, int commit) {
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int G1 = c.a.gamma - 1;
   const int nseg = c.L.nseg;
+  // Every load that depends on no other goes out first, before the window check and the
+  // label stores (which may alias them as far as the compiler knows): the decision record,
+  // the drafted tokens, the context length and lane s's draw sums of segment s (when a wave
+  // covers every segment).
+  const bool lanes_cover = nseg <= kWave;
+  Decision d;
+  double r1v[kDrawSums] = {0.0, 0.0, 0.0, 0.0};
+  int tok = -1, ctx0 = 0;  // thread i < gamma: drafted token i; thread 0: the context length
+  if (commit) {
+    d = c.dec[b];
+    if (tid < G1) tok = c.a.tokens[size_t(b) * G1 + tid];
+    if (tid == 0) ctx0 = c.a.context_lens[b];
+    if (wave == 0 && lanes_cover && lane < nseg) {
+      const double* r = c.r1 + (size_t(b) * nseg + lane) * kDrawSums;
+#pragma unroll
+      for (int q = 0; q < kDrawSums; ++q) r1v[q] = r[q];
+    }
+  }
   if (!req_ok(c, b)) return;
   const int w = c.a.cu[b + 1] - c.a.cu[b];
-  if (c.a.labels) {  // one wave per draft: lanes sum the segment shares of the overlap
-    for (int k = wave; k < G1; k += kPickThreads / kWave) {
+  if (c.a.labels) {  // one wave per draft (wave 0 is left to the draw when there is one):
+                     // lanes sum the segment shares of the overlap
+    const int first = commit ? 1 : 0, stride = kPickThreads / kWave - first;
+    for (int k = wave - first; k >= 0 && k < G1; k += stride) {
       const size_t o = size_t(b) * G1 + k;
       double ov = 0.0;
       if (k < w - 1)
@@ -590,11 +618,49 @@ __global__ __launch_bounds__(kPickThreads) void pick_kernel(Ctx c, int commit) {
     }
   }
   if (!commit) return;
-  const Decision d = c.dec[b];
   if (d.n < 0) return;
   __shared__ double tab[256];
   fill_exp2_tab(c.P, tab);
-  if (wave == 0) {
+  if (wave == 0 && lanes_cover) {
+    // the general path below with every per-segment value held by its lane: the same sums
+    // in the same order, without re-reading the draw sums for each step
+    const double St = wave_sum_f64(r1v[0]), Sd = wave_sum_f64(r1v[1]);
+    bool residual = d.id_d >= 0;
+    const double rho = residual ? St / Sd : 0.0;
+    const double drho = rho - d.rho32;
+    auto lane_mass = [&](bool res) {
+      if (lane >= nseg) return 0.0;
+      if (!res) return r1v[0];
+      const double m = r1v[2] - drho * r1v[3];
+      return m > 0.0 ? m : 0.0;
+    };
+    double mass = lane_mass(residual);
+    double Q = wave_sum_f64(mass);
+    if (residual && !(Q > 0.0)) {  // residual identically zero: draw from p_t instead
+      residual = false;
+      Q = St;
+      mass = lane_mass(false);
+    }
+    const double t = double(c.a.u_res[b]) * Q;
+    int seg = -1;
+    double base = 0.0;
+    locate(t, 0.0, nseg, [&](int) { return mass; }, seg, base);
+    // lane u: sub-segment u of the chosen segment (kSub <= kWave)
+    double sm = 0.0;
+    if (lane < kSub) sm = sub_mass(c, b, seg, lane, residual, drho);
+    int sub = -1;
+    double base2 = base;
+    locate(t, base, kSub, [&](int) { return sm; }, sub, base2);
+    if (lane == 0) {
+      s_t = t;
+      s_base = base2;
+      s_pos = seg * kSeg + sub * kSubLen;
+      s_residual = residual;
+      s_rho = rho;
+      s_y = 0x7fffffff;
+      s_last = -1;
+    }
+  } else if (wave == 0) {
     double St, Sd;
     draw_totals(c, b, St, Sd);
     bool residual = d.id_d >= 0;
@@ -653,14 +719,14 @@ __global__ __launch_bounds__(kPickThreads) void pick_kernel(Ctx c, int commit) {
     atomicMax(&s_last, v);
   }
   __syncthreads();
+  // the commit, one thread per block position (rounding that left u * Q past this
+  // sub-segment's end takes its last positive entry)
+  const int y = s_y != 0x7fffffff ? s_y : (s_last >= 0 ? s_last : s_pos);
+  const int n = d.n;
+  if (tid < c.a.gamma) c.a.committed[size_t(b) * c.a.gamma + tid] = tid < n ? tok : (tid == n ? y : -1);
   if (tid == 0) {
-    // rounding left u * Q past this sub-segment's end: its last positive entry
-    const int y = s_y != 0x7fffffff ? s_y : (s_last >= 0 ? s_last : s_pos);
-    const int n = d.n;
-    int32_t* com = c.a.committed + size_t(b) * c.a.gamma;
-    for (int i = 0; i < c.a.gamma; ++i) com[i] = i < n ? c.a.tokens[size_t(b) * G1 + i] : (i == n ? y : -1);
     c.a.accept_len[b] = n;
-    c.a.context_lens[b] += n + 1;
+    c.a.context_lens[b] = ctx0 + n + 1;
   }
 }
 
