@@ -13,7 +13,7 @@
 //   decide_kernel   one workgroup per request: row normalisers (max M, sum S) of the
 //                   request's rows from the segment stats, p_t(x) and p_d(x) at the drafted
 //                   tokens in float64, accept bits, first rejection, which rows the draw uses.
-//   pair_kernel     grid (segment, slot).  Draw slots (one per request, dispatched first):
+//   pair_kernel_*   grid (segment, slot).  Draw slots (one per request, dispatched first):
 //                   float64 sums over the draw rows (target row n, and draft row n for a
 //                   residual draw) of e_t = exp(x_t - M_t), e_d = exp(x_d - M_d), and of the
 //                   unnormalised residual max(0, e_t - rho' e_d) with the draft entries it
@@ -33,6 +33,8 @@
 // draw reads is float64: exp is 2^y by range reduction, a 256-entry table of 2^(j/256) and a
 // degree-4 Taylor polynomial of 2^f on |f| <= 1/512 (about 1.5 ulp); the table itself and the
 // few other float64 exponentials use a degree-13 polynomial on |f| <= 1/2.
+#include <type_traits>
+
 #include "exp2_f64.h"
 #include "rva_common.h"
 
@@ -429,11 +431,8 @@ __device__ __forceinline__ void block_sums_f64(double (&v)[N], double (*sm)[N]) 
 
 // blockIdx.y < draw_slots: the draw slot of request blockIdx.y (float64-heavy, dispatched
 // first); above: draft pair (blockIdx.y - draw_slots) = b*G1 + k for the labels (when per_pair).
-// 8 waves per SIMD (64 VGPRs): four workgroups per CU, so that one computing still leaves
-// three streaming (the draw slots' float64 path spills a few registers to scratch).
 template <typename T>
-__global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) void pair_kernel(
-    Ctx c, int draw_slots, int per_pair) {
+__device__ __forceinline__ void pair_body(const Ctx& c, int draw_slots, int per_pair) {
   __shared__ double sm[kWideThreads / kWave][kDrawSums + 1];
   __shared__ double smd[kWideThreads / kWave];
   const int seg = blockIdx.x;
@@ -529,6 +528,17 @@ __global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(8,
   }
   acc = block_sum_f64<kWideThreads>(acc, smd);
   if (threadIdx.x == 0) c.tv[(size_t(b) * G1 + k) * c.L.nseg + seg] = acc;
+}
+
+// bfloat16 rows: 8 waves per SIMD (64 VGPRs), four workgroups per CU, so that one computing
+// still leaves three streaming (the draw slots' float64 path spills a few registers to
+// scratch).  float32 rows hold twice the registers and keep the default.
+__global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) void pair_kernel_bf16(
+    Ctx c, int draw_slots, int per_pair) {
+  pair_body<uint16_t>(c, draw_slots, per_pair);
+}
+__global__ __launch_bounds__(kWideThreads) void pair_kernel_f32(Ctx c, int draw_slots, int per_pair) {
+  pair_body<float>(c, draw_slots, per_pair);
 }
 
 // ------------------------------------------------------------------ pick + commit + labels
@@ -743,8 +753,12 @@ hipError_t launch_typed(const Ctx& c, bool commit, hipStream_t stream) {
   const int draw_slots = commit ? a.B : 0;
   const int slots = draw_slots + (with_labels ? a.B * G1 : 0);
   if (slots > 0) {
-    hipLaunchKernelGGL(pair_kernel<T>, dim3(nseg, slots), dim3(kWideThreads), 0, stream, c,
-                       draw_slots, int(with_labels));
+    if constexpr (std::is_same<T, uint16_t>::value)
+      hipLaunchKernelGGL(pair_kernel_bf16, dim3(nseg, slots), dim3(kWideThreads), 0, stream, c,
+                         draw_slots, int(with_labels));
+    else
+      hipLaunchKernelGGL(pair_kernel_f32, dim3(nseg, slots), dim3(kWideThreads), 0, stream, c,
+                         draw_slots, int(with_labels));
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   hipLaunchKernelGGL(pick_kernel<T>, dim3(a.B), dim3(kPickThreads), 0, stream, c, int(commit));
