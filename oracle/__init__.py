@@ -25,10 +25,10 @@ Sources (web pages; cited by title and section, never by a line of any copy):
           (semi-autoregressive generation, the Markov head), "07 · Confidence Head",
           "08 · Core Innovation B", "09 · End-to-End Cycle".
 
-Pins: each function is checked in ``tests/test_oracle_pins.py`` and
-``tests/test_oracle_calibration.py`` against values the pages print (``tests/golden/``),
-closed forms, special cases that reduce to a library routine, and brute force on tiny
-inputs.  Parity unpinned: that the Sequential Temperature Scaling fit in
+Pins: each function is checked in ``tests/test_oracle_pins.py``,
+``tests/test_oracle_calibration.py`` and ``tests/test_oracle_markov.py`` against values
+the pages print (``tests/golden/``), closed forms, special cases that reduce to a library
+routine, and brute force on tiny inputs.  Parity unpinned: that the Sequential Temperature Scaling fit in
 ``calibration.py`` is the one the pages' authors ran (no page prints fitted temperatures;
 the estimator itself is pinned by its single-position special case, by recovery of known
 temperatures and by optimality).
