@@ -724,9 +724,13 @@ __global__ __launch_bounds__(kPickThreads) void pick_kernel(Ctx c, int commit) {
   double cum = s_base;
   for (int i = 0; i < wave; ++i) cum += s_wave[i];
   cum += inc;
-  if (wgt > 0.0) {
-    if (cum > s_t) atomicMin(&s_y, v);
-    atomicMax(&s_last, v);
+  // the first entry past u * Q and the last positive entry: found per wave by ballot (entry
+  // v = s_pos + tid is in lane order), then one LDS atomic per wave -- one atomic per lane
+  // on a single address serialises the whole workgroup
+  const unsigned long long hit = __ballot(wgt > 0.0 && cum > s_t), pos = __ballot(wgt > 0.0);
+  if (lane == 0) {
+    if (hit) atomicMin(&s_y, v + __ffsll(hit) - 1);
+    if (pos) atomicMax(&s_last, v + 63 - __clzll(pos));
   }
   __syncthreads();
   // the commit, one thread per block position (rounding that left u * Q past this
