@@ -629,8 +629,11 @@ __global__ __launch_bounds__(kPickThreads) void pick_kernel(Ctx c, int commit) {
   }
   if (!commit) return;
   if (d.n < 0) return;
+  // the 2^(j/256) table of the rescan is filled by waves 1.. while wave 0 locates the
+  // sub-segment; the barrier after the search publishes both
+  static_assert(kPickThreads - kWave >= 256, "waves 1.. fill the 256-entry table");
   __shared__ double tab[256];
-  fill_exp2_tab(c.P, tab);
+  if (tid >= kWave && tid - kWave < 256) tab[tid - kWave] = exp2_f64(c.P, double(tid - kWave) / 256.0);
   if (wave == 0 && lanes_cover) {
     // the general path below with every per-segment value held by its lane: the same sums
     // in the same order, without re-reading the draw sums for each step
