@@ -9,7 +9,7 @@
 //   conf_head_kernel  one wave per (request, draft position): float64 dot product of the
 //                     hidden state with the head weights, + bias, / T_k, logistic in
 //                     float64, rounded to float32.  Skipped when the caller supplies c.
-//   schedule_kernel   ONE workgroup of 1024 threads for the whole batch:
+//   schedule_kernel   ONE workgroup (256 to 1024 threads, by batch size) for the whole batch:
 //                     (1) one lane per request forms the survival product left to right
 //                         in float32 (bit-identical to a sequential definition);
 //                     (2) a bitonic sort in LDS of 64-bit keys (inverted survival bits,
@@ -49,9 +49,10 @@ __global__ __launch_bounds__(256) void conf_head_kernel(const T* __restrict__ hi
   }
 }
 
+template <int NT>
 __device__ __forceinline__ double block_exclusive_scan_f64(double v, double* lds_waves,
                                                            double* total) {
-  // Inclusive scan inside the wave, then across the 16 wave totals.
+  // Inclusive scan inside the wave, then across the NT / 64 wave totals.
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   double x = v;
 #pragma unroll
@@ -62,17 +63,17 @@ __device__ __forceinline__ double block_exclusive_scan_f64(double v, double* lds
   if (lane == kWave - 1) lds_waves[wave] = x;
   __syncthreads();
   if (wave == 0) {
-    double t = lane < kSchedThreads / kWave ? lds_waves[lane] : 0.0;
+    double t = lane < NT / kWave ? lds_waves[lane] : 0.0;
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
       const double y = __shfl_up(t, o);
       if (lane >= o) t += y;
     }
-    if (lane < kSchedThreads / kWave) lds_waves[lane] = t;  // inclusive wave prefix
+    if (lane < NT / kWave) lds_waves[lane] = t;  // inclusive wave prefix
   }
   __syncthreads();
   const double wave_off = wave > 0 ? lds_waves[wave - 1] : 0.0;
-  *total = lds_waves[kSchedThreads / kWave - 1];
+  *total = lds_waves[NT / kWave - 1];
   return wave_off + x - v;
 }
 
@@ -89,7 +90,7 @@ __device__ __forceinline__ uint64_t bitonic_keep(uint64_t x, uint64_t y, int i, 
   return keep_min ? (x < y ? x : y) : (x > y ? x : y);
 }
 
-// Ascending bitonic sort of Npad (a power of two, <= E * kSchedThreads) keys; thread t holds
+// Ascending bitonic sort of Npad (a power of two, <= E * NT) keys; thread t holds
 // the E consecutive elements t*E .. t*E + E - 1 in x.  Partners in the same thread are swapped
 // in registers, partners in the same wave by lane shuffles, and only partners in other waves
 // go through LDS (two barriers per such step).
@@ -132,8 +133,10 @@ __device__ __forceinline__ void bitonic_sort(uint64_t (&x)[E], uint64_t* lds, in
   }
 }
 
-template <int E>
-__global__ __launch_bounds__(kSchedThreads) void schedule_kernel(
+// E keys per thread, NT threads (small batches take fewer waves: each sort step's shuffles
+// and barriers then involve fewer of them).
+template <int E, int NT>
+__global__ __launch_bounds__(NT) void schedule_kernel(
     int B, int G, int mode, const float* __restrict__ conf, float* __restrict__ conf_out,
     float* __restrict__ surv_out, float bias, const float* __restrict__ alpha,
     const float* __restrict__ theta, int32_t* __restrict__ windows, int32_t* __restrict__ K_out,
@@ -141,9 +144,9 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(
   __shared__ uint64_t keys[kMaxCand];
   __shared__ float sa[kMaxCand];
   __shared__ int cnt[kMaxCand];
-  __shared__ double wave_tot[kSchedThreads / kWave];
-  __shared__ double red_ratio[kSchedThreads / kWave];
-  __shared__ int red_K[kSchedThreads / kWave];
+  __shared__ double wave_tot[NT / kWave];
+  __shared__ double red_ratio[NT / kWave];
+  __shared__ int red_K[NT / kWave];
 
   const int tid = threadIdx.x;
   const int N = B * G;
@@ -162,14 +165,14 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(
   const float theta_N = theta[B + N];
   // (1) survival: the confidences are staged in LDS by one coalesced load, then one lane per
   // request forms the float32 products left to right
-  for (int i = tid; i < N; i += kSchedThreads) {
+  for (int i = tid; i < N; i += NT) {
     const float c = conf[i];
     if (!(c >= 0.f && c <= 1.f)) flag(status, RVA_DEV_BAD_CONF);
     if (conf_out) conf_out[i] = c;
     sa[i] = c;
   }
   __syncthreads();
-  for (int b = tid; b < B; b += kSchedThreads) {
+  for (int b = tid; b < B; b += NT) {
     float a = 1.f;
     for (int j = 0; j < G; ++j) {
       a = (j == 0) ? sa[b * G + j] : __fmul_rn(a, sa[b * G + j]);
@@ -206,7 +209,7 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(
     if (r < N) run += double(__uint_as_float(~uint32_t(keys[r] >> 32)));
   }
   double total;
-  double prefix = block_exclusive_scan_f64(run, wave_tot, &total);
+  double prefix = block_exclusive_scan_f64<NT>(run, wave_tot, &total);
 
   // (4) ratio (B + S_K) / T(B, K); K = r + 1 for rank r, K = 0 handled by thread 0
   const double ba = double(bias) + double(alpha_B);
@@ -250,8 +253,8 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(
   }
   __syncthreads();
   if (wave == 0) {
-    best = lane < kSchedThreads / kWave ? red_ratio[lane] : -INFINITY;
-    bestK = lane < kSchedThreads / kWave ? red_K[lane] : 0x7fffffff;
+    best = lane < NT / kWave ? red_ratio[lane] : -INFINITY;
+    bestK = lane < NT / kWave ? red_K[lane] : 0x7fffffff;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
       const double ob = __shfl_xor(best, o);
@@ -281,7 +284,7 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(
     if (r < Kstar && r < N) atomicAdd(&cnt[int(uint32_t(keys[r]) / uint32_t(G))], 1);
   }
   __syncthreads();
-  for (int b = tid; b < B; b += kSchedThreads) windows[b] = 1 + cnt[b];
+  for (int b = tid; b < B; b += NT) windows[b] = 1 + cnt[b];
   if (tid == 0) {
     *K_out = Kstar;
     *ratio_out = ratio;
@@ -317,15 +320,21 @@ hipError_t launch_schedule(int B, int gamma, int mode, const void* hidden, int h
   float* echo = conf_in ? conf_out : nullptr;
   int Npad = 2;
   while (Npad < rows) Npad <<= 1;
-  if (Npad <= kSchedThreads)
-    hipLaunchKernelGGL(schedule_kernel<1>, dim3(1), dim3(kSchedThreads), 0, stream, B, G, mode,
+  if (Npad <= 256)
+    hipLaunchKernelGGL((schedule_kernel<1, 256>), dim3(1), dim3(256), 0, stream, B, G, mode,
                        conf, echo, surv_out, bias, alpha, theta, windows, K_out, ratio_out, status);
+  else if (Npad <= 512)
+    hipLaunchKernelGGL((schedule_kernel<1, 512>), dim3(1), dim3(512), 0, stream, B, G, mode,
+                       conf, echo, surv_out, bias, alpha, theta, windows, K_out, ratio_out, status);
+  else if (Npad <= kSchedThreads)
+    hipLaunchKernelGGL((schedule_kernel<1, kSchedThreads>), dim3(1), dim3(kSchedThreads), 0, stream, B, G,
+                       mode, conf, echo, surv_out, bias, alpha, theta, windows, K_out, ratio_out, status);
   else if (Npad <= 2 * kSchedThreads)
-    hipLaunchKernelGGL(schedule_kernel<2>, dim3(1), dim3(kSchedThreads), 0, stream, B, G, mode,
-                       conf, echo, surv_out, bias, alpha, theta, windows, K_out, ratio_out, status);
+    hipLaunchKernelGGL((schedule_kernel<2, kSchedThreads>), dim3(1), dim3(kSchedThreads), 0, stream, B, G,
+                       mode, conf, echo, surv_out, bias, alpha, theta, windows, K_out, ratio_out, status);
   else
-    hipLaunchKernelGGL(schedule_kernel<4>, dim3(1), dim3(kSchedThreads), 0, stream, B, G, mode,
-                       conf, echo, surv_out, bias, alpha, theta, windows, K_out, ratio_out, status);
+    hipLaunchKernelGGL((schedule_kernel<4, kSchedThreads>), dim3(1), dim3(kSchedThreads), 0, stream, B, G,
+                       mode, conf, echo, surv_out, bias, alpha, theta, windows, K_out, ratio_out, status);
   return hipGetLastError();
 }
 
