@@ -165,10 +165,17 @@ __device__ __forceinline__ void build_table(const AttnArgs& a, ReqTable& t, bool
   __syncthreads();
 }
 
-// First global tile of workgroup p's share, and the workgroup whose share holds tile x.
-__device__ __forceinline__ int share_lo(int T, int P, int p) { return int((long long)T * p / P); }
+// Workgroup p's share of the T weighted units is [share_lo(p), share_lo(p + 1)); share_owner
+// is the workgroup whose share holds unit x.  With at least as many units as workgroups the
+// shares are the even split floor(T p / P), none of them empty.  With fewer (a small batch
+// of short contexts), workgroup p < T takes unit p alone and the others take nothing: an
+// even split would leave empty shares between non-empty ones, and the merge of a cut
+// segment reads one partial from every workgroup from its first to its last share.
+__device__ __forceinline__ int share_lo(int T, int P, int p) {
+  return T >= P ? int((long long)T * p / P) : min(p, T);
+}
 __device__ __forceinline__ int share_owner(int T, int P, int x) {
-  return int(((long long)(x + 1) * P - 1) / T);
+  return T >= P ? int(((long long)(x + 1) * P - 1) / T) : x;
 }
 
 // Largest b with pre[b] <= x (skips requests without tiles).
