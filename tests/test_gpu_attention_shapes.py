@@ -6,7 +6,9 @@ Each case builds a small seeded batch and compares the HIP path with the oracle
 * head dimension 64 on the fast path (bf16), GQA groups of 1, 4 and 8, page sizes 32, 128
   and 256, and one float32 case on the generic path (page 16);
 * column blocks NB = 1, 2 and 4 (window rows x group of 16, 32 and 64 columns);
-* contexts of 0, 1, one short of / exactly / one past a 32-key tile and of a page.
+* contexts of 0, 1, one short of / exactly / one past a 32-key tile and of a page;
+* batches whose weighted work is below the grid size, and one long segment spread over
+  every workgroup.
 
 Bar: max over (row, head) of max|o - r| / max|r| <= 1e-2; pad rows [M, tier) zero and rows
 past the tier untouched; both caches after the call (the appended window K/V and every
@@ -35,6 +37,10 @@ CASES = [
     ("d128-g1-p256-nb1", "bf16", 128, 8, 8, 256, [0, 5, 255, 256, 700], [16, 3, 1, 9, 16]),
     ("d128-g4-p32-nb2", "bf16", 128, 16, 4, 32, [31, 32, 63, 64, 257, 1000], [8, 7, 1, 5, 8, 2]),
     ("d128-f32-p16-generic", "f32", 128, 4, 2, 16, [0, 17, 40], [3, 1, 4]),
+    # one segment over every workgroup (the merge's loop over more than four shares)
+    ("d128-g4-p64-one-long", "bf16", 128, 4, 1, 64, [20000], [3]),
+    ("d64-g16-p64-nb4", "bf16", 64, 32, 2, 64, [700, 33, 2000], [4, 2, 3]),
+    ("d64-g2-p32-nb2", "bf16", 64, 4, 2, 32, [1000, 64, 5], [16, 9, 12]),
 ]
 
 
