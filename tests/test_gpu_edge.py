@@ -142,3 +142,11 @@ def test_accept_odd_vocab(V):
     print(f"[accept-vocab] V={V}", flush=True)
     _accept_case(6, 5, V, [5, 1, 3, 4, 2, 5], seed=V)
     _accept_case(6, 5, V, [5, 1, 3, 4, 2, 5], seed=V + 1, dtype=torch.float32)
+
+
+def test_accept_vocab_beyond_one_wave_of_segments():
+    """V = 1,100,000: 68 segments of 16384, more than one wave's 64 lanes, so the pick's
+    segment search takes its general path (segment sums re-read per step) and the
+    normaliser loops stride over the segments."""
+    print("[accept-vocab] V=1100000", flush=True)
+    _accept_case(3, 3, 1_100_000, [3, 1, 2], seed=11)
