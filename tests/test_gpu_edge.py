@@ -2,8 +2,9 @@
 
 Covers shapes the five workloads do not reach: scheduler candidate counts on every sort
 layout (up to 1024, 2048 and 4096 candidates), heavy survival ties, single-draft and
-single-request batches, and acceptance batches whose windows are all 1 (no drafts: every
-request takes the bonus draw) or all gamma.
+single-request batches, acceptance batches whose windows are all 1 (no drafts: every
+request takes the bonus draw) or all gamma, odd and very large vocabularies, and packs of
+rows whose size is not a multiple of 16 bytes.
 """
 
 from __future__ import annotations
@@ -150,3 +151,38 @@ def test_accept_vocab_beyond_one_wave_of_segments():
     normaliser loops stride over the segments."""
     print("[accept-vocab] V=1100000", flush=True)
     _accept_case(3, 3, 1_100_000, [3, 1, 2], seed=11)
+
+
+@pytest.mark.parametrize("elems,dtype", [(3, torch.bfloat16), (2050, torch.bfloat16), (5, torch.float32)],
+                         ids=["6-byte-rows", "4100-byte-rows", "20-byte-rows"])
+def test_pack_unaligned_rows(elems, dtype):
+    """Row sizes that are not multiples of 16 bytes take the scalar copy path; the total
+    14 rounds up to tier 16 (two zero rows); rows past the tier keep their contents."""
+    print(f"[pack-edge] {elems} x {dtype}", flush=True)
+    rng = np.random.default_rng(elems)
+    B, gamma = 5, 4
+    windows = np.array([1, 4, 2, 3, 4], np.int32)
+    ctx = rng.integers(0, 1000, size=B).astype(np.int32)
+    tiers = [8, 12, 16, 20]
+    max_rows = 20
+    src = torch.from_numpy(rng.standard_normal((B, gamma, elems)).astype(np.float32)).to(dtype)
+    ref = oracle.pack_ragged(windows, ctx, tiers, src=src.double().numpy(), max_rows=max_rows)
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    dst = torch.full((max_rows, elems), 7.0, dtype=dtype, device=DEV)
+    cu = torch.empty(B + 1, dtype=torch.int32, device=DEV)
+    row_req = torch.empty(max_rows, dtype=torch.int32, device=DEV)
+    row_pos = torch.empty(max_rows, dtype=torch.int32, device=DEV)
+    tt = torch.empty(2, dtype=torch.int32, device=DEV)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    rva.pack_ragged(B, gamma, d(windows), d(ctx), tiers, src.to(DEV), dst, max_rows, cu, row_req,
+                    row_pos, tt, status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    M, tier = ref["M"], ref["tier"]
+    assert (M, tier) == (14, 16) and tt.cpu().tolist() == [M, tier]
+    assert cu.cpu().tolist() == list(ref["cu_seqlens"])
+    assert row_req.cpu().tolist() == list(ref["row_req"])
+    assert row_pos.cpu().tolist() == list(ref["row_pos"])
+    got = dst.double().cpu().numpy()
+    assert np.array_equal(got[:tier], ref["dst"][:tier])
+    assert np.all(got[tier:] == 7.0)
