@@ -41,6 +41,10 @@ CASES = [
     ("d128-g4-p64-one-long", "bf16", 128, 4, 1, 64, [20000], [3]),
     ("d64-g16-p64-nb4", "bf16", 64, 32, 2, 64, [700, 33, 2000], [4, 2, 3]),
     ("d64-g2-p32-nb2", "bf16", 64, 4, 2, 32, [1000, 64, 5], [16, 9, 12]),
+    # more work units than workgroups at D = 64: segments cut between two or three shares
+    ("d64-g4-p64-long-nb1", "bf16", 64, 8, 2, 64, [4000, 3100, 5000, 2500, 4100, 3999, 4500, 3000],
+     [4, 1, 3, 4, 2, 4, 1, 3]),
+    ("d64-g8-p64-long-nb4", "bf16", 64, 16, 2, 64, [3000, 4096, 2048, 5000], [8, 6, 2, 7]),
 ]
 
 
