@@ -3,8 +3,9 @@
 Covers shapes the five workloads do not reach: scheduler candidate counts on every sort
 layout (up to 1024, 2048 and 4096 candidates), heavy survival ties, single-draft and
 single-request batches, acceptance batches whose windows are all 1 (no drafts: every
-request takes the bonus draw) or all gamma, odd and very large vocabularies, and packs of
-rows whose size is not a multiple of 16 bytes.
+request takes the bonus draw) or all gamma, cap-accept with caps of 1, random and the whole
+block, odd and very large vocabularies, and packs of rows whose size is not a multiple of
+16 bytes.
 """
 
 from __future__ import annotations
@@ -186,3 +187,60 @@ def test_pack_unaligned_rows(elems, dtype):
     got = dst.double().cpu().numpy()
     assert np.array_equal(got[:tier], ref["dst"][:tier])
     assert np.all(got[tier:] == 7.0)
+
+
+@pytest.mark.parametrize("cap_kind", ["all-1", "random", "all-gamma"])
+def test_accept_capped_edges(cap_kind):
+    """Cap-accept with caps of 1 (only the anchor's bonus draw may be committed), random
+    caps, and caps equal to the block (plain static acceptance), against the oracle."""
+    print(f"[accept-capped-edge] {cap_kind}", flush=True)
+    rng = np.random.default_rng({"all-1": 21, "random": 22, "all-gamma": 23}[cap_kind])
+    B, gamma, V = 12, 6, 40_000
+    G1 = gamma - 1
+    caps = {"all-1": np.ones(B, np.int32), "all-gamma": np.full(B, gamma, np.int32),
+            "random": rng.integers(1, gamma + 1, size=B).astype(np.int32)}[cap_kind]
+    cu = (np.arange(B + 1) * gamma).astype(np.int32)  # whole blocks verified
+    max_rows = B * gamma + 2
+    tl = (rng.standard_normal((max_rows, V)) * 2.0).astype(np.float32)
+    dl = (rng.standard_normal((B * G1, V)) * 2.0).astype(np.float32)
+    for b in range(0, B, 2):  # drafts close to the target for half the requests
+        for k in range(G1):
+            dl[b * G1 + k] = tl[cu[b] + k] + 0.3 * rng.standard_normal(V).astype(np.float32)
+    tl_t = torch.from_numpy(tl).to(torch.bfloat16)
+    dl_t = torch.from_numpy(dl).to(torch.bfloat16)
+    tokens = rng.integers(0, V, size=(B, G1)).astype(np.int32)
+    ua = rng.random((B, G1)).astype(np.float32)
+    ur = rng.random(B).astype(np.float32)
+    ctx0 = rng.integers(10, 100, size=B).astype(np.int32)
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    acc = torch.empty(B, dtype=torch.int32, device=DEV)
+    full = torch.empty(B, dtype=torch.int32, device=DEV)
+    com = torch.empty((B, gamma), dtype=torch.int32, device=DEV)
+    ctx = d(ctx0)
+    pt = torch.empty((B, G1), dtype=torch.float32, device=DEV)
+    pd = torch.empty((B, G1), dtype=torch.float32, device=DEV)
+    lab = torch.empty((B, G1), dtype=torch.float32, device=DEV)
+    ws = torch.empty(rva.accept_workspace_size(B, gamma, V, max_rows), dtype=torch.uint8, device=DEV)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    rva.accept_capped(B, gamma, V, max_rows, tl_t.to(DEV), dl_t.to(DEV), d(tokens), d(ua), d(ur),
+                      d(cu), d(caps), acc, full, com, ctx, pt, pd, lab, ws, status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    tl64, dl64 = tl_t.double().numpy(), dl_t.double().numpy()
+    acc_h, full_h, com_h, ctx_h, lab_h = (x.cpu().numpy() for x in (acc, full, com, ctx, lab))
+    flips = 0
+    for b in range(B):
+        r = oracle.accept_request_capped(tl64[cu[b]:cu[b] + gamma], dl64[b * G1:(b + 1) * G1],
+                                         tokens[b], ua[b], ur[b], int(caps[b]))
+        band = any(m < 1e-6 for m in r["margins"]) or r["draw_margin"] < 1e-9
+        same = acc_h[b] == r["n"] and full_h[b] == r["n_full"] and \
+            list(com_h[b, : r["n"] + 1]) == list(r["committed"])
+        if not same:
+            assert band, f"request {b}: {acc_h[b]}/{full_h[b]} {com_h[b]} vs {r['n']}/{r['n_full']} {r['committed']}"
+            flips += 1
+            continue
+        assert np.all(com_h[b, r["n"] + 1:] == -1)
+        assert ctx_h[b] == ctx0[b] + r["n"] + 1
+        assert acc_h[b] <= caps[b] - 1
+        np.testing.assert_allclose(lab_h[b], r["labels"], atol=1e-5, rtol=0)
+    assert flips <= 1
