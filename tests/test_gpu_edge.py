@@ -1,7 +1,8 @@
 """GPU edge cases through the C ABI, each against the oracle.
 
 Covers shapes the five workloads do not reach: scheduler candidate counts on every sort
-layout (up to 1024, 2048 and 4096 candidates), heavy survival ties, single-draft and
+layout (up to 1024, 2048 and 4096 candidates), heavy survival ties, the confidence head
+with per-position temperatures (bf16 and f32 hidden states), single-draft and
 single-request batches, acceptance batches whose windows are all 1 (no drafts: every
 request takes the bonus draw) or all gamma, cap-accept with caps of 1, random and the whole
 block, odd and very large vocabularies, and packs of rows whose size is not a multiple of
@@ -244,3 +245,40 @@ def test_accept_capped_edges(cap_kind):
         assert acc_h[b] <= caps[b] - 1
         np.testing.assert_allclose(lab_h[b], r["labels"], atol=1e-5, rtol=0)
     assert flips <= 1
+
+
+@pytest.mark.parametrize("hdtype", [torch.bfloat16, torch.float32], ids=["bf16-hidden", "f32-hidden"])
+def test_schedule_head_with_temperatures(hdtype):
+    """The confidence head with per-position temperatures (c = sigmoid(z / T_k)) feeding the
+    window choice, against the oracle: confidences and survival bit-exact, windows exact
+    unless the oracle flags a near tie."""
+    print(f"[schedule-head-T] {hdtype}", flush=True)
+    rng = np.random.default_rng(31)
+    B, gamma, H = 24, 7, 640
+    G = gamma - 1
+    hidden = torch.from_numpy((rng.standard_normal((B, G, H)) * 0.5).astype(np.float32)).to(hdtype)
+    head_w = (rng.standard_normal(H) * 0.08).astype(np.float32)
+    head_b = np.float32(1.2)
+    T = np.array([0.7, 1.0, 1.3, 1.9, 2.5, 4.0], np.float32)
+    alpha = np.zeros(B + 1, np.float32)
+    theta = (np.float32(0.19) * np.arange(B * gamma + 1, dtype=np.float32)).astype(np.float32)
+    bias = np.float32(20.0)
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    conf_out = torch.empty((B, G), dtype=torch.float32, device=DEV)
+    surv = torch.empty((B, G), dtype=torch.float32, device=DEV)
+    windows = torch.empty(B, dtype=torch.int32, device=DEV)
+    K = torch.empty(1, dtype=torch.int32, device=DEV)
+    ratio = torch.empty(1, dtype=torch.float64, device=DEV)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    rva.schedule_windows(B, gamma, 0, hidden.to(DEV), H, d(head_w), float(head_b), None, d(T),
+                         float(bias), d(alpha), d(theta), conf_out, surv, windows, K, ratio, status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    c = oracle.confidence_from_head(hidden.double().numpy(), head_w, head_b, T)
+    a = oracle.survival(c)
+    ref = oracle.schedule_windows(a, gamma, bias, alpha, theta)
+    assert np.array_equal(conf_out.cpu().numpy().view(np.uint32), c.view(np.uint32))
+    assert np.array_equal(surv.cpu().numpy().view(np.uint32), a.view(np.uint32))
+    if not ref["near_tie"]:
+        assert np.array_equal(windows.cpu().numpy(), ref["windows"])
+        assert int(K.item()) == ref["K"]
