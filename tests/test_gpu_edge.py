@@ -282,3 +282,43 @@ def test_schedule_head_with_temperatures(hdtype):
     if not ref["near_tie"]:
         assert np.array_equal(windows.cpu().numpy(), ref["windows"])
         assert int(K.item()) == ref["K"]
+
+
+def test_accept_without_optional_outputs():
+    """Acceptance with no labels and no probability outputs (the pair pass then runs only
+    its draw slots) commits exactly what the full call commits on the same inputs."""
+    print("[accept-optional] labels/probs off", flush=True)
+    rng = np.random.default_rng(41)
+    B, gamma, V = 16, 8, 30_000
+    G1 = gamma - 1
+    windows = rng.integers(1, gamma + 1, size=B)
+    cu = np.concatenate([[0], np.cumsum(windows)]).astype(np.int32)
+    max_rows = int(cu[-1]) + 2
+    tl = (rng.standard_normal((max_rows, V)) * 2.0).astype(np.float32)
+    dl = (rng.standard_normal((B * G1, V)) * 2.0).astype(np.float32)
+    for b in range(0, B, 2):
+        for k in range(windows[b] - 1):
+            dl[b * G1 + k] = tl[cu[b] + k] + 0.3 * rng.standard_normal(V).astype(np.float32)
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    tl_d = torch.from_numpy(tl).to(torch.bfloat16).to(DEV)
+    dl_d = torch.from_numpy(dl).to(torch.bfloat16).to(DEV)
+    tokens = d(rng.integers(0, V, size=(B, G1)).astype(np.int32))
+    ua = d(rng.random((B, G1)).astype(np.float32))
+    ur = d(rng.random(B).astype(np.float32))
+    ctx0 = rng.integers(10, 100, size=B).astype(np.int32)
+    ws = torch.empty(rva.accept_workspace_size(B, gamma, V, max_rows), dtype=torch.uint8, device=DEV)
+    runs = []
+    for full_outputs in (True, False):
+        acc = torch.empty(B, dtype=torch.int32, device=DEV)
+        com = torch.empty((B, gamma), dtype=torch.int32, device=DEV)
+        ctx = d(ctx0)
+        opt = [torch.empty((B, G1), dtype=torch.float32, device=DEV) if full_outputs else None
+               for _ in range(3)]
+        status = torch.zeros(1, dtype=torch.int32, device=DEV)
+        rva.accept_and_commit(B, gamma, V, max_rows, tl_d, dl_d, tokens, ua, ur, d(cu), acc, com, ctx,
+                              opt[0], opt[1], opt[2], ws, status)
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0
+        runs.append((acc.cpu().numpy(), com.cpu().numpy(), ctx.cpu().numpy()))
+    for x, y in zip(runs[0], runs[1]):
+        assert np.array_equal(x, y)
