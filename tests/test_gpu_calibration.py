@@ -134,3 +134,33 @@ def test_fit_then_ece_drops():
     after, _ = _gpu_ece(z, n, None, T, 15)
     print(f"[ece] before {before[0]:.4f} after {after[0]:.4f}, T = {np.round(T, 3)}", flush=True)
     assert after[0] < 0.5 * before[0]
+
+
+@pytest.mark.parametrize("kind", ["unobserved-tail", "all-survive"])
+def test_sts_fit_degenerate(kind):
+    """Positions nobody observed keep T = 1 with NLL 0; outcomes that are all survivals put
+    the minimum on the bracket's lower end (sigmoid(z / T) -> 1 as T -> 0 for z > 0)."""
+    print(f"[sts-degenerate] {kind}", flush=True)
+    rng = np.random.default_rng(77)
+    if kind == "unobserved-tail":
+        N, G1 = 500, 5
+        z = rng.normal(1.0, 1.5, size=(N, G1)).astype(np.float32)
+        o = rng.integers(0, 3, size=N).astype(np.int32)  # positions 3..5 never observed
+        n = np.minimum(rng.integers(0, G1 + 1, size=N), o).astype(np.int32)
+    else:
+        N, G1 = 300, 2
+        z = rng.uniform(0.5, 3.0, size=(N, G1)).astype(np.float32)
+        o = None
+        n = np.full(N, G1, np.int32)
+    ref = oracle.sts_fit(z, n, observed_len=o)
+    T, nll = _gpu_fit(z, n, o)
+    for k in range(G1):
+        if ref["n_obs"][k] == 0:
+            assert T[k] == 1.0 and nll[k] == 0.0
+        else:
+            assert abs(T[k] / ref["T64"][k] - 1) <= T_TOL, (k, T[k], ref["T64"][k])
+            assert abs(nll[k] - ref["nll"][k]) <= NLL_TOL * abs(ref["nll"][k]) + 1e-12
+    if kind == "unobserved-tail":
+        assert list(ref["n_obs"][2:]) == [0, 0, 0]
+    else:
+        assert np.allclose(T, np.float32(0.05), rtol=1e-5)
