@@ -61,6 +61,7 @@ CASES = [
     ("small-bf16-r128", 3, 6, 4096, 128, "bf16", None),
     ("ragged-vocab", 70, 3, 1003, 256, "bf16", None),     # V not a multiple of 8, B > 64
     ("mixed-b64", 64, 7, 151936, 256, "bf16", [0, 17, 40, 63]),
+    ("one-request-one-draft", 1, 1, 333, 128, "bf16", None),  # B = 1, G1 = 1, V < 3 tiles
 ]
 
 
