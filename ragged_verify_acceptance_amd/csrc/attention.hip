@@ -492,7 +492,9 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, SkShared<D, NBMAX
   }
   if (bad) flag(a.status, RVA_DEV_BAD_PAGE);
 
-  // ---- merge the 4 waves: exchange (m, l), rescale, park in LDS slices, combine
+  // ---- merge the 4 waves
+  constexpr int S = NBMAX <= 2 ? 4 : 2;
+  constexpr int ROWS = NBMAX * 16;
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     float sum = l[nb];
@@ -503,35 +505,46 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, SkShared<D, NBMAX
       sh.l[wave][nb * 16 + lc] = sum;
     }
   }
-  __syncthreads();
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int col = nb * 16 + lc;
-    float M = -INFINITY;
-#pragma unroll
-    for (int v = 0; v < kWaves; ++v) M = fmaxf(M, sh.m[v][col]);
-    float Ls = 0.f;
-#pragma unroll
-    for (int v = 0; v < kWaves; ++v)
-      if (sh.m[v][col] != -INFINITY) Ls += sh.l[v][col] * __builtin_amdgcn_exp2f(sh.m[v][col] - M);
-    const float e = (m[nb] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m[nb] - M);
-#pragma unroll
-    for (int db = 0; db < DB; ++db) oacc[db][nb] *= e;
-    if (wave == 0 && lq == 0) {
-      sh.M[col] = M;
-      sh.Ls[col] = Ls;
-    }
-  }
-  constexpr int S = NBMAX <= 2 ? 4 : 2;
-  if (wave < S) {
+  if constexpr (S == kWaves) {
+    // one slice per wave: each wave parks its unscaled (m, l, o) and a single barrier
+    // separates that from the combine, which weighs slice v by 2^(m_v - M) per column
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int t = 0; t < 4; ++t) sh.o[wave][nb * 16 + lc][db * 16 + 4 * lq + t] = oacc[db][nb][t];
-  }
-  if constexpr (S < kWaves) {
+    __syncthreads();
+  } else {
+    // two slices: waves 2, 3 add into waves 0, 1's, so every wave first rescales to the
+    // common maximum (the combine below then finds weights of 1 for every slice)
+    __syncthreads();
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int col = nb * 16 + lc;
+      float M = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < kWaves; ++v) M = fmaxf(M, sh.m[v][col]);
+      const float e = (m[nb] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m[nb] - M);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db][nb] *= e;
+      if (wave == 0 && lq == 0) {
+        float Ls = 0.f;
+#pragma unroll
+        for (int v = 0; v < kWaves; ++v)
+          if (sh.m[v][col] != -INFINITY) Ls += sh.l[v][col] * __builtin_amdgcn_exp2f(sh.m[v][col] - M);
+        sh.M[col] = M;
+        sh.Ls[col] = Ls;
+      }
+    }
+    if (wave < S) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int t = 0; t < 4; ++t) sh.o[wave][nb * 16 + lc][db * 16 + 4 * lq + t] = oacc[db][nb][t];
+    }
     __syncthreads();
     if (wave >= S) {
 #pragma unroll
@@ -541,19 +554,36 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, SkShared<D, NBMAX
 #pragma unroll
           for (int t = 0; t < 4; ++t) sh.o[wave - S][nb * 16 + lc][db * 16 + 4 * lq + t] += oacc[db][nb][t];
     }
+    __syncthreads();
   }
-  __syncthreads();
-  constexpr int ROWS = NBMAX * 16;
   for (int it = tid; it < nq * (D / 8); it += kThreads) {  // 8 consecutive d per thread
     const int col = it / (D / 8), d0 = (it % (D / 8)) * 8;
+    float wgt[S];
+    float M, Ls;
+    if constexpr (S == kWaves) {
+      M = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < kWaves; ++v) M = fmaxf(M, sh.m[v][col]);
+      Ls = 0.f;
+#pragma unroll
+      for (int v = 0; v < kWaves; ++v) {
+        const float mv = sh.m[v][col];
+        wgt[v] = mv == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mv - M);
+        Ls += sh.l[v][col] * wgt[v];
+      }
+    } else {
+      M = sh.M[col];
+      Ls = sh.Ls[col];
+#pragma unroll
+      for (int v = 0; v < S; ++v) wgt[v] = 1.f;
+    }
     float v[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) v[u] = 0.f;
 #pragma unroll
     for (int sl = 0; sl < S; ++sl)
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] += sh.o[sl][col][d0 + u];
-    const float Ls = sh.Ls[col];
+      for (int u = 0; u < 8; ++u) v[u] += wgt[sl] * sh.o[sl][col][d0 + u];
     const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
     if (full) {
       uint32_t pk[4];
@@ -568,7 +598,7 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, SkShared<D, NBMAX
       reinterpret_cast<float4*>(ws_o)[1] = make_float4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
       if (d0 == 0) {
         float* ws_lse = static_cast<float*>(a.ws) + size_t(gridDim.x) * 2 * ROWS * D;
-        ws_lse[size_t(slot_index) * ROWS + col] = Ls > 0.f ? sh.M[col] + __log2f(Ls) : -INFINITY;
+        ws_lse[size_t(slot_index) * ROWS + col] = Ls > 0.f ? M + __log2f(Ls) : -INFINITY;
       }
     }
   }
