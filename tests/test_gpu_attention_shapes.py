@@ -45,6 +45,9 @@ CASES = [
     ("d64-g4-p64-long-nb1", "bf16", 64, 8, 2, 64, [4000, 3100, 5000, 2500, 4100, 3999, 4500, 3000],
      [4, 1, 3, 4, 2, 4, 1, 3]),
     ("d64-g8-p64-long-nb4", "bf16", 64, 16, 2, 64, [3000, 4096, 2048, 5000], [8, 6, 2, 7]),
+    # one kv head for all query heads (group 32), and pages of 1024 slots
+    ("d128-mqa-g32-p64", "bf16", 128, 32, 1, 64, [500, 3000, 7], [2, 1, 2]),
+    ("d128-g4-p1024", "bf16", 128, 16, 4, 1024, [1023, 1024, 2500, 0], [8, 3, 5, 8]),
 ]
 
 
