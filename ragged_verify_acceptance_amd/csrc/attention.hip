@@ -14,9 +14,11 @@
 //   * Balance: persistent grid, one workgroup per CU slot; all segments form one weighted
 //     sequence (each segment = its tiles + a fixed start cost of kSegCost tile units) and
 //     workgroup p owns the contiguous share [W p / P, W (p+1) / P) (stream-K over bytes AND
-//     per-segment overhead).  A segment that lies inside one share is finished by that
-//     workgroup; a segment cut by share boundaries leaves at most one partial per workgroup
-//     side and attn_merge_kernel combines them.  No workgroup ever waits for another.
+//     per-segment overhead; with W < P, unit p alone).  A segment that lies inside one
+//     share is finished by that workgroup; a segment cut by share boundaries leaves at most
+//     one partial per workgroup side and attn_merge_kernel combines them.  No workgroup
+//     ever waits for another.  At a segment's end the 4 waves park (m, l, o) in LDS slices
+//     and combine them after one barrier.
 //   * Inside a workgroup the 4 waves take the segment's tiles round-robin, one wave per
 //     SIMD.  Each wave alternates two register buffers, so the next tile (16 KB at
 //     D = 128) is in flight while it computes the current one (NB = 4 keeps one buffer: its
