@@ -37,3 +37,21 @@ def _library_built():
     if not os.path.exists(_build.LIB_PATH):
         _build.build(verbose=True)
     yield
+
+
+def pytest_terminal_summary(terminalreporter, exitstatus, config):
+    """Flip counts of the GPU parity tests: requests whose integer outputs differ from the
+    oracle inside the flip band (accept test |u - p_t/p_d| < 1e-6, draw u*S within 1e-9*S of
+    a bin edge, scheduler near-tie), per test."""
+    try:
+        from tests.reference import FLIPS
+    except Exception:  # pragma: no cover
+        return
+    if not FLIPS:
+        return
+    tw = terminalreporter
+    total_c = sum(c for c, _ in FLIPS.values())
+    total_f = sum(f for _, f in FLIPS.values())
+    tw.write_sep("-", f"flip counts: {total_f} in band over {total_c} checked decisions/requests")
+    for tag, (c, f) in sorted(FLIPS.items()):
+        tw.write_line(f"  {tag}: {f} / {c}")
