@@ -8,6 +8,7 @@
  *                                   survival, per-request verify window
  *   rva_pack_ragged        stage 2  ragged packing of the window rows + tier rounding
  *   rva_verify_attention   stage 3  varlen GQA attention over the paged KV cache (+ append)
+ *   rva_verify_attention_noalloc  stage 3 with a library-owned scratch (no workspace)
  *   rva_accept_and_commit  stage 4  speculative-sampling acceptance, draw, commit
  *                          (+ stage 5 TV labels when `labels` is given)
  *   rva_confidence_labels  stage 5  TV-distance confidence labels on their own
@@ -27,7 +28,8 @@
  *
  * Conventions shared by every call
  *   - Ownership: the caller allocates every buffer and owns it; the library allocates
- *     nothing and keeps no state between calls (the thread-local error text aside).
+ *     nothing and keeps no state between calls (the thread-local error text aside, and the
+ *     static scratch that rva_verify_attention_noalloc uses in place of a workspace).
  *   - Pointers: all array arguments are DEVICE pointers unless the parameter name ends
  *     in `_host`.  Scalars are passed by value.
  *   - Asynchrony: a call validates its scalar arguments on the host, enqueues kernels on
@@ -202,6 +204,35 @@ rva_status rva_verify_attention(int B, int max_window, int max_rows, int Hq, int
 
 size_t rva_verify_attention_workspace_size(int B, int max_window, int Hq, int Hkv, int D,
                                            int page_size, int max_pages, int kv_dtype);
+
+/*
+ * Stage 3 without a workspace -- rva_verify_attention_noalloc
+ *
+ * For callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.  Identical to rva_verify_attention
+ * (same arguments minus the workspace, same kernels, bit-identical results), except that
+ * the stream-K partials and merge records go to a library-owned static scratch of
+ * 24 MiB per device instead of a caller workspace.  Nothing is allocated by the call.
+ *   - The scratch is a file-scope device array, zero at load and held by each device the
+ *     library runs on until the process ends; its device address is looked up once per
+ *     device (on the first call with that device current).
+ *   - Every call on one device shares that device's scratch and leaves the last call's
+ *     contents in it; calls that overlap on one device (two streams, or two host threads)
+ *     RACE and must be serialised by the caller.  Calls on different devices are
+ *     independent.
+ *   - A shape whose scratch need (rva_verify_attention_workspace_size) exceeds 24 MiB
+ *     returns RVA_ERR_WORKSPACE_TOO_SMALL and enqueues nothing: use rva_verify_attention
+ *     then.  Shapes whose path needs no scratch (fp32 KV, non-power-of-two pages) always
+ *     fit.
+ */
+rva_status rva_verify_attention_noalloc(int B, int max_window, int max_rows, int Hq, int Hkv,
+                                        int D, int page_size, int num_pages, int max_pages,
+                                        int kv_dtype, const void* q, const void* k_new,
+                                        const void* v_new, void* k_cache, void* v_cache,
+                                        const int32_t* block_table, const int32_t* context_lens,
+                                        const int32_t* cu_seqlens, const int32_t* total_tier,
+                                        float softmax_scale, void* out, int32_t* device_status,
+                                        hipStream_t stream);
 
 /*
  * Stages 4 (+5) -- rva_accept_and_commit

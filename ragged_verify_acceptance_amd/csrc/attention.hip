@@ -975,7 +975,35 @@ hipError_t launch_generic(const AttnArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Library-owned scratch of rva_verify_attention_noalloc: the stream-K partials and the
+// merge records live here instead of in a caller workspace.  Zero-initialised at load, held
+// by every device the library runs on until the process ends; every noalloc call on one
+// device shares it (calls that overlap on one device race).  Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in): the device address comes
+// from hipGetSymbolAddress, once per device.
+constexpr size_t kScratchBytes = size_t(24) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 }  // namespace
+
+hipError_t attention_scratch(void** ptr, size_t* bytes) {
+  static std::mutex mu;
+  static void* addr[64] = {nullptr};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  *bytes = kScratchBytes;
+  return hipSuccess;
+}
 
 size_t attention_workspace_bytes(int B, int max_window, int Hq, int Hkv, int D, int page_size,
                                  int max_pages, int kv_dtype) {

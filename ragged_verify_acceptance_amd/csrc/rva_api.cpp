@@ -115,14 +115,18 @@ size_t rva_verify_attention_workspace_size(int B, int max_window, int Hq, int Hk
   return rva::attention_workspace_bytes(B, max_window, Hq, Hkv, D, page_size, max_pages, kv_dtype);
 }
 
-rva_status rva_verify_attention(int B, int max_window, int max_rows, int Hq, int Hkv, int D,
-                                int page_size, int num_pages, int max_pages, int kv_dtype,
-                                const void* q, const void* k_new, const void* v_new,
-                                void* k_cache, void* v_cache, const int32_t* block_table,
-                                const int32_t* context_lens, const int32_t* cu_seqlens,
-                                const int32_t* total_tier, float softmax_scale, void* out,
-                                int32_t* device_status, void* workspace, size_t workspace_bytes,
-                                hipStream_t stream) {
+namespace {
+
+// Shared by both attention entry points.  lib_scratch: the workspace is the library's
+// static scratch (looked up after the arguments are validated).
+rva_status attention_call(const char* name, int B, int max_window, int max_rows, int Hq,
+                          int Hkv, int D, int page_size, int num_pages, int max_pages,
+                          int kv_dtype, const void* q, const void* k_new, const void* v_new,
+                          void* k_cache, void* v_cache, const int32_t* block_table,
+                          const int32_t* context_lens, const int32_t* cu_seqlens,
+                          const int32_t* total_tier, float softmax_scale, void* out,
+                          int32_t* device_status, void* workspace, size_t workspace_bytes,
+                          bool lib_scratch, hipStream_t stream) {
   REQUIRE(B >= 1 && B <= 65535, "B must be in [1, 65535] (got %d)", B);
   REQUIRE(max_window >= 1, "max_window must be >= 1");
   REQUIRE(max_rows >= 1, "max_rows must be >= 1");
@@ -143,8 +147,18 @@ rva_status rva_verify_attention(int B, int max_window, int max_rows, int Hq, int
           "q, k_new, v_new, caches and out must be 16-byte aligned");
   (void)esz;
   const size_t need = rva::attention_workspace_bytes(B, max_window, Hq, Hkv, D, page_size, max_pages, kv_dtype);
+  if (lib_scratch) {
+    rva_status s = hip_result(rva::attention_scratch(&workspace, &workspace_bytes), name);
+    if (s != RVA_OK) return s;
+    if (need > workspace_bytes)
+      return fail(RVA_ERR_WORKSPACE_TOO_SMALL,
+                  "%s: this shape needs %zu bytes of scratch; the library's static scratch holds "
+                  "%zu (use rva_verify_attention with a workspace)",
+                  name, need, workspace_bytes);
+  }
   if (need > 0 && (workspace == nullptr || workspace_bytes < need))
-    return fail(RVA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+    return fail(RVA_ERR_WORKSPACE_TOO_SMALL, "%s: workspace needs %zu bytes (got %zu)", name, need,
+                workspace_bytes);
   REQUIRE(workspace == nullptr || aligned(workspace, 16), "workspace must be 16-byte aligned");
   rva::AttnArgs a;
   a.B = B;
@@ -172,7 +186,37 @@ rva_status rva_verify_attention(int B, int max_window, int max_rows, int Hq, int
   a.out = out;
   a.status = device_status;
   a.ws = workspace;
-  return hip_result(rva::launch_attention(a, kv_dtype, stream), "rva_verify_attention launch");
+  return hip_result(rva::launch_attention(a, kv_dtype, stream), name);
+}
+
+}  // namespace
+
+rva_status rva_verify_attention(int B, int max_window, int max_rows, int Hq, int Hkv, int D,
+                                int page_size, int num_pages, int max_pages, int kv_dtype,
+                                const void* q, const void* k_new, const void* v_new,
+                                void* k_cache, void* v_cache, const int32_t* block_table,
+                                const int32_t* context_lens, const int32_t* cu_seqlens,
+                                const int32_t* total_tier, float softmax_scale, void* out,
+                                int32_t* device_status, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
+  return attention_call("rva_verify_attention", B, max_window, max_rows, Hq, Hkv, D, page_size,
+                        num_pages, max_pages, kv_dtype, q, k_new, v_new, k_cache, v_cache,
+                        block_table, context_lens, cu_seqlens, total_tier, softmax_scale, out,
+                        device_status, workspace, workspace_bytes, false, stream);
+}
+
+rva_status rva_verify_attention_noalloc(int B, int max_window, int max_rows, int Hq, int Hkv,
+                                        int D, int page_size, int num_pages, int max_pages,
+                                        int kv_dtype, const void* q, const void* k_new,
+                                        const void* v_new, void* k_cache, void* v_cache,
+                                        const int32_t* block_table, const int32_t* context_lens,
+                                        const int32_t* cu_seqlens, const int32_t* total_tier,
+                                        float softmax_scale, void* out, int32_t* device_status,
+                                        hipStream_t stream) {
+  return attention_call("rva_verify_attention_noalloc", B, max_window, max_rows, Hq, Hkv, D,
+                        page_size, num_pages, max_pages, kv_dtype, q, k_new, v_new, k_cache,
+                        v_cache, block_table, context_lens, cu_seqlens, total_tier, softmax_scale,
+                        out, device_status, nullptr, 0, true, stream);
 }
 
 size_t rva_accept_workspace_size(int B, int gamma, int V, int max_rows) {

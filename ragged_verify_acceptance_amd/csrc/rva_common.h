@@ -95,6 +95,9 @@ struct AttnArgs {
 size_t attention_workspace_bytes(int B, int max_window, int Hq, int Hkv, int D, int page_size,
                                  int max_pages, int kv_dtype);
 hipError_t launch_attention(const AttnArgs& a, int kv_dtype, hipStream_t stream);
+// Device address and size of the library-owned attention scratch on the current device
+// (looked up once per device with hipGetSymbolAddress).
+hipError_t attention_scratch(void** ptr, size_t* bytes);
 
 struct AcceptArgs {
   int B, gamma, V, max_rows;

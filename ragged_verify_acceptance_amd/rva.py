@@ -33,7 +33,7 @@ _STATUS = {0: "RVA_OK", 1: "RVA_ERR_INVALID_ARGUMENT", 2: "RVA_ERR_UNSUPPORTED",
 
 EXPORTED = [
     "rva_schedule_windows", "rva_pack_ragged", "rva_verify_attention",
-    "rva_verify_attention_workspace_size", "rva_accept_and_commit",
+    "rva_verify_attention_workspace_size", "rva_verify_attention_noalloc", "rva_accept_and_commit",
     "rva_accept_workspace_size", "rva_confidence_labels", "rva_accept_capped", "rva_sts_fit",
     "rva_sts_fit_workspace_size", "rva_calibration_ece", "rva_calibration_ece_workspace_size",
     "rva_markov_sample", "rva_markov_workspace_size", "rva_last_error", "rva_version",
@@ -57,6 +57,8 @@ _SIGS = {
     "rva_verify_attention": [_i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p,
                              _p, _p, _f, _p, _p, _p, _z, _p],
     "rva_verify_attention_workspace_size": [_i, _i, _i, _i, _i, _i, _i, _i],
+    "rva_verify_attention_noalloc": [_i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p,
+                                     _p, _p, _p, _p, _f, _p, _p, _p],
     "rva_accept_and_commit": [_i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p,
                               _p, _p, _p, _z, _p],
     "rva_accept_workspace_size": [_i, _i, _i, _i],
@@ -174,6 +176,17 @@ def verify_attention(B, max_window, max_rows, Hq, Hkv, D, page_size, num_pages, 
         _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
         _ptr(context_lens), _ptr(cu_seqlens), _ptr(total_tier), float(softmax_scale), _ptr(out),
         _ptr(device_status), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def verify_attention_noalloc(B, max_window, max_rows, Hq, Hkv, D, page_size, num_pages, max_pages,
+                             q, k_new, v_new, k_cache, v_cache, block_table, context_lens,
+                             cu_seqlens, total_tier, softmax_scale, out, device_status=None,
+                             stream=None):
+    _check("rva_verify_attention_noalloc", lib().rva_verify_attention_noalloc(
+        B, max_window, max_rows, Hq, Hkv, D, page_size, num_pages, max_pages, dtype_code(q),
+        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+        _ptr(context_lens), _ptr(cu_seqlens), _ptr(total_tier), float(softmax_scale), _ptr(out),
+        _ptr(device_status), _stream(stream)))
 
 
 def accept_workspace_size(B, gamma, V, max_rows):

@@ -29,7 +29,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     L = rva.lib()
     names = declared_functions()
-    assert "rva_verify_attention" in names and len(names) == 16
+    assert "rva_verify_attention" in names and len(names) == 17
     for n in names:
         assert hasattr(L, n), f"{n} declared in rva.h but not exported"
     assert set(names) == set(rva.EXPORTED)
@@ -107,6 +107,24 @@ def test_attention_validation():
     assert _attn(ws=FAKE, ws_bytes=need - 1) == WS_SMALL
     # the float32 generic path needs no workspace
     assert rva.verify_attention_workspace_size(2, 6, 4, 2, 64, 16, 5, 0) == 0
+
+
+def _attn_noalloc(B=2, max_window=6, max_rows=16, Hq=32, Hkv=8, D=128, page=64, num_pages=10,
+                  max_pages=5, dtype=1, q=FAKE):
+    return rva.lib().rva_verify_attention_noalloc(B, max_window, max_rows, Hq, Hkv, D, page,
+                                                  num_pages, max_pages, dtype, q, FAKE, FAKE, FAKE,
+                                                  FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, None, None)
+
+
+def test_attention_noalloc_validation():
+    """The no-workspace variant validates its arguments before it looks up the library's
+    scratch, with the same codes as the workspace variant (no GPU needed for these)."""
+    assert _attn_noalloc(Hq=30) == INVALID
+    assert _attn_noalloc(D=96) == UNSUPPORTED
+    assert _attn_noalloc(max_window=17) == UNSUPPORTED
+    assert _attn_noalloc(dtype=5) == INVALID
+    assert _attn_noalloc(q=None) == INVALID
+    assert _attn_noalloc(q=ctypes.c_void_p(0x100002)) == INVALID
 
 
 def _accept(B=2, gamma=6, V=1024, dtype=1, max_rows=16, ws=FAKE, ws_bytes=None):
