@@ -263,7 +263,7 @@ def sts_bench(wl, steps, reps, cpu):
     g.manual_seed(wl.seed)
     sig = torch.tensor([wl.classes[b % len(wl.classes)].sigma for b in range(B)], device=dev)
     cu = torch.arange(0, B * gamma + 1, gamma, dtype=torch.int32, device=dev)
-    acc_ws = torch.empty(rva.accept_workspace_size(B, gamma, V, B * gamma), dtype=torch.uint8, device=dev)
+    acc_ws = torch.zeros(rva.accept_workspace_size(B, gamma, V, B * gamma), dtype=torch.uint8, device=dev)
     accept_len = torch.empty(B, dtype=torch.int32, device=dev)
     committed = torch.empty((B, gamma), dtype=torch.int32, device=dev)
     ctx = torch.zeros(B, dtype=torch.int32, device=dev)

@@ -96,7 +96,7 @@ def _accept_case(B, gamma, V, windows, seed, dtype=torch.bfloat16):
     pt = torch.empty((B, G1), dtype=torch.float32, device=DEV)
     pd = torch.empty((B, G1), dtype=torch.float32, device=DEV)
     lab = torch.empty((B, G1), dtype=torch.float32, device=DEV)
-    ws = torch.empty(rva.accept_workspace_size(B, gamma, V, max_rows), dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(rva.accept_workspace_size(B, gamma, V, max_rows), dtype=torch.uint8, device=DEV)
     status = torch.zeros(1, dtype=torch.int32, device=DEV)
     rva.accept_and_commit(B, gamma, V, max_rows, tl_t.to(DEV), dl_t.to(DEV), d(tokens), d(ua),
                           d(ur), d(cu), acc, com, ctx, pt, pd, lab, ws, status)
@@ -221,7 +221,7 @@ def test_accept_capped_edges(cap_kind):
     pt = torch.empty((B, G1), dtype=torch.float32, device=DEV)
     pd = torch.empty((B, G1), dtype=torch.float32, device=DEV)
     lab = torch.empty((B, G1), dtype=torch.float32, device=DEV)
-    ws = torch.empty(rva.accept_workspace_size(B, gamma, V, max_rows), dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(rva.accept_workspace_size(B, gamma, V, max_rows), dtype=torch.uint8, device=DEV)
     status = torch.zeros(1, dtype=torch.int32, device=DEV)
     rva.accept_capped(B, gamma, V, max_rows, tl_t.to(DEV), dl_t.to(DEV), d(tokens), d(ua), d(ur),
                       d(cu), d(caps), acc, full, com, ctx, pt, pd, lab, ws, status)
@@ -306,7 +306,7 @@ def test_accept_without_optional_outputs():
     ua = d(rng.random((B, G1)).astype(np.float32))
     ur = d(rng.random(B).astype(np.float32))
     ctx0 = rng.integers(10, 100, size=B).astype(np.int32)
-    ws = torch.empty(rva.accept_workspace_size(B, gamma, V, max_rows), dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(rva.accept_workspace_size(B, gamma, V, max_rows), dtype=torch.uint8, device=DEV)
     runs = []
     for full_outputs in (True, False):
         acc = torch.empty(B, dtype=torch.int32, device=DEV)

@@ -129,7 +129,7 @@ def test_accept_token_out_of_range():
     acc = torch.empty(B, dtype=torch.int32, device=DEV)
     com = torch.empty((B, gamma), dtype=torch.int32, device=DEV)
     ctx = d(ctx0)
-    ws = torch.empty(rva.accept_workspace_size(B, gamma, V, max_rows), dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(rva.accept_workspace_size(B, gamma, V, max_rows), dtype=torch.uint8, device=DEV)
     status = torch.zeros(1, dtype=torch.int32, device=DEV)
     rva.accept_and_commit(B, gamma, V, max_rows, tl.to(DEV), dl.to(DEV), d(tokens), d(ua), d(ur),
                           d(cu), acc, com, ctx, None, None, None, ws, status)

@@ -106,7 +106,7 @@ class DeviceStep:
         self.labels = torch.empty((B, G1), **f32)
         self.accept_len_full = torch.empty(B, **i32)  # cap-accept mode
         self.cap_windows = torch.empty(B, **i32)
-        self.acc_ws = torch.empty(rva.accept_workspace_size(B, gamma, wl.V, self.max_rows),
+        self.acc_ws = torch.zeros(rva.accept_workspace_size(B, gamma, wl.V, self.max_rows),
                                   dtype=torch.uint8, device=dev)
 
     # ------------------------------------------------------------------ calls
