@@ -81,8 +81,6 @@ typedef enum { RVA_MODE_COMPACT = 0, RVA_MODE_STATIC = 1 } rva_mode;
 #define RVA_DEV_BAD_CONTEXT  0x10 /* context_lens[b] < 0 or L + w beyond the page table */
 #define RVA_DEV_BAD_PAGE     0x20 /* block_table entry outside [0, num_pages)           */
 #define RVA_DEV_BAD_ROWS     0x40 /* packed rows beyond max_rows                        */
-#define RVA_DEV_TIMEOUT      0x80 /* a bounded wait between workgroups gave up (outputs of
-                                     the call are unspecified)                           */
 
 /*
  * Stage 1 -- rva_schedule_windows

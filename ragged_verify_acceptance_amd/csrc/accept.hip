@@ -1,52 +1,36 @@
-// Stages 4 and 5 in one pass over the logits: full-vocabulary speculative-sampling acceptance,
-// the residual / bonus draw, the commit, and the TV-distance confidence labels.
+// Stages 4 and 5: full-vocabulary speculative-sampling acceptance, the residual / bonus
+// draw, the commit, and the TV-distance confidence labels.
 //
 // Sources: "DSpark：投机解码与生产级 Serving 学习笔记" (sorenprojections.com) section 02
 // (the acceptance rule keeps the target distribution; acceptance is prefix-only) and
 // section 07 (label c* = 1 - 0.5 ||p_d - p_t||_1); "DFlash 到 DSpark in SGLang" section
 // "Background" (each verify forward also yields one target token).
 //
-// Work split.  An ITEM is one packed target row r < M (M = cu[B]): for a row that is not the
-// last of its request's window it is the PAIR (target row r, draft row of the same position),
-// otherwise the target row alone (the bonus row).  A row is cut into segments of 32 KB
-// (16384 bf16 / 8192 float32 entries) and a UNIT is one segment of an item: one workgroup of
-// 512 threads holds it in registers (4 x 16 B per thread and row) from its HBM read to the
-// end, so every logit is read from HBM once.
-//
-// The segments of one item form a TEAM.  After reading its unit, a workgroup posts the
-// segment statistics (max and float64 sum of exp(x - max), per row) and waits for the rest of
-// its team; every member then combines the same posted values in the same order, so all
-// of them hold identical row normalisers and take identical decisions.  Then, from the
-// registers:
-//   * the accept test of the pair's drafted token, u < min(1, p_t(x) / p_d(x)), in float64;
-//   * the segment's share of the label, sum min(p_t, p_d) = 1 - TV;
-//   * for the units that may carry the draw -- a pair whose own test rejects (it is the draw
-//     row when every earlier draft was accepted), or the bonus row of the window -- the
-//     float64 segment sums of the draw: S_t, S_d (exact normalisers), the unnormalised
-//     residual A(rho') = sum max(0, e_t - rho' e_d) and the draft mass D it keeps, at
-//     rho' = S_t / S_d of the float32-accurate normalisers (e = exp(x - max)).
-// The last workgroup of a request to finish (per-request counter) decides: accept length
-// from the posted test results, the residual or bonus draw, the segment holding u * Q (the
-// residual masses corrected to the exact rho to first order, A(rho) = A(rho') - (rho - rho')
-// D, exact but for entries whose sign differs between rho' and rho), then one exact float64
-// rescan of that segment (a re-read of 32 or 64 KB) and the commit; it also sums the label
-// shares.
-//
-// Exchange.  Every posted value is a 64-bit word (tag << 32 | payload), written and read with
-// relaxed agent-scope atomics, so a word is valid exactly when it carries this call's tag:
-// no counters guard the data, no fences, nothing to reset.  The tag is epoch + 1, the epoch
-// word of the workspace advanced by the last workgroup of the call (counters per 64
-// workgroups, then per call); the workspace must be zero before its first use with a shape.
-// Waits only ever point at units that are read before the waiter's own (same team, earlier
-// dispatch): posts never wait.  A wait gives up after 20 ms (RVA_DEV_TIMEOUT), so a kernel
-// always ends.
-//
-// Dispatch order.  Workgroups i, i+8, i+16, ... run on one XCD; an item's units take
-// consecutive places in one XCD's order (item k -> XCD k mod 8), so a team is dispatched
-// together and its exchange stays local.
-//
-// The draw returns an index that has to agree with a float64 definition, so everything it
-// reads is float64: exp is 2^y by range reduction, a 256-entry table of 2^(j/256) and a
+// Rows are cut into segments of kSeg vocabulary entries (32 KB of bf16).  Four kernels:
+//   stats_kernel    grid (segment, row): exact max m_s and sum of exp(x - m_s) of every
+//                   active row (float32 exp2, float32 runs of 8, float64 accumulation).  The
+//                   one full HBM pass over the logits.
+//   decide_kernel   one workgroup per request: row normalisers (max M, sum S) of the
+//                   request's rows from the segment stats, p_t(x) and p_d(x) at the drafted
+//                   tokens in float64, accept bits, first rejection, which rows the draw uses.
+//   pair_kernel_*   grid (segment, slot).  Draw slots (one per request, dispatched first):
+//                   float64 sums over the draw rows (target row n, and draft row n for a
+//                   residual draw) of e_t = exp(x_t - M_t), e_d = exp(x_d - M_d), and of the
+//                   unnormalised residual max(0, e_t - rho' e_d) with the draft entries it
+//                   keeps, at rho' = S_t / S_d from the float32-accurate stats; per segment
+//                   and per 512-entry sub-segment.  Pair slots: the segment's share of the
+//                   overlap sum min(p_t, p_d) = 1 - TV of every other draft pair, as
+//                   2^min(l_t, l_d) with l = (x - M) log2 e - log2 S (one float32
+//                   exponential per entry pair, float64 sum).
+//   pick_kernel     one workgroup per request: labels = the summed overlaps; the exact ratio
+//                   rho = S_t / S_d from the float64 sums corrects each residual mass to
+//                   first order, A(rho) = A(rho') - (rho - rho') D (exact up to the entries
+//                   whose sign differs between rho' and rho, a second-order term); u * Q
+//                   locates the segment, then the sub-segment, whose 512 entries are
+//                   rescanned with exact weights max(0, e_t - rho e_d) and a block-wide
+//                   prefix sum; then the commit (accept_len, committed, context_lens).
+// The draw returns an index that has to agree with a float64 definition, so everything the
+// draw reads is float64: exp is 2^y by range reduction, a 256-entry table of 2^(j/256) and a
 // degree-4 Taylor polynomial of 2^f on |f| <= 1/512 (about 1.5 ulp); the table itself and the
 // few other float64 exponentials use a degree-13 polynomial on |f| <= 1/2.
 #include <type_traits>
@@ -57,319 +41,513 @@
 namespace rva {
 namespace {
 
-constexpr int kNT = 512;                    // threads per workgroup
-constexpr int kWaves = kNT / kWave;
-constexpr int kVec = 4;                     // 16-byte vectors per thread and row
-constexpr int kSegBytes = kNT * kVec * 16;  // one row's part of a unit: 32 KB
-constexpr int kLanes = 8;                   // workgroups i, i + 8, ... share an XCD
-constexpr int kChunk = 8 * kLanes;          // workgroups per completion counter
-constexpr int kStatWords = 6;               // m_t, S_t (hi, lo), m_d, S_d (hi, lo)
-constexpr int kDrawWords = 10;              // S_t, S_d, A, D, rho' in float64 (hi, lo)
+constexpr int kSeg = 16384;
+constexpr int kThreads = 256;          // stats pass
+constexpr int kPer = kSeg / kThreads;  // entries per thread per segment in the stats pass
+constexpr int kWideThreads = 512;      // float64 passes (draw sums, pair pass)
+constexpr int kWidePer = kSeg / kWideThreads;
+constexpr int kSubLen = 512;                // sub-segment: what one wave covers per group
+constexpr int kSub = kSeg / kSubLen;         // sub-segments per segment
+constexpr int kPickThreads = kSubLen;        // the pick rescans one sub-segment, an entry a thread
+static_assert(kSubLen == 8 * kWave, "a wave's group of 8 entries per lane is one sub-segment");
+static_assert(kSub <= kWave, "the pick holds one sub-segment per lane");
 constexpr float kLog2e = 1.44269504088896341f;
-constexpr unsigned long long kWaitTicks = 2000000ull;  // 20 ms at the 100 MHz constant clock
 
+// e^(x - m) in float32 (x = -inf gives 0; m must be finite)
 __device__ __forceinline__ float exp_shift(float x, float m) {
   return __builtin_amdgcn_exp2f((x - m) * kLog2e);
 }
 
-// ------------------------------------------------------------------ tagged words
-__device__ __forceinline__ void put(uint64_t* p, uint32_t tag, uint32_t v) {
-  __hip_atomic_store(p, (uint64_t(tag) << 32) | v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void put_f64(uint64_t* p, uint32_t tag, double d) {
-  put(p, tag, uint32_t(__double2hiint(d)));
-  put(p + 1, tag, uint32_t(__double2loint(d)));
-}
-__device__ __forceinline__ uint64_t get(const uint64_t* p) {
-  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float payload_f32(uint64_t w) { return __uint_as_float(uint32_t(w)); }
-__device__ __forceinline__ double payload_f64(uint64_t hi, uint64_t lo) {
-  return __hiloint2double(int(uint32_t(hi)), int(uint32_t(lo)));
-}
-
-// values that are the same in every lane (read back from LDS) live in scalar registers
-__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
-__device__ __forceinline__ uint32_t uni(uint32_t v) { return uint32_t(__builtin_amdgcn_readfirstlane(int(v))); }
-__device__ __forceinline__ float uni(float v) { return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v))); }
-__device__ __forceinline__ double uni(double v) {
-  return __hiloint2double(__builtin_amdgcn_readfirstlane(__double2hiint(v)),
-                          __builtin_amdgcn_readfirstlane(__double2loint(v)));
-}
-
-// ------------------------------------------------------------------ workspace
-struct Control {
-  uint32_t epoch;   // tags of the current call are epoch + 1
-  uint32_t done;    // completed counter chunks of the current call
-  uint32_t giveup;  // set when a wait timed out: later waits return at once
+// Per-request decision record written by decide_kernel.
+struct Decision {
+  int n;         // accepted drafts; -1: request skipped (invalid window)
+  int id_t;      // row id of the draw's target row
+  int id_d;      // row id of the residual draw's draft row, -1 for the bonus draw
+  int pad;
+  float Mt, Md;  // maxima of those rows
+  double rho32;  // S_t / S_d from the float32-accurate segment stats
 };
+
+// Float64 per-segment sums of a draw slot: S_t, S_d, A(rho'), D (see the header); per
+// sub-segment: S_t, A(rho'), D.
+constexpr int kDrawSums = 4;
+constexpr int kSubSums = 3;
 
 struct WsLayout {
-  int nseg, n_chunks;
-  size_t off_ctl, off_req, off_chunk, off_stat, off_bit, off_share, off_draw, total;
+  int nseg, n_ids;
+  size_t off_m, off_s, off_nm, off_tv, off_dec, off_r1, off_sub, total;
 };
 
-__host__ __device__ inline int seg_len_entries(int elem_bytes) { return kSegBytes / elem_bytes; }
-
-__host__ __device__ inline WsLayout ws_layout(int B, int gamma, int V, int max_rows, int elem_bytes) {
-  (void)gamma;
+__host__ __device__ inline WsLayout ws_layout(int B, int gamma, int V, int max_rows) {
   WsLayout w;
-  const int len = seg_len_entries(elem_bytes);
-  w.nseg = (V + len - 1) / len;
-  const long long grid = (long long)kLanes * w.nseg * ((max_rows + kLanes - 1) / kLanes);
-  w.n_chunks = int((grid + kChunk - 1) / kChunk);
+  w.nseg = (V + kSeg - 1) / kSeg;
+  const int G1 = gamma - 1;
+  w.n_ids = max_rows + B * G1;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
     off += (bytes + 255) & ~size_t(255);
     return o;
   };
-  w.off_ctl = take(sizeof(Control));
-  w.off_req = take(sizeof(uint32_t) * size_t(B));
-  w.off_chunk = take(sizeof(uint32_t) * size_t(w.n_chunks));
-  w.off_stat = take(sizeof(uint64_t) * size_t(max_rows) * w.nseg * kStatWords);
-  w.off_bit = take(sizeof(uint64_t) * size_t(max_rows));
-  w.off_share = take(sizeof(uint64_t) * size_t(max_rows) * w.nseg);
-  w.off_draw = take(sizeof(uint64_t) * size_t(max_rows) * w.nseg * kDrawWords);
+  w.off_m = take(sizeof(float) * size_t(w.n_ids) * w.nseg);
+  w.off_s = take(sizeof(double) * size_t(w.n_ids) * w.nseg);
+  w.off_nm = take(sizeof(float2) * size_t(w.n_ids));
+  w.off_tv = take(sizeof(double) * size_t(B) * G1 * w.nseg);
+  w.off_dec = take(sizeof(Decision) * size_t(B));
+  w.off_r1 = take(sizeof(double) * size_t(B) * w.nseg * kDrawSums);
+  w.off_sub = take(sizeof(double) * size_t(B) * w.nseg * kSub * kSubSums);
   w.total = off;
   return w;
 }
 
+// Row ids: target row r (packed row index) is id r; draft row (b, k) is id max_rows + b*G1 + k.
 struct Ctx {
   AcceptArgs a;
   Exp2Poly P;
   WsLayout L;
-  Control* ctl;
-  uint32_t* req_cnt;   // [B] workgroups of the request that have finished
-  uint32_t* chunk;     // [n_chunks] workgroups of the chunk that have finished
-  uint64_t* stat;      // [max_rows][nseg][kStatWords]
-  uint64_t* bit;       // [max_rows]: the pair's accept test (1 = rejected)
-  uint64_t* share;     // [max_rows][nseg]: label share (float32 payload)
-  uint64_t* draw;      // [max_rows][nseg][kDrawWords]
-  int commit;          // 0: labels only
+  float* st_m;    // [n_ids][nseg] segment maxima
+  double* st_s;   // [n_ids][nseg] segment sums of exp(x - m_s)
+  float2* nm;     // [n_ids] (row max, 1 / row sum) of the rows decide_kernel covered
+  double* tv;     // [B*G1][nseg] segment shares of the overlap sum min(p_t, p_d) = 1 - TV
+  Decision* dec;  // [B]
+  double* r1;     // [B][nseg][kDrawSums] float64 sums of the draw slots
+  double* sub;    // [B][nseg][kSub][kSubSums] the same per sub-segment
 };
 
-// ------------------------------------------------------------------ a thread's share of a unit
+// Request b's packed rows [cu[b], cu[b] + w) lie inside [0, max_rows) and w in [1, gamma].
+__device__ __forceinline__ bool req_ok(const Ctx& c, int b) {
+  const int r0 = c.a.cu[b], r1 = c.a.cu[b + 1];
+  return r0 >= 0 && r1 - r0 >= 1 && r1 - r0 <= c.a.gamma && r1 <= c.a.max_rows;
+}
+
 template <typename T>
-struct Seg {
-  static constexpr int kEpv = 16 / int(sizeof(T));    // entries per vector: 8 bf16, 4 float32
-  static constexpr int kLen = kSegBytes / int(sizeof(T));
-  static constexpr int kPer = kVec * kEpv;            // entries per thread
-  uint4 v[kVec];
+__device__ __forceinline__ const T* row_ptr(const Ctx& c, int id) {
+  if (id < c.a.max_rows) return static_cast<const T*>(c.a.target) + size_t(id) * c.a.V;
+  return static_cast<const T*>(c.a.draft) + size_t(id - c.a.max_rows) * c.a.V;
+}
 
-  __device__ __forceinline__ static uint32_t comp(const uint4& q, int k) {
-    return k == 0 ? q.x : k == 1 ? q.y : k == 2 ? q.z : q.w;
+// A thread's share (kSeg / NT entries) of one segment, kept as loaded: bf16 as packed pairs
+// (half the registers of float32), float32 as is.  Entry q = 8 g + j of thread t is
+// segment entry g * 8 NT + 8 t + j, so for each group g a wave covers 512 consecutive
+// entries (sub-segment 8 g NT / 512 + wave).  Entries past the row end read as -inf.
+template <typename T, int NT>
+struct SegData;
+
+template <int NT>
+struct SegData<uint16_t, NT> {
+  static constexpr int P = kSeg / NT;
+  uint32_t w[P / 2];
+  __device__ __forceinline__ float operator[](int q) const {
+    return (q & 1) ? __uint_as_float(w[q >> 1] & 0xffff0000u) : __uint_as_float(w[q >> 1] << 16);
   }
-  // entry e (< kEpv) of vector i; the thread's vector i holds segment entries
-  // (i * kNT + threadIdx.x) * kEpv + e
-  __device__ __forceinline__ float at(int i, int e) const {
-    if constexpr (std::is_same<T, uint16_t>::value) {
-      const uint32_t w = comp(v[i], e >> 1);
-      return (e & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
-    } else {
-      return __uint_as_float(comp(v[i], e));
-    }
-  }
-  __device__ __forceinline__ static int index(int seg, int i, int e) {
-    return seg * kLen + (i * kNT + int(threadIdx.x)) * kEpv + e;
-  }
-  // entries past the row end read as -inf
-  __device__ __forceinline__ void load(const T* row, int V, int seg, bool vec_ok) {
+  __device__ __forceinline__ void load(const uint16_t* row, int V, int seg) {
+    constexpr uint32_t kNegInf2 = 0xff80ff80u;  // two bf16 -inf
+    const int base = seg * kSeg + int(threadIdx.x) * 8;
+    if (V % 8 == 0) {
 #pragma unroll
-    for (int i = 0; i < kVec; ++i) {
-      const int base = index(seg, i, 0);
-      if (vec_ok && base + kEpv <= V) {
-        v[i] = *reinterpret_cast<const uint4*>(row + base);
-      } else {
-        uint32_t w[4];
-        if constexpr (std::is_same<T, uint16_t>::value) {
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const uint32_t lo = base + 2 * k < V ? row[base + 2 * k] : 0xff80u;
-            const uint32_t hi = base + 2 * k + 1 < V ? row[base + 2 * k + 1] : 0xff80u;
-            w[k] = lo | (hi << 16);
-          }
+      for (int g = 0; g < P / 8; ++g) {
+        const int v = base + g * 8 * NT;
+        if (v < V) {
+          const uint4 u = *reinterpret_cast<const uint4*>(row + v);
+          w[4 * g] = u.x;
+          w[4 * g + 1] = u.y;
+          w[4 * g + 2] = u.z;
+          w[4 * g + 3] = u.w;
         } else {
-#pragma unroll
-          for (int k = 0; k < 4; ++k) w[k] = base + k < V ? __float_as_uint(row[base + k]) : 0xff800000u;
+          w[4 * g] = w[4 * g + 1] = w[4 * g + 2] = w[4 * g + 3] = kNegInf2;
         }
-        v[i] = make_uint4(w[0], w[1], w[2], w[3]);
       }
+    } else {
+#pragma unroll
+      for (int g = 0; g < P / 8; ++g)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int v = base + g * 8 * NT + 2 * k;
+          const uint32_t lo = v < V ? row[v] : 0xff80u;
+          const uint32_t hi = v + 1 < V ? row[v + 1] : 0xff80u;
+          w[4 * g + k] = lo | (hi << 16);
+        }
     }
   }
-  // keeps the widened values from being held across phases (they are one instruction each)
-  __device__ __forceinline__ void touch() {
+};
+
+template <int NT>
+struct SegData<float, NT> {
+  static constexpr int P = kSeg / NT;
+  float f[P];
+  __device__ __forceinline__ float operator[](int q) const { return f[q]; }
+  __device__ __forceinline__ void load(const float* row, int V, int seg) {
+    const int base = seg * kSeg + int(threadIdx.x) * 8;
+    if (V % 4 == 0) {
 #pragma unroll
-    for (int i = 0; i < kVec; ++i) touch(i);
-  }
-  __device__ __forceinline__ void touch(int i) {
-    asm volatile("" : "+v"(v[i].x), "+v"(v[i].y), "+v"(v[i].z), "+v"(v[i].w));
+      for (int g = 0; g < P / 8; ++g)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int v = base + g * 8 * NT + 4 * h;
+          float4 u = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+          if (v < V) u = *reinterpret_cast<const float4*>(row + v);
+          f[8 * g + 4 * h] = u.x;
+          f[8 * g + 4 * h + 1] = u.y;
+          f[8 * g + 4 * h + 2] = u.z;
+          f[8 * g + 4 * h + 3] = u.w;
+        }
+    } else {
+#pragma unroll
+      for (int g = 0; g < P / 8; ++g)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int v = base + g * 8 * NT + j;
+          f[8 * g + j] = v < V ? row[v] : -INFINITY;
+        }
+    }
   }
 };
 
-// ------------------------------------------------------------------ block reductions
-struct Shared {
-  float f[kWaves];
-  double d[kWaves][5];
-  double tab[256];
-  // item description and decisions, broadcast by wave 0
-  int M, b, r0, w, cap, item_ok, last;
-  float Mt, Md;
-  double St, Sd;
-  float it, id;  // 1 / S in float32 (labels)
-  int reject;
-  // pick
-  double t, base, rho;
-  int seg, residual, n, n_full, y, ylast;
-};
-
-__device__ __forceinline__ float block_max(float v, Shared& sh) {
+template <int NT>
+__device__ __forceinline__ float block_max(float v, float* sm) {
   v = wave_max(v);
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   __syncthreads();
-  if (lane == 0) sh.f[wave] = v;
+  if (lane == 0) sm[wave] = v;
   __syncthreads();
-  float r = sh.f[0];
+  float r = sm[0];
 #pragma unroll
-  for (int i = 1; i < kWaves; ++i) r = fmaxf(r, sh.f[i]);
+  for (int i = 1; i < NT / kWave; ++i) r = fmaxf(r, sm[i]);
   return r;
 }
 
-// float64 sums of N values in a fixed order (wave butterfly, then the wave totals in order);
-// every thread gets the results
+// float64 sum in a fixed order (wave butterfly, then the wave totals in order); every thread
+// receives the same value.
+template <int NT>
+__device__ __forceinline__ double block_sum_f64(double v, double* sm) {
+  v = wave_sum_f64(v);
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  __syncthreads();
+  if (lane == 0) sm[wave] = v;
+  __syncthreads();
+  double r = sm[0];
+#pragma unroll
+  for (int i = 1; i < NT / kWave; ++i) r += sm[i];
+  return r;
+}
+
+// Draw-row totals S_t, S_d over all segments: one wave, lanes over segments, butterfly sum
+// (every lane gets the same value).
+__device__ __forceinline__ void draw_totals(const Ctx& c, int b, double& St, double& Sd) {
+  const int lane = threadIdx.x % kWave;
+  double st = 0.0, sd = 0.0;
+  for (int s = lane; s < c.L.nseg; s += kWave) {
+    const double* r = c.r1 + (size_t(b) * c.L.nseg + s) * kDrawSums;
+    st += r[0];
+    sd += r[1];
+  }
+  St = wave_sum_f64(st);
+  Sd = wave_sum_f64(sd);
+}
+
+// Draw mass of segment s: the residual A(rho) (first-order corrected, clamped at 0) or the
+// target mass S_t of the segment (bonus draw and the all-zero-residual fallback).
+__device__ __forceinline__ double seg_mass(const Ctx& c, int b, int s, bool residual, double drho) {
+  const double* r = c.r1 + (size_t(b) * c.L.nseg + s) * kDrawSums;
+  if (!residual) return r[0];
+  const double m = r[2] - drho * r[3];
+  return m > 0.0 ? m : 0.0;
+}
+
+// Draw mass of sub-segment u of segment s (same rule as seg_mass).
+__device__ __forceinline__ double sub_mass(const Ctx& c, int b, int s, int u, bool residual,
+                                           double drho) {
+  const double* r = c.sub + ((size_t(b) * c.L.nseg + s) * kSub + u) * kSubSums;
+  if (!residual) return r[0];
+  const double m = r[1] - drho * r[2];
+  return m > 0.0 ? m : 0.0;
+}
+
+// ------------------------------------------------------------------ stats
+__device__ __forceinline__ bool id_active(const Ctx& c, int id) {
+  if (id < c.a.max_rows) return id < c.a.cu[c.a.B];
+  const int j = id - c.a.max_rows, G1 = c.a.gamma - 1;
+  const int b = j / G1, k = j % G1;
+  return req_ok(c, b) && k < c.a.cu[b + 1] - c.a.cu[b] - 1;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void stats_kernel(Ctx c) {
+  __shared__ float smf[kThreads / kWave];
+  __shared__ double smd[kThreads / kWave];
+  const int seg = blockIdx.x, id = blockIdx.y;
+  if (!id_active(c, id)) return;
+  SegData<T, kThreads> x;
+  x.load(row_ptr<T>(c, id), c.a.V, seg);
+  float m = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) m = fmaxf(m, x[i]);
+  m = block_max<kThreads>(m, smf);
+  const float ms = m == -INFINITY ? 0.f : m;  // fully masked segment: every term is 0
+  double s = 0.0;
+#pragma unroll
+  for (int i = 0; i < kPer; i += 8) {
+    float run = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) run += exp_shift(x[i + j], ms);
+    s += double(run);
+  }
+  s = block_sum_f64<kThreads>(s, smd);
+  if (threadIdx.x == 0) {
+    c.st_m[size_t(id) * c.L.nseg + seg] = m;
+    c.st_s[size_t(id) * c.L.nseg + seg] = s;
+  }
+}
+
+// ------------------------------------------------------------------ decide
+constexpr int kDecideThreads = 512;
+
+// Row rr of request b in decide order: target rows 0..w-1, then draft rows 0..w-2.
+__device__ __forceinline__ int decide_row_id(const Ctx& c, int b, int r0, int w, int rr) {
+  return rr < w ? r0 + rr : c.a.max_rows + b * (c.a.gamma - 1) + (rr - w);
+}
+
+template <typename T>
+__global__ __launch_bounds__(kDecideThreads) void decide_kernel(Ctx c, int commit) {
+  __shared__ float sM[2 * 64];
+  __shared__ double sS[2 * 64];
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int G1 = c.a.gamma - 1;
+  // wave 0, lane k: the drafted token and its uniform are loaded before the window is known
+  // (they do not depend on it), so that only the logit loads wait for cu_seqlens
+  int x = 0;
+  float u = 0.f;
+  if (commit && wave == 0 && lane < G1) {
+    x = c.a.tokens[size_t(b) * G1 + lane];
+    u = c.a.u_acc[size_t(b) * G1 + lane];
+  }
+  if (!req_ok(c, b)) {
+    if (tid == 0) {
+      flag(c.a.status, RVA_DEV_BAD_WINDOW);
+      if (commit) c.dec[b].n = -1;
+    }
+    return;
+  }
+  const int r0 = c.a.cu[b];
+  const int w = c.a.cu[b + 1] - r0;
+  // wave 0, lane k < w-1: issue the drafted token's logit loads before the stats sweep
+  float lt = 0.f, ld = 0.f;
+  if (commit && wave == 0 && lane < w - 1) {
+    const size_t o = size_t(b) * G1 + lane;
+    if (x < 0 || x >= c.a.V) {
+      flag(c.a.status, RVA_DEV_BAD_TOKEN);
+      x = x < 0 ? 0 : c.a.V - 1;
+    }
+    lt = Elem<T>::load(row_ptr<T>(c, r0 + lane), x);
+    ld = Elem<T>::load(row_ptr<T>(c, c.a.max_rows + int(o)), x);
+  }
+  // row normalisers: one wave per row, lanes over segments
+  const int nrows = 2 * w - 1;
+  for (int rr = wave; rr < nrows; rr += kDecideThreads / kWave) {
+    const int id = decide_row_id(c, b, r0, w, rr);
+    const float* rm = c.st_m + size_t(id) * c.L.nseg;
+    const double* rs = c.st_s + size_t(id) * c.L.nseg;
+    float m = -INFINITY;
+    for (int s = lane; s < c.L.nseg; s += kWave) m = fmaxf(m, rm[s]);
+    m = wave_max(m);
+    double acc = 0.0;
+    for (int s = lane; s < c.L.nseg; s += kWave) acc += rs[s] * exp_shift_f64(c.P, rm[s], m);
+    acc = wave_sum_f64(acc);
+    if (lane == 0) {
+      sM[rr] = m;
+      sS[rr] = acc;
+      c.nm[id] = make_float2(m, float(1.0 / acc));
+    }
+  }
+  if (!commit) return;
+  __syncthreads();
+  if (wave != 0) return;
+  const float qnan = __int_as_float(0x7fc00000);
+  bool reject = false;
+  if (lane < G1) {
+    const size_t o = size_t(b) * G1 + lane;
+    if (lane < w - 1) {
+      const double pt = exp_shift_f64(c.P, lt, sM[lane]) / sS[lane];
+      const double pd = exp_shift_f64(c.P, ld, sM[w + lane]) / sS[w + lane];
+      if (c.a.pt_at) c.a.pt_at[o] = float(pt);
+      if (c.a.pd_at) c.a.pd_at[o] = float(pd);
+      const double r = pd == 0.0 ? INFINITY : pt / pd;
+      reject = !(double(u) < (r < 1.0 ? r : 1.0));
+    } else {
+      if (c.a.pt_at) c.a.pt_at[o] = qnan;
+      if (c.a.pd_at) c.a.pd_at[o] = qnan;
+    }
+  }
+  // first rejected draft (G1 <= 63: one lane per draft)
+  const unsigned long long rej = __ballot(reject);
+  const int n_full = rej ? __ffsll(rej) - 1 : w - 1;
+  // cap-accept: the whole block was verified, but only drafts inside the window (cap - 1 of
+  // them) may be committed; a rejection inside the window draws its residual, otherwise the
+  // bonus comes from the window's last target row -- what compact mode does for that window
+  int cap = w;
+  if (c.a.cap) {
+    cap = c.a.cap[b];
+    if (cap < 1 || cap > w) {
+      if (lane == 0) flag(c.a.status, RVA_DEV_BAD_WINDOW);
+      cap = cap < 1 ? 1 : w;
+    }
+  }
+  const bool residual = n_full < cap - 1;
+  const int n = residual ? n_full : cap - 1;
+  if (lane == 0) {
+    Decision d;
+    d.n = n;
+    d.id_t = r0 + n;
+    d.id_d = residual ? c.a.max_rows + b * G1 + n : -1;
+    d.pad = 0;
+    d.Mt = sM[n];
+    d.Md = residual ? sM[w + n] : 0.f;
+    d.rho32 = residual ? sS[n] / sS[w + n] : 0.0;
+    c.dec[b] = d;
+    if (c.a.accept_len_full) c.a.accept_len_full[b] = n_full;
+  }
+}
+
+// ------------------------------------------------------------------ pair pass
+// Wave butterfly then wave totals in order, for N sums at once; thread 0 gets the results.
 template <int N>
-__device__ __forceinline__ void block_sums(double (&v)[N], Shared& sh) {
-  static_assert(N <= 5, "");
+__device__ __forceinline__ void block_sums_f64(double (&v)[N], double (*sm)[N]) {
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
 #pragma unroll
   for (int q = 0; q < N; ++q) v[q] = wave_sum_f64(v[q]);
-  __syncthreads();
   if (lane == 0)
 #pragma unroll
-    for (int q = 0; q < N; ++q) sh.d[wave][q] = v[q];
+    for (int q = 0; q < N; ++q) sm[wave][q] = v[q];
   __syncthreads();
+  if (threadIdx.x == 0)
 #pragma unroll
-  for (int q = 0; q < N; ++q) {
-    double r = sh.d[0][q];
-#pragma unroll
-    for (int i = 1; i < kWaves; ++i) r += sh.d[i][q];
-    v[q] = r;
-  }
+    for (int q = 0; q < N; ++q) {
+      double r = sm[0][q];
+      for (int i = 1; i < kWideThreads / kWave; ++i) r += sm[i][q];
+      v[q] = r;
+    }
 }
 
-// max and float64 sum of exp(x - max) of a thread-distributed segment (float32 exponentials
-// in runs of 8, float64 accumulation)
+// blockIdx.y < draw_slots: the draw slot of request blockIdx.y (float64-heavy, dispatched
+// first); above: draft pair (blockIdx.y - draw_slots) = b*G1 + k for the labels (when per_pair).
 template <typename T>
-__device__ __forceinline__ void seg_stats(Seg<T>& s, Shared& sh, float& m, double& S) {
-  float mt = -INFINITY;
+__device__ __forceinline__ void pair_body(const Ctx& c, int draw_slots, int per_pair) {
+  __shared__ double sm[kWideThreads / kWave][kDrawSums + 1];
+  __shared__ double smd[kWideThreads / kWave];
+  const int seg = blockIdx.x;
+  const int G1 = c.a.gamma - 1;
+  const int y = blockIdx.y;
+  if (y < draw_slots) {
+    const int b = y;
+    const Decision d = c.dec[b];
+    if (d.n < 0) return;
+    const bool residual = d.id_d >= 0;
+    const bool lab = per_pair && residual;  // this pair's overlap share is taken here too
+    SegData<T, kWideThreads> xt, xd;
+    xt.load(row_ptr<T>(c, d.id_t), c.a.V, seg);
+    double v[kDrawSums + 1] = {0.0, 0.0, 0.0, 0.0, 0.0};
+    double it = 0.0, id = 0.0;
+    if (residual) xd.load(row_ptr<T>(c, d.id_d), c.a.V, seg);
+    __shared__ double tab[256];
+    fill_exp2_tab(c.P, tab);  // overlaps the row loads
+    if (lab) {
+      it = double(c.nm[d.id_t].y);
+      id = double(c.nm[d.id_d].y);
+    }
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    double* subp = c.sub + (size_t(b) * c.L.nseg + seg) * kSub * kSubSums;
 #pragma unroll
-  for (int i = 0; i < kVec; ++i) {
+    for (int g = 0; g < kWidePer / 8; ++g) {
+      double gs[kSubSums] = {0.0, 0.0, 0.0};
 #pragma unroll
-    for (int e = 0; e < Seg<T>::kEpv; ++e) mt = fmaxf(mt, s.at(i, e));
-    s.touch(i);
+      for (int j = 0; j < 8; ++j) {
+        const double et = exp_shift_tab(c.P, tab, xt[8 * g + j], d.Mt);
+        gs[0] += et;
+        if (residual) {
+          const double ed = exp_shift_tab(c.P, tab, xd[8 * g + j], d.Md);
+          v[1] += ed;
+          const double r = et - d.rho32 * ed;
+          if (r > 0.0) {
+            gs[1] += r;
+            gs[2] += ed;
+          }
+          v[4] += fmin(et * it, ed * id);  // overlap min(p_t, p_d)
+        }
+      }
+      v[0] += gs[0];
+      v[2] += gs[1];
+      v[3] += gs[2];
+#pragma unroll
+      for (int q = 0; q < kSubSums; ++q) gs[q] = wave_sum_f64(gs[q]);
+      if (lane == 0)
+#pragma unroll
+        for (int q = 0; q < kSubSums; ++q) subp[(g * (kWideThreads / kWave) + wave) * kSubSums + q] = gs[q];
+    }
+    block_sums_f64<kDrawSums + 1>(v, sm);
+    if (threadIdx.x == 0) {
+      double* r = c.r1 + (size_t(b) * c.L.nseg + seg) * kDrawSums;
+#pragma unroll
+      for (int q = 0; q < kDrawSums; ++q) r[q] = v[q];
+      if (lab) c.tv[(size_t(b) * G1 + d.n) * c.L.nseg + seg] = v[4];
+    }
+    return;
   }
-  m = block_max(mt, sh);
-  const float ms = m == -INFINITY ? 0.f : m;  // fully masked segment: every term is 0
+  const int j = y - draw_slots;
+  const int b = j / G1, k = j % G1;
+  if (!req_ok(c, b)) return;
+  if (k >= c.a.cu[b + 1] - c.a.cu[b] - 1) return;
+  if (draw_slots > 0) {
+    const Decision d = c.dec[b];
+    if (d.id_d >= 0 && d.n == k) return;  // done by the draw slot
+  }
+  const int id_t = c.a.cu[b] + k;
+  const int id_d = c.a.max_rows + b * G1 + k;
+  SegData<T, kWideThreads> xt, xd;
+  xt.load(row_ptr<T>(c, id_t), c.a.V, seg);
+  xd.load(row_ptr<T>(c, id_d), c.a.V, seg);
+  const float2 nt = c.nm[id_t], nd = c.nm[id_d];
+  // min(p_t, p_d) = 2^min(lt, ld) with l = (x - M) log2 e - log2 S = x log2 e + c,
+  // c = -(M log2 e + log2 S): one FMA per entry and one exponential per entry pair (the label
+  // is the segment sums of these overlaps).  Forming l from x log2 e instead of (x - M) log2 e
+  // moves it by a few float32 ulp of |x log2 e| (< 30 for logits of magnitude < 20), a
+  // relative change of about 1e-6 in each term.
+  const float ct = -fmaf(nt.x, kLog2e, -__log2f(nt.y));  // nm.y = 1 / S
+  const float cd = -fmaf(nd.x, kLog2e, -__log2f(nd.y));
   double acc = 0.0;
-  float run = 0.f;
 #pragma unroll
-  for (int i = 0; i < kVec; ++i) {
+  for (int i = 0; i < kWidePer; i += 8) {
+    float run = 0.f;
 #pragma unroll
-    for (int e = 0; e < Seg<T>::kEpv; ++e) {
-      run += exp_shift(s.at(i, e), ms);
-      if (((i * Seg<T>::kEpv + e) & 7) == 7) {
-        acc += double(run);
-        run = 0.f;
-      }
+    for (int u = 0; u < 8; ++u) {
+      const float lt = fmaf(xt[i + u], kLog2e, ct);
+      const float ld = fmaf(xd[i + u], kLog2e, cd);
+      run += __builtin_amdgcn_exp2f(fminf(lt, ld));
     }
-    s.touch(i);
+    acc += double(run);
   }
-  double v[1] = {acc};
-  block_sums<1>(v, sh);
-  S = v[0];
+  acc = block_sum_f64<kWideThreads>(acc, smd);
+  if (threadIdx.x == 0) c.tv[(size_t(b) * G1 + k) * c.L.nseg + seg] = acc;
 }
 
-// ------------------------------------------------------------------ waiting for words
-// Each lane with `mine` waits until its word carries the tag; one wave calls this (wave-uniform
-// loop, no barrier inside).  Gives up after kWaitTicks (sets giveup and RVA_DEV_TIMEOUT).
-__device__ __forceinline__ uint64_t wait_word(Control* ctl, int32_t* status, uint32_t tag,
-                                              const uint64_t* p, bool mine) {
-  uint64_t w = mine ? get(p) : 0;
-  if (__all(!mine || uint32_t(w >> 32) == tag)) return w;
-  const unsigned long long t0 = wall_clock64();
-  while (__any(mine && uint32_t(w >> 32) != tag)) {
-    if (__hip_atomic_load(&ctl->giveup, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) break;
-    if (wall_clock64() - t0 > kWaitTicks) {
-      if ((threadIdx.x % kWave) == 0) {
-        atomicOr(&ctl->giveup, 1u);
-        flag(status, RVA_DEV_TIMEOUT);
-      }
-      break;
-    }
-    __builtin_amdgcn_s_sleep(1);
-    if (mine && uint32_t(w >> 32) != tag) w = get(p);
-  }
-  return w;
+// bfloat16 rows: 8 waves per SIMD (64 VGPRs), four workgroups per CU, so that one computing
+// still leaves three streaming (the draw slots' float64 path spills a few registers to
+// scratch).  float32 rows hold twice the registers and keep the default.
+__global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) void pair_kernel_bf16(
+    Ctx c, int draw_slots, int per_pair) {
+  pair_body<uint16_t>(c, draw_slots, per_pair);
+}
+__global__ __launch_bounds__(kWideThreads) void pair_kernel_f32(Ctx c, int draw_slots, int per_pair) {
+  pair_body<float>(c, draw_slots, per_pair);
 }
 
-// Row normalisers of an item from its team's posted statistics (wave 0; every lane gets them).
-// The order of combination is fixed, so every caller obtains the same bits.
-__device__ __forceinline__ void team_normalisers(Control* ctl, int32_t* status, const Exp2Poly& P,
-                                                 const uint64_t* stat, int nseg, uint32_t tag,
-                                                 int item, bool pair, float& Mt, double& St,
-                                                 float& Md, double& Sd) {
-  const int lane = threadIdx.x % kWave;
-  const uint64_t* base = stat + size_t(item) * nseg * kStatWords;
-  const int nw = pair ? kStatWords : 3;
-  // wait until every word is there (lanes over words, 64 at a time)
-  for (int k0 = 0; k0 < nseg * kStatWords; k0 += kWave) {
-    const int k = k0 + lane;
-    const bool mine = k < nseg * kStatWords && (k % kStatWords) < nw;
-    wait_word(ctl, status, tag, base + k, mine);
-  }
-  float mt = -INFINITY, md = -INFINITY;
-  for (int s = lane; s < nseg; s += kWave) {
-    mt = fmaxf(mt, payload_f32(get(base + s * kStatWords)));
-    if (pair) md = fmaxf(md, payload_f32(get(base + s * kStatWords + 3)));
-  }
-  Mt = wave_max(mt);
-  Md = wave_max(md);
-  double at = 0.0, ad = 0.0;
-  for (int s = lane; s < nseg; s += kWave) {
-    const uint64_t* q = base + s * kStatWords;
-    at += payload_f64(get(q + 1), get(q + 2)) * exp_shift_f64(P, payload_f32(get(q)), Mt);
-    if (pair) ad += payload_f64(get(q + 4), get(q + 5)) * exp_shift_f64(P, payload_f32(get(q + 3)), Md);
-  }
-  St = wave_sum_f64(at);
-  Sd = wave_sum_f64(ad);
-}
-
-// wave-parallel search of the request holding packed row r: the largest b with cu[b] <= r
-// (cu non-decreasing); every lane gets it
-__device__ __forceinline__ int find_request(const int32_t* cu, int B, int r) {
-  const int lane = threadIdx.x % kWave;
-  int lo = 0, n = B;
-  while (n > 1) {
-    const int step = (n - 1 + kWave - 1) / kWave;
-    const int k = lo + 1 + lane * step;
-    const bool le = k < lo + n && cu[k] <= r;
-    const int cnt = __popcll(__ballot(le));
-    if (cnt == 0) {
-      n = 1;
-    } else {
-      const int nlo = lo + 1 + (cnt - 1) * step;
-      n = min(step, lo + n - nlo);
-      lo = nlo;
-    }
-  }
-  return lo;
-}
-
-// One wave: the first of n items (masses >= 0, in index order) at which the running sum,
-// started at `start`, passes t; `base` = the running sum before it.  If rounding leaves t
-// unpassed, the last item with mass (or item 0).
+// ------------------------------------------------------------------ pick + commit + labels
+// One wave: the first of n items (masses mass(i) >= 0, in index order) at which the running
+// sum, started at `start`, passes t; `found` = that item and `base` = the running sum before
+// it.  If rounding leaves t unpassed, the last item with mass (or item 0).
 template <typename F>
-__device__ __forceinline__ void locate(double t, double start, int n, F mass, int& found, double& base) {
+__device__ __forceinline__ void locate(double t, double start, int n, F mass, int& found,
+                                       double& base) {
   const int lane = threadIdx.x % kWave;
   int last = 0;
   double base_last = start, carry = start;
@@ -406,466 +584,215 @@ __device__ __forceinline__ void locate(double t, double start, int n, F mass, in
   }
 }
 
-// ------------------------------------------------------------------ the pick (last arriver)
-// What the pick needs, staged in LDS by the workgroup that runs it (the pick is a separate,
-// not inlined function, so that its registers do not weigh on the streaming path).
-struct PickCtx {
-  const void* target;
-  const void* draft;
-  const int32_t* tokens;
-  const float* u_res;
-  int32_t* committed;
-  int32_t* accept_len;
-  int32_t* context_lens;
-  int32_t* accept_len_full;
-  float* pt_at;
-  float* pd_at;
-  float* labels;
-  int32_t* status;
-  const uint64_t* stat;
-  const uint64_t* bit;
-  const uint64_t* share;
-  const uint64_t* draw;
-  Control* ctl;
-  int V, gamma, nseg, commit;
-  uint32_t tag;
-  int b, r0, w, cap;
-};
-__constant__ Exp2Poly kPickPoly = kExp2Taylor;
-
-// Decision, draw and commit of request pc.b, and its labels; the whole workgroup.
 template <typename T>
-__device__ __attribute__((noinline)) void pick(const PickCtx& pc, Shared& sh) {
-  Seg<T> xt, xd;
-  const PickCtx& a = pc;
-  const Exp2Poly& P = kPickPoly;
-  const uint32_t tag = pc.tag;
-  const int b = pc.b, r0 = pc.r0, w = pc.w, cap = pc.cap;
+__global__ __launch_bounds__(kPickThreads) void pick_kernel(Ctx c, int commit) {
+  __shared__ double s_t, s_base, s_rho;
+  __shared__ int s_pos, s_residual;
+  __shared__ double s_wave[kPickThreads / kWave];
+  __shared__ int s_y, s_last;
+  const int b = blockIdx.x;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-  const int G1 = a.gamma - 1, nseg = pc.nseg;
-  const float qnan = __int_as_float(0x7fc00000);
-  // labels: wave k sums the shares of draft k (fixed order: lanes over segments, butterfly)
-  if (a.labels) {
-    for (int k = wave; k < G1; k += kWaves) {
+  const int G1 = c.a.gamma - 1;
+  const int nseg = c.L.nseg;
+  // Every load that depends on no other goes out first, before the window check and the
+  // label stores (which may alias them as far as the compiler knows): the decision record,
+  // the drafted tokens, the context length and lane s's draw sums of segment s (when a wave
+  // covers every segment).
+  const bool lanes_cover = nseg <= kWave;
+  Decision d;
+  double r1v[kDrawSums] = {0.0, 0.0, 0.0, 0.0};
+  int tok = -1, ctx0 = 0;  // thread i < gamma: drafted token i; thread 0: the context length
+  if (commit) {
+    d = c.dec[b];
+    if (tid < G1) tok = c.a.tokens[size_t(b) * G1 + tid];
+    if (tid == 0) ctx0 = c.a.context_lens[b];
+    if (wave == 0 && lanes_cover && lane < nseg) {
+      const double* r = c.r1 + (size_t(b) * nseg + lane) * kDrawSums;
+#pragma unroll
+      for (int q = 0; q < kDrawSums; ++q) r1v[q] = r[q];
+    }
+  }
+  if (!req_ok(c, b)) return;
+  const int w = c.a.cu[b + 1] - c.a.cu[b];
+  if (c.a.labels) {  // one wave per draft (wave 0 is left to the draw when there is one):
+                     // lanes sum the segment shares of the overlap
+    const int first = commit ? 1 : 0, stride = kPickThreads / kWave - first;
+    for (int k = wave - first; k >= 0 && k < G1; k += stride) {
+      const size_t o = size_t(b) * G1 + k;
       double ov = 0.0;
-      if (k < w - 1) {
-        const uint64_t* q = pc.share + size_t(r0 + k) * nseg;
-        for (int s0 = 0; s0 < nseg; s0 += kWave) {
-          const int s = s0 + lane;
-          const uint64_t wd = wait_word(pc.ctl, pc.status, tag, q + s, s < nseg);
-          if (s < nseg) ov += double(payload_f32(wd));
-        }
-        ov = wave_sum_f64(ov);
-      }
-      if (lane == 0) a.labels[size_t(b) * G1 + k] = k < w - 1 ? float(ov) : qnan;
+      if (k < w - 1)
+        for (int s = lane; s < nseg; s += kWave) ov += c.tv[o * nseg + s];
+      ov = wave_sum_f64(ov);
+      // c* = 1 - TV = sum_v min(p_d, p_t)
+      if (lane == 0) c.a.labels[o] = k < w - 1 ? float(ov) : __int_as_float(0x7fc00000);
     }
   }
-  if (!pc.commit) return;
-  if (tid >= w - 1 && tid < G1) {  // positions past the window
-    if (a.pt_at) a.pt_at[size_t(b) * G1 + tid] = qnan;
-    if (a.pd_at) a.pd_at[size_t(b) * G1 + tid] = qnan;
-  }
-  // decision: the first rejected draft (test results posted by the pairs' teams)
-  if (wave == 0) {
-    const bool mine = lane < w - 1;
-    const uint64_t wd = wait_word(pc.ctl, pc.status, tag, pc.bit + r0 + lane, mine);
-    const unsigned long long rej = __ballot(mine && (uint32_t(wd) & 1u));
-    const int n_full = rej ? __ffsll(rej) - 1 : w - 1;
-    const bool residual = n_full < cap - 1;
-    const int n = residual ? n_full : cap - 1;
-    // the draw's segment sums (lanes over segments)
-    const int item = r0 + n;
-    const uint64_t* dq = pc.draw + size_t(item) * nseg * kDrawWords;
-    for (int k0 = 0; k0 < nseg * kDrawWords; k0 += kWave) {
-      const int k = k0 + lane;
-      wait_word(pc.ctl, pc.status, tag, dq + k, k < nseg * kDrawWords && (residual || (k % kDrawWords) < 2));
-    }
-    auto dval = [&](int s, int q) { return payload_f64(get(dq + s * kDrawWords + 2 * q), get(dq + s * kDrawWords + 2 * q + 1)); };
-    double st = 0.0, sd = 0.0;
-    for (int s = lane; s < nseg; s += kWave) {
-      st += dval(s, 0);
-      if (residual) sd += dval(s, 1);
-    }
-    st = wave_sum_f64(st);
-    sd = wave_sum_f64(sd);
-    const double rho = residual ? st / sd : 0.0;
-    const double drho = residual ? rho - dval(0, 4) : 0.0;
-    bool res = residual;
-    auto mass = [&](int s) {
-      if (!res) return dval(s, 0);
-      const double m = dval(s, 2) - drho * dval(s, 3);
+  if (!commit) return;
+  if (d.n < 0) return;
+  // the 2^(j/256) table of the rescan is filled by waves 1.. while wave 0 locates the
+  // sub-segment; the barrier after the search publishes both
+  static_assert(kPickThreads - kWave >= 256, "waves 1.. fill the 256-entry table");
+  __shared__ double tab[256];
+  if (tid >= kWave && tid - kWave < 256) tab[tid - kWave] = exp2_f64(c.P, double(tid - kWave) / 256.0);
+  if (wave == 0 && lanes_cover) {
+    // the general path below with every per-segment value held by its lane: the same sums
+    // in the same order, without re-reading the draw sums for each step
+    const double St = wave_sum_f64(r1v[0]), Sd = wave_sum_f64(r1v[1]);
+    bool residual = d.id_d >= 0;
+    const double rho = residual ? St / Sd : 0.0;
+    const double drho = rho - d.rho32;
+    auto lane_mass = [&](bool res) {
+      if (lane >= nseg) return 0.0;
+      if (!res) return r1v[0];
+      const double m = r1v[2] - drho * r1v[3];
       return m > 0.0 ? m : 0.0;
     };
-    double q = 0.0;
-    for (int s = lane; s < nseg; s += kWave) q += mass(s);
-    double Q = wave_sum_f64(q);
-    if (res && !(Q > 0.0)) {  // residual identically zero: draw from p_t of that row instead
-      res = false;
-      Q = st;
+    double mass = lane_mass(residual);
+    double Q = wave_sum_f64(mass);
+    if (residual && !(Q > 0.0)) {  // residual identically zero: draw from p_t instead
+      residual = false;
+      Q = St;
+      mass = lane_mass(false);
     }
-    const double t = double(a.u_res[b]) * Q;
-    int seg = 0;
+    const double t = double(c.a.u_res[b]) * Q;
+    int seg = -1;
     double base = 0.0;
-    locate(t, 0.0, nseg, mass, seg, base);
+    locate(t, 0.0, nseg, [&](int) { return mass; }, seg, base);
+    // lane u: sub-segment u of the chosen segment (kSub <= kWave)
+    double sm = 0.0;
+    if (lane < kSub) sm = sub_mass(c, b, seg, lane, residual, drho);
+    int sub = -1;
+    double base2 = base;
+    locate(t, base, kSub, [&](int) { return sm; }, sub, base2);
     if (lane == 0) {
-      sh.n = n;
-      sh.n_full = n_full;
-      sh.residual = res;
-      sh.rho = rho;
-      sh.t = t;
-      sh.base = base;
-      sh.seg = seg;
-      sh.y = 0x7fffffff;
-      sh.ylast = -1;
-      sh.Mt = 0.f;
-      sh.Md = 0.f;
+      s_t = t;
+      s_base = base2;
+      s_pos = seg * kSeg + sub * kSubLen;
+      s_residual = residual;
+      s_rho = rho;
+      s_y = 0x7fffffff;
+      s_last = -1;
     }
-  }
-  __syncthreads();
-  const int n = sh.n, seg = sh.seg;
-  const bool res = sh.residual;
-  const int item = r0 + n;
-  // the maxima the candidate units used for e_t, e_d: the item's team normalisers
-  if (wave == 0) {
-    float Mt, Md;
+  } else if (wave == 0) {
     double St, Sd;
-    team_normalisers(pc.ctl, pc.status, P, pc.stat, nseg, tag, item, res, Mt, St, Md, Sd);
+    draw_totals(c, b, St, Sd);
+    bool residual = d.id_d >= 0;
+    const double rho = residual ? St / Sd : 0.0;
+    const double drho = rho - d.rho32;
+    double q = 0.0;
+    for (int s = lane; s < nseg; s += kWave) q += seg_mass(c, b, s, residual, drho);
+    double Q = wave_sum_f64(q);
+    if (residual && !(Q > 0.0)) {  // residual identically zero: draw from p_t instead
+      residual = false;
+      Q = St;
+    }
+    const double t = double(c.a.u_res[b]) * Q;
+    // first segment whose running mass passes t, then the first sub-segment inside it
+    int seg = -1;
+    double base = 0.0;
+    locate(t, 0.0, nseg, [&](int s) { return seg_mass(c, b, s, residual, drho); }, seg, base);
+    int sub = -1;
+    double base2 = base;
+    locate(t, base, kSub, [&](int u) { return sub_mass(c, b, seg, u, residual, drho); }, sub, base2);
     if (lane == 0) {
-      sh.Mt = Mt;
-      sh.Md = Md;
+      s_t = t;
+      s_base = base2;
+      s_pos = seg * kSeg + sub * kSubLen;
+      s_residual = residual;
+      s_rho = rho;
+      s_y = 0x7fffffff;
+      s_last = -1;
     }
-  }
-  fill_exp2_tab(P, sh.tab);  // ends with a barrier: sh.Mt / sh.Md visible
-  const T* trow = static_cast<const T*>(a.target) + size_t(item) * a.V;
-  const T* drow = static_cast<const T*>(a.draft) + size_t(b * G1 + n) * a.V;
-  const bool vec_ok = a.V % Seg<T>::kEpv == 0;
-  xt.load(trow, a.V, seg, vec_ok);
-  if (res) xd.load(drow, a.V, seg, vec_ok);
-  const float Mt = sh.Mt, Md = sh.Md;
-  const double rho = sh.rho;
-  // exact weights in index order: vector group i covers entries [i kNT kEpv, (i+1) kNT kEpv)
-  // of the segment with thread t holding kEpv consecutive ones
-  double running = sh.base;
-  // the weights are formed twice (thread sum, then the running sum), so that none is held
-  auto weight = [&](int i, int e) {
-    double x = exp_shift_tab(P, sh.tab, xt.at(i, e), Mt);
-    if (res) {
-      x -= rho * exp_shift_tab(P, sh.tab, xd.at(i, e), Md);
-      x = x > 0.0 ? x : 0.0;
-    }
-    return x;
-  };
-#pragma unroll
-  for (int i = 0; i < kVec; ++i) {
-    double tsum = 0.0;
-#pragma unroll
-    for (int e = 0; e < Seg<T>::kEpv; ++e) tsum += weight(i, e);
-    // inclusive prefix of the thread sums over the workgroup
-    double inc = tsum;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const double y = __shfl_up(inc, o);
-      if (lane >= o) inc += y;
-    }
-    __syncthreads();
-    if (lane == kWave - 1) sh.d[wave][0] = inc;
-    __syncthreads();
-    double before = running;
-    for (int k = 0; k < wave; ++k) before += sh.d[k][0];
-    double total = 0.0;
-#pragma unroll
-    for (int k = 0; k < kWaves; ++k) total += sh.d[k][0];
-    double cum = before + (inc - tsum);  // running sum before this thread's entries
-    int hit = 0x7fffffff, lastpos = -1;
-#pragma unroll
-    for (int e = 0; e < Seg<T>::kEpv; ++e) {
-      const double wv = weight(i, e);
-      cum += wv;
-      const int v = Seg<T>::index(seg, i, e);
-      if (wv > 0.0) {
-        lastpos = v;
-        if (hit == 0x7fffffff && cum > sh.t) hit = v;
-      }
-    }
-    // the first hit in index order (thread order within the group), the last positive entry
-    const unsigned long long hb = __ballot(hit != 0x7fffffff), pb = __ballot(lastpos >= 0);
-    if (hb && lane == __ffsll(hb) - 1) atomicMin(&sh.y, hit);
-    if (pb && lane == 63 - __clzll(pb)) atomicMax(&sh.ylast, lastpos);
-    running += total;
   }
   __syncthreads();
-  const int y = sh.y != 0x7fffffff ? sh.y : (sh.ylast >= 0 ? sh.ylast : seg * Seg<T>::kLen);
-  if (tid < a.gamma) {
-    const int tok = tid < n ? a.tokens[size_t(b) * G1 + tid] : 0;
-    a.committed[size_t(b) * a.gamma + tid] = tid < n ? tok : (tid == n ? y : -1);
+  const bool residual = s_residual;
+  const int v = s_pos + tid;
+  double wgt = 0.0;
+  if (v < c.a.V) {
+    wgt = exp_shift_tab(c.P, tab, Elem<T>::load(row_ptr<T>(c, d.id_t), v), d.Mt);
+    if (residual) {
+      wgt -= s_rho * exp_shift_tab(c.P, tab, Elem<T>::load(row_ptr<T>(c, d.id_d), v), d.Md);
+      wgt = wgt > 0.0 ? wgt : 0.0;
+    }
   }
+  // inclusive prefix in index order: wave scan, then the wave totals
+  double inc = wgt;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const double x = __shfl_up(inc, o);
+    if (lane >= o) inc += x;
+  }
+  if (lane == kWave - 1) s_wave[wave] = inc;
+  __syncthreads();
+  double cum = s_base;
+  for (int i = 0; i < wave; ++i) cum += s_wave[i];
+  cum += inc;
+  // the first entry past u * Q and the last positive entry: found per wave by ballot (entry
+  // v = s_pos + tid is in lane order), then one LDS atomic per wave -- one atomic per lane
+  // on a single address serialises the whole workgroup
+  const unsigned long long hit = __ballot(wgt > 0.0 && cum > s_t), pos = __ballot(wgt > 0.0);
+  if (lane == 0) {
+    if (hit) atomicMin(&s_y, v + __ffsll(hit) - 1);
+    if (pos) atomicMax(&s_last, v + 63 - __clzll(pos));
+  }
+  __syncthreads();
+  // the commit, one thread per block position (rounding that left u * Q past this
+  // sub-segment's end takes its last positive entry)
+  const int y = s_y != 0x7fffffff ? s_y : (s_last >= 0 ? s_last : s_pos);
+  const int n = d.n;
+  if (tid < c.a.gamma) c.a.committed[size_t(b) * c.a.gamma + tid] = tid < n ? tok : (tid == n ? y : -1);
   if (tid == 0) {
-    a.accept_len[b] = n;
-    a.context_lens[b] = a.context_lens[b] + n + 1;
-    if (a.accept_len_full) a.accept_len_full[b] = sh.n_full;
+    c.a.accept_len[b] = n;
+    c.a.context_lens[b] = ctx0 + n + 1;
   }
-}
-
-// ------------------------------------------------------------------ the kernel
-// Units of lane x (workgroups x, x + 8, ...): items x, x + 8, x + 16, ..., nseg units each.
-__device__ __forceinline__ int lane_units(int x, int M, int nseg) {
-  return x < M ? ((M - x + kLanes - 1) / kLanes) * nseg : 0;
 }
 
 template <typename T>
-__global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(6, 6))) void accept_kernel(Ctx c) {
-  __shared__ Shared sh;
+hipError_t launch_typed(const Ctx& c, bool commit, hipStream_t stream) {
   const AcceptArgs& a = c.a;
-  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int nseg = c.L.nseg, G1 = a.gamma - 1;
-  const int bid = blockIdx.x, x = bid % kLanes, q = bid / kLanes;
-  const int item = (q / nseg) * kLanes + x, seg = q % nseg;
-  if (item >= a.max_rows) return;  // grid padding (never counted)
-  const uint32_t epoch = uni(__hip_atomic_load(&c.ctl->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-  const uint32_t tag = epoch + 1u == 0u ? 1u : epoch + 1u;
-
-  // ---- which request, which position (wave 0)
-  if (wave == 0) {
-    const int M = a.cu[a.B];
-    int b = 0, r0 = 0, w = 0, cap = 0, ok = 0;
-    if (item < M) {
-      b = find_request(a.cu, a.B, item);
-      r0 = a.cu[b];
-      w = a.cu[b + 1] - r0;
-      ok = r0 >= 0 && w >= 1 && w <= a.gamma && r0 + w <= a.max_rows && item >= r0 && item < r0 + w;
-      cap = w;
-      if (ok && c.commit && a.cap) {
-        cap = a.cap[b];
-        if (cap < 1 || cap > w) {
-          if (lane == 0 && seg == 0 && item == r0) flag(a.status, RVA_DEV_BAD_WINDOW);
-          cap = cap < 1 ? 1 : w;
-        }
-      }
-      if (!ok && lane == 0 && seg == 0) flag(a.status, RVA_DEV_BAD_WINDOW);
-    }
-    if (lane == 0) {
-      sh.M = M;
-      sh.b = b;
-      sh.r0 = r0;
-      sh.w = w;
-      sh.cap = cap;
-      sh.item_ok = ok;
-    }
+  const bool with_labels = a.labels != nullptr;
+  hipLaunchKernelGGL(stats_kernel<T>, dim3(nseg, c.L.n_ids), dim3(kThreads), 0, stream, c);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(decide_kernel<T>, dim3(a.B), dim3(kDecideThreads), 0, stream, c, int(commit));
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int draw_slots = commit ? a.B : 0;
+  const int slots = draw_slots + (with_labels ? a.B * G1 : 0);
+  if (slots > 0) {
+    if constexpr (std::is_same<T, uint16_t>::value)
+      hipLaunchKernelGGL(pair_kernel_bf16, dim3(nseg, slots), dim3(kWideThreads), 0, stream, c,
+                         draw_slots, int(with_labels));
+    else
+      hipLaunchKernelGGL(pair_kernel_f32, dim3(nseg, slots), dim3(kWideThreads), 0, stream, c,
+                         draw_slots, int(with_labels));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  __syncthreads();
-  const int M = min(max(uni(sh.M), 0), a.max_rows);
-  if (item >= M) return;  // no such row this call (not counted: the chunk targets follow M)
-  const int b = uni(sh.b), r0 = uni(sh.r0), w = uni(sh.w), cap = uni(sh.cap);
-  const bool ok = uni(sh.item_ok) != 0;
-  const int j = item - r0;
-  const bool pair = ok && j < w - 1;
-  Seg<T> xt, xd;
-  if (ok) {
-    const bool vec_ok = a.V % Seg<T>::kEpv == 0;
-    const T* trow = static_cast<const T*>(a.target) + size_t(item) * a.V;
-    const T* drow = static_cast<const T*>(a.draft) + size_t(b * G1 + j) * a.V;
-    xt.load(trow, a.V, seg, vec_ok);
-    if (pair) xd.load(drow, a.V, seg, vec_ok);
-    // the drafted token, its uniform and its two logits (wave 0, lane 0)
-    float lt = 0.f, ld = 0.f, u = 0.f;
-    if (pair && c.commit && wave == 0 && lane == 0) {
-      int xtok = a.tokens[size_t(b) * G1 + j];
-      u = a.u_acc[size_t(b) * G1 + j];
-      if (xtok < 0 || xtok >= a.V) {
-        if (seg == 0) flag(a.status, RVA_DEV_BAD_TOKEN);
-        xtok = xtok < 0 ? 0 : a.V - 1;
-      }
-      lt = Elem<T>::load(trow, xtok);
-      ld = Elem<T>::load(drow, xtok);
-    }
-    // ---- segment statistics, posted for the team
-    float mt, md = -INFINITY;
-    double St, Sd = 0.0;
-    seg_stats(xt, sh, mt, St);
-    if (pair) seg_stats(xd, sh, md, Sd);
-    uint64_t* sw = c.stat + (size_t(item) * nseg + seg) * kStatWords;
-    if (tid == 0) {
-      put(sw, tag, __float_as_uint(mt));
-      put_f64(sw + 1, tag, St);
-      if (pair) {
-        put(sw + 3, tag, __float_as_uint(md));
-        put_f64(sw + 4, tag, Sd);
-      }
-    }
-    // ---- the team's normalisers, the accept test (wave 0)
-    if (wave == 0) {
-      float Mt, Md;
-      double St_, Sd_;
-      team_normalisers(c.ctl, a.status, c.P, c.stat, nseg, tag, item, pair, Mt, St_, Md, Sd_);
-      int reject = 0;
-      if (pair && c.commit && lane == 0) {
-        const double pt = exp_shift_f64(c.P, lt, Mt) / St_;
-        const double pd = exp_shift_f64(c.P, ld, Md) / Sd_;
-        const double r = pd == 0.0 ? INFINITY : pt / pd;
-        reject = !(double(u) < (r < 1.0 ? r : 1.0));
-        if (seg == 0) {
-          if (a.pt_at) a.pt_at[size_t(b) * G1 + j] = float(pt);
-          if (a.pd_at) a.pd_at[size_t(b) * G1 + j] = float(pd);
-          put(c.bit + item, tag, uint32_t(reject));
-        }
-      }
-      if (lane == 0) {
-        sh.Mt = Mt;
-        sh.Md = Md;
-        sh.St = St_;
-        sh.Sd = Sd_;
-        sh.it = float(1.0 / St_);
-        sh.id = pair ? float(1.0 / Sd_) : 0.f;
-        sh.reject = reject;
-      }
-    }
-    __syncthreads();
-    // ---- the label share: sum min(p_t, p_d) over the segment = 2^min(l_t, l_d), with
-    // l = x log2 e + c, c = -(M log2 e + log2 S): one FMA per entry, one exponential per
-    // entry pair (forming l from x log2 e instead of (x - M) log2 e moves it by a few float32
-    // ulp of |x log2 e|, about 1e-6 relative per term)
-    if (pair && a.labels) {
-      const float ct = uni(-fmaf(sh.Mt, kLog2e, -__log2f(sh.it)));
-      const float cd = uni(-fmaf(sh.Md, kLog2e, -__log2f(sh.id)));
-      double acc = 0.0;
-#pragma unroll
-      for (int i = 0; i < kVec; ++i) {
-        float run = 0.f;
-#pragma unroll
-        for (int e = 0; e < Seg<T>::kEpv; ++e)
-          run += __builtin_amdgcn_exp2f(fminf(fmaf(xt.at(i, e), kLog2e, ct), fmaf(xd.at(i, e), kLog2e, cd)));
-        acc += double(run);
-        xt.touch(i);
-        xd.touch(i);
-      }
-      double v[1] = {acc};
-      block_sums<1>(v, sh);
-      if (tid == 0) put(c.share + size_t(item) * nseg + seg, tag, __float_as_uint(float(v[0])));
-    }
-    // ---- the draw's segment sums, for the units that may carry it
-    const bool residual_cand = c.commit && pair && j < cap - 1 && uni(sh.reject);
-    const bool bonus_cand = c.commit && j == cap - 1;
-    if (residual_cand || bonus_cand) {
-      fill_exp2_tab(c.P, sh.tab);
-      const float Mt = uni(sh.Mt), Md = uni(sh.Md);
-      const double rho1 = residual_cand ? uni(sh.St) / uni(sh.Sd) : 0.0;
-      double v[4] = {0.0, 0.0, 0.0, 0.0};  // S_t, S_d, A(rho'), D
-#pragma unroll
-      for (int i = 0; i < kVec; ++i) {
-        xt.touch(i);
-        xd.touch(i);
-#pragma unroll
-        for (int e = 0; e < Seg<T>::kEpv; ++e) {
-          const double et = exp_shift_tab(c.P, sh.tab, xt.at(i, e), Mt);
-          v[0] += et;
-          if (residual_cand) {
-            const double ed = exp_shift_tab(c.P, sh.tab, xd.at(i, e), Md);
-            v[1] += ed;
-            const double r = et - rho1 * ed;
-            if (r > 0.0) {
-              v[2] += r;
-              v[3] += ed;
-            }
-          }
-        }
-      }
-      block_sums<4>(v, sh);
-      uint64_t* dw = c.draw + (size_t(item) * nseg + seg) * kDrawWords;
-      if (tid < 5) {
-        const double val = tid == 4 ? rho1 : v[tid];
-        if (tid < 1 || residual_cand) put_f64(dw + 2 * tid, tag, val);
-      }
-    }
-    // ---- the request's last workgroup decides, draws and commits
-    if (tid == 0) {
-      const uint32_t target = uint32_t(w) * uint32_t(nseg);
-      const uint32_t old = atomicAdd(&c.req_cnt[b], 1u);
-      sh.last = old + 1u == target;
-      if (sh.last) atomicExch(&c.req_cnt[b], 0u);
-    }
-    __syncthreads();
-    if (sh.last) {
-      __shared__ PickCtx pc;
-      if (tid == 0) {
-        pc.target = a.target;
-        pc.draft = a.draft;
-        pc.tokens = a.tokens;
-        pc.u_res = a.u_res;
-        pc.committed = a.committed;
-        pc.accept_len = a.accept_len;
-        pc.context_lens = a.context_lens;
-        pc.accept_len_full = a.accept_len_full;
-        pc.pt_at = a.pt_at;
-        pc.pd_at = a.pd_at;
-        pc.labels = a.labels;
-        pc.status = a.status;
-        pc.stat = c.stat;
-        pc.bit = c.bit;
-        pc.share = c.share;
-        pc.draw = c.draw;
-        pc.ctl = c.ctl;
-        pc.V = a.V;
-        pc.gamma = a.gamma;
-        pc.nseg = nseg;
-        pc.commit = c.commit;
-        pc.tag = tag;
-        pc.b = b;
-        pc.r0 = r0;
-        pc.w = w;
-        pc.cap = cap;
-      }
-      __syncthreads();
-      pick<T>(pc, sh);
-    }
-  }
-  // ---- completion: the last workgroup of the call advances the epoch
-  if (tid == 0) {
-    const int k = bid / kChunk;
-    int in_chunk = 0;
-#pragma unroll
-    for (int xx = 0; xx < kLanes; ++xx) in_chunk += min(max(lane_units(xx, M, nseg) - k * (kChunk / kLanes), 0), kChunk / kLanes);
-    const int chunks = (lane_units(0, M, nseg) + kChunk / kLanes - 1) / (kChunk / kLanes);
-    if (atomicAdd(&c.chunk[k], 1u) + 1u == uint32_t(in_chunk)) {
-      atomicExch(&c.chunk[k], 0u);
-      if (atomicAdd(&c.ctl->done, 1u) + 1u == uint32_t(chunks)) {
-        atomicExch(&c.ctl->done, 0u);
-        atomicExch(&c.ctl->giveup, 0u);
-        atomicExch(&c.ctl->epoch, tag);
-      }
-    }
-  }
+  hipLaunchKernelGGL(pick_kernel<T>, dim3(a.B), dim3(kPickThreads), 0, stream, c, int(commit));
+  return hipGetLastError();
 }
 
 }  // namespace
 
-// sized for float32 rows (twice the segments of bf16), so one size serves both dtypes
 size_t accept_workspace_bytes(int B, int gamma, int V, int max_rows) {
-  const size_t a = ws_layout(B, gamma, V, max_rows, 2).total;
-  const size_t b = ws_layout(B, gamma, V, max_rows, 4).total;
-  return a > b ? a : b;
+  return ws_layout(B, gamma, V, max_rows).total;
 }
 
 hipError_t launch_accept(const AcceptArgs& a, int logit_dtype, bool commit, hipStream_t stream) {
   Ctx c;
   c.a = a;
   c.P = kExp2Taylor;
-  const int eb = logit_dtype == RVA_BF16 ? 2 : 4;
-  c.L = ws_layout(a.B, a.gamma, a.V, a.max_rows, eb);
-  c.commit = commit ? 1 : 0;
+  c.L = ws_layout(a.B, a.gamma, a.V, a.max_rows);
   char* base = static_cast<char*>(a.ws);
-  c.ctl = reinterpret_cast<Control*>(base + c.L.off_ctl);
-  c.req_cnt = reinterpret_cast<uint32_t*>(base + c.L.off_req);
-  c.chunk = reinterpret_cast<uint32_t*>(base + c.L.off_chunk);
-  c.stat = reinterpret_cast<uint64_t*>(base + c.L.off_stat);
-  c.bit = reinterpret_cast<uint64_t*>(base + c.L.off_bit);
-  c.share = reinterpret_cast<uint64_t*>(base + c.L.off_share);
-  c.draw = reinterpret_cast<uint64_t*>(base + c.L.off_draw);
-  const long long grid = (long long)kLanes * c.L.nseg * ((a.max_rows + kLanes - 1) / kLanes);
-  if (logit_dtype == RVA_BF16)
-    hipLaunchKernelGGL(accept_kernel<uint16_t>, dim3(unsigned(grid)), dim3(kNT), 0, stream, c);
-  else
-    hipLaunchKernelGGL(accept_kernel<float>, dim3(unsigned(grid)), dim3(kNT), 0, stream, c);
-  return hipGetLastError();
+  c.st_m = reinterpret_cast<float*>(base + c.L.off_m);
+  c.st_s = reinterpret_cast<double*>(base + c.L.off_s);
+  c.nm = reinterpret_cast<float2*>(base + c.L.off_nm);
+  c.tv = reinterpret_cast<double*>(base + c.L.off_tv);
+  c.dec = reinterpret_cast<Decision*>(base + c.L.off_dec);
+  c.r1 = reinterpret_cast<double*>(base + c.L.off_r1);
+  c.sub = reinterpret_cast<double*>(base + c.L.off_sub);
+  return logit_dtype == RVA_BF16 ? launch_typed<uint16_t>(c, commit, stream)
+                                 : launch_typed<float>(c, commit, stream);
 }
 
 }  // namespace rva

@@ -27,7 +27,6 @@ DEV_BAD_COST = 0x08
 DEV_BAD_CONTEXT = 0x10
 DEV_BAD_PAGE = 0x20
 DEV_BAD_ROWS = 0x40
-DEV_TIMEOUT = 0x80
 
 _STATUS = {0: "RVA_OK", 1: "RVA_ERR_INVALID_ARGUMENT", 2: "RVA_ERR_UNSUPPORTED",
            3: "RVA_ERR_WORKSPACE_TOO_SMALL", 4: "RVA_ERR_HIP"}
