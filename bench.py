@@ -13,7 +13,9 @@ inside the timed region) so every step redoes the same work.
 Prints ONE JSON line: packed verify tokens/s for the step, plus the achieved HBM GB/s of
 verify attention + acceptance, the roofline of the dominant kernel (verify attention,
 timed with HIP events on the stream it runs on) and the CPU oracle's rate on a bounded
-sample of the same workload.
+sample of the same workload.  The default (compact) run also times static full-block
+verify on the same inputs (`static`), and compares the step's commits and labels with the
+oracle's on the sample (`parity_sample`: mismatches, and how many sit in the flip band).
 """
 
 from __future__ import annotations
@@ -110,6 +112,7 @@ def cpu_baseline(inp, windows, n_req):
     conf = inp.conf()
     bias, alpha, theta = inp.cost_tables()
     reps, dt = 0, 0.0
+    results = {}
     with threadpool_limits(1):
         # the sample is repeated until about 10 s of CPU work (at most 5 passes)
         while reps < 5 and dt < 10.0:
@@ -121,14 +124,110 @@ def cpu_baseline(inp, windows, n_req):
                                     np.float32(1.0 / np.sqrt(wl.D)))
             for j, b in enumerate(reqs):
                 tl, dl, toks = logits[j]
-                oracle.accept_request(tl, dl, toks[: ws[j] - 1], ua[b, : ws[j] - 1], ur[b])
+                results[b] = oracle.accept_request(tl, dl, toks[: ws[j] - 1], ua[b, : ws[j] - 1],
+                                                   ur[b])
             dt += time.perf_counter() - t0
             reps += 1
-    return {"value": reps * R / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+    return results, {"value": reps * R / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"first {n_req} of {inp.B} requests of {wl.name} ({R} packed verify rows): "
                       f"full-batch scheduling + pack, then attention and acceptance+labels of the "
                       f"sample, float64 NumPy, 1 thread, {reps} pass(es) in {dt:.1f} s on "
                       f"{cpu_model()} ({len(os.sched_getaffinity(0))} cores visible)"}
+
+
+def stage_times(ds, n_ev, stream, capped=False):
+    """Mean HIP-event durations (ms) of schedule + pack, attention and acceptance inside
+    whole steps, on the stream the kernels are launched on."""
+    import torch
+
+    wl = ds.wl
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_ev)]
+    for i in range(n_ev):
+        ds.restore()
+        ev[i][0].record(stream)
+        ds.schedule()
+        if capped:
+            ds.cap_windows.copy_(ds.windows)
+            ds.windows.fill_(wl.gamma)
+        ds.pack()
+        ev[i][1].record(stream)
+        ds.attention()
+        ev[i][2].record(stream)
+        if capped:
+            ds.accept_capped(None)
+        else:
+            ds.accept(labels=True)
+        ev[i][3].record(stream)
+    torch.cuda.synchronize()
+    return tuple(float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(n_ev)]))
+                 for j in range(3))
+
+
+def time_steps(step, steps, warmup, stream):
+    """Mean ms per step over exactly `steps` back-to-back steps after `warmup` untimed ones."""
+    import torch
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def static_arm(inp, steps, warmup, stream):
+    """Static full-block verify on the same inputs: every request verifies its whole block
+    (window gamma), the arm the compact mode is compared with."""
+    from workloads.device import DeviceStep
+
+    wl = inp.wl
+    ds = DeviceStep(inp, mode="static")
+    ds.prepare()
+
+    def step():
+        ds.restore()
+        ds.step()
+
+    ms = time_steps(step, steps, warmup, stream)
+    t_front, t_attn, t_acc = stage_times(ds, max(10, steps // 2), stream)
+    windows = ds.windows.cpu().numpy()
+    M = int(ds.total_tier[0].item())
+    attn_b, acc_b, _ = algorithmic_bytes(wl, inp.context_lens, windows)
+    committed = int(ds.accept_len.sum().item()) + inp.B
+    gbs = (attn_b + acc_b) / ((t_attn + t_acc) * 1e-3) / 1e9
+    return {"ms_per_step": ms, "packed_rows_M": M, "tokens_per_s": M / (ms * 1e-3),
+            "committed_tokens_per_step": committed,
+            "goodput_committed_tokens_per_s": committed / (ms * 1e-3),
+            "attn_ms": t_attn, "accept_ms": t_acc, "schedule_pack_ms": t_front,
+            "verify_attn_accept_GBps": gbs, "pct_peak": 100.0 * gbs / PEAK_HBM_GBS,
+            "device_status": int(ds.status.item())}
+
+
+def sample_parity(ds, results, windows):
+    """The GPU step's commits and labels against the oracle's on the baseline sample:
+    requests whose commit differs, and how many of those sit in the flip band (an accept
+    test within 1e-6 of its threshold, or a draw within 1e-9 of a bin edge)."""
+    committed = ds.committed.cpu().numpy()
+    accept_len = ds.accept_len.cpu().numpy()
+    labels = ds.labels.cpu().numpy()
+    mism = band = 0
+    lab_err = 0.0
+    for b, r in results.items():
+        w = int(windows[b])
+        n = int(accept_len[b])
+        same = n == r["n"] and list(committed[b, : n + 1]) == list(r["committed"])
+        near = any(m < 1e-6 for m in r["margins"]) or r["draw_margin"] < 1e-9
+        if not same:
+            mism += 1
+            band += int(near)
+        if w > 1:
+            lab_err = max(lab_err, float(np.max(np.abs(labels[b, : w - 1] - np.asarray(r["labels"])))))
+    return {"requests_checked": len(results), "commit_mismatches": mism,
+            "mismatches_in_flip_band": band, "labels_max_abs_err": lab_err}
 
 
 def cost_table(inp, reps, warm):
@@ -369,8 +468,6 @@ def main():
     ap.add_argument("--flush-mall", action="store_true",
                     help="touch 1 GiB before every timed step (working sets under the 256 MB "
                          "Infinity Cache); each step is then timed alone and the median reported")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="accepted for older profiling commands: the 1 GiB copy always runs")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
@@ -503,28 +600,7 @@ def main():
         ms_serial = s0.elapsed_time(s1) / args.steps
 
     # ---- per-stage durations inside whole steps (HIP events on the launch stream)
-    n_ev = max(10, args.steps // 2)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(n_ev)]
-    for i in range(n_ev):
-        ds.restore()
-        ev[i][0].record(stream)
-        ds.schedule()
-        if capped:
-            ds.cap_windows.copy_(ds.windows)
-            ds.windows.fill_(wl.gamma)
-        ds.pack()
-        ev[i][1].record(stream)
-        ds.attention()
-        ev[i][2].record(stream)
-        if capped:
-            ds.accept_capped(None)
-        else:
-            ds.accept(labels=True)
-        ev[i][3].record(stream)
-    torch.cuda.synchronize()
-    t_front = np.mean([ev[i][0].elapsed_time(ev[i][1]) for i in range(n_ev)])
-    t_attn = np.mean([ev[i][1].elapsed_time(ev[i][2]) for i in range(n_ev)])
-    t_acc = np.mean([ev[i][2].elapsed_time(ev[i][3]) for i in range(n_ev)])
+    t_front, t_attn, t_acc = stage_times(ds, max(10, args.steps // 2), stream, capped)
     status = int(ds.status.item())
 
     attn_gbs = attn_b / (t_attn * 1e-3) / 1e9
@@ -577,8 +653,12 @@ def main():
         res["cap_accept"] = {"accepted_drafts_capped": acc, "accepted_drafts_uncapped": full,
                              "utilisation": acc / max(1, full),
                              "mean_cap_window": float(caps.mean())}
+    if args.mode == "compact" and graph is None and flush is None:
+        res["static"] = static_arm(inp, args.steps, args.warmup, stream)
     if args.cpu_sample > 0:
-        res["cpu_baseline"] = cpu_baseline(inp, windows, min(args.cpu_sample, inp.B))
+        results, res["cpu_baseline"] = cpu_baseline(inp, windows, min(args.cpu_sample, inp.B))
+        if not capped:
+            res["parity_sample"] = sample_parity(ds, results, windows)
     print(json.dumps(res))
 
 

@@ -48,3 +48,30 @@ def test_theta_high_concurrency_is_current():
     theta, mean_w = mk.derive()
     assert theta == THETA_HIGH_CONCURRENCY
     assert mean_w == 3.0
+
+
+def test_draft_overlap_tracks_confidence():
+    """Each draft row's noise is chosen so that its acceptance probability, the overlap
+    sum_v min(p_t, p_d) of the oracle's label, is the request's drawn confidence."""
+    from oracle.acceptance import softmax64, tv_label
+
+    inp = Inputs(get("mixed-b64"))
+    for b in range(3):
+        tl, dl, _ = inp.request_logits(b)
+        t, d = tl.double().numpy(), dl.double().numpy()
+        c = inp.conf64(b)
+        for k in range(inp.wl.G1):
+            ov = tv_label(softmax64(d[k]), softmax64(t[k]))
+            assert abs(ov - c[k]) < 0.03, (b, k, ov, c[k])
+
+
+def test_head_hidden_uses_the_drawn_confidence():
+    """The head workload's hidden states encode the same confidences that set its draft
+    noise: the head's logit on the (unrounded) hidden state is log(c / (1 - c))."""
+    inp = Inputs(get("qwen3-4b"))
+    h = inp.hidden().double().numpy()
+    w = inp.head_w.astype(np.float64)
+    for b in range(2):
+        c = inp.conf64(b)
+        z = h[b] @ w + float(inp.head_b)
+        np.testing.assert_allclose(1.0 / (1.0 + np.exp(-z)), c, atol=2e-2)

@@ -25,7 +25,9 @@ THETA_HIGH_CONCURRENCY = 0.06617
 
 @dataclass(frozen=True)
 class ConfClass:
-    """One traffic class: confidences c ~ Beta(a, b); draft-logit noise std sigma."""
+    """One traffic class: confidences c ~ Beta(a, b).  sigma: the draft-logit noise std at
+    the class's mean confidence (the synthetic acceptance traces of the STS benchmark use it;
+    the workloads' draft rows take each draft's own sigma from its drawn confidence)."""
 
     a: float
     b: float

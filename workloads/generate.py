@@ -16,7 +16,11 @@ any request can be regenerated alone and arrays are independent of each other):
 * q, k_new, v_new (all gamma block positions) and the cached context K/V: N(0, 1),
   rounded to the KV dtype.
 * target logits: N(0, std^2) per row (gamma rows per request, std = 2); draft row k =
-  target row k-1 + N(0, sigma^2) with the class's sigma; both rounded to the logit dtype.
+  target row k-1 + N(0, sigma_k^2); both rounded to the logit dtype.  sigma_k follows the
+  request's drawn confidence c_k for draft k, so that the draft is accepted with probability
+  c_k: with n ~ N(0, sigma^2) added to every logit, p_d / p_t = exp(n - sigma^2 / 2) under
+  p_t, whose expected overlap sum_v min(p_t, p_d) is 2 Phi(-sigma / 2) for a large
+  vocabulary; sigma_k = -2 Phi^-1(c_k / 2) (0.125, 0.25, 0.5 at c = 0.95, 0.9, 0.8).
 * draft tokens: drawn from softmax(draft row) with the Gumbel-max trick in float64
   (argmax of logits + Gumbel noise), i.e. a sample of the drafter, not part of the path.
 * u_accept[b, k], u_resample[b]: U[0, 1) float32.
@@ -38,12 +42,22 @@ any request can be regenerated alone and arrays are independent of each other):
 
 from __future__ import annotations
 
+from statistics import NormalDist
+
 import numpy as np
 import torch
 
 from .configs import Workload
 
 _TORCH = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+def draft_sigma(c: np.ndarray) -> np.ndarray:
+    """Draft-logit noise std (float32) at which a draft is accepted with probability c:
+    sigma = -2 Phi^-1(c / 2), clamped to c in [1e-6, 1 - 1e-6]."""
+    nd = NormalDist()
+    cc = np.clip(np.asarray(c, np.float64), 1e-6, 1.0 - 1e-6)
+    return np.array([-2.0 * nd.inv_cdf(x / 2.0) for x in cc], np.float32)
 
 
 def _round(x: np.ndarray, dtype: str) -> torch.Tensor:
@@ -93,13 +107,18 @@ class Inputs:
         return self.wl.classes[int(self.classes[b])]
 
     # ------------------------------------------------------------------ stage 1 inputs
+    def conf64(self, b: int) -> np.ndarray:
+        """Request b's drawn confidences [gamma-1] (float64): the Beta draw behind both the
+        given confidences and the head's hidden states."""
+        c = self.cls(b)
+        return self._rng(b, self._CONF).beta(c.a, c.b, size=self.wl.G1)
+
     def conf(self) -> np.ndarray:
         """[B, gamma-1] float32 confidences (beta workloads)."""
         if "conf" not in self._cache:
             out = np.empty((self.B, self.wl.G1), np.float32)
             for b in range(self.B):
-                c = self.cls(b)
-                out[b] = self._rng(b, self._CONF).beta(c.a, c.b, size=self.wl.G1)
+                out[b] = self.conf64(b)
             self._cache["conf"] = out
         return self._cache["conf"]
 
@@ -156,7 +175,7 @@ class Inputs:
         wl = self.wl
         r = self._rng(b, self._LOGITS)
         t = r.standard_normal((wl.gamma, wl.V), dtype=np.float32) * np.float32(wl.target_logit_std)
-        noise = r.standard_normal((wl.G1, wl.V), dtype=np.float32) * np.float32(self.cls(b).sigma)
+        noise = r.standard_normal((wl.G1, wl.V), dtype=np.float32) * draft_sigma(self.conf64(b))[:, None]
         d = t[:-1] + noise
         tt, dd = _round(t, wl.logit_dtype), _round(d, wl.logit_dtype)
         # Gumbel-max draw of each draft token from softmax(draft row), float64
