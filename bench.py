@@ -52,25 +52,41 @@ def algorithmic_bytes(wl, context_lens, windows):
     return attn, accept, flops
 
 
-def counter_traffic(workload):
-    """HBM bytes per launch of rva_verify_attention from the committed rocprofv3 counter
-    summary (FETCH_SIZE and WRITE_SIZE passes, each scaled by the copy calibration), or None
-    when there is none for this workload or the attention source changed since it was taken."""
+def profile_fields(name):
+    """Fields ("key: value" lines) of a committed rocprofv3 summary under profiles/, or None
+    when it is missing or the attention source changed since its counters were taken."""
     import hashlib
 
-    path = os.path.join(ROOT, "profiles", f"verify_attention_{workload}_hbm_counters.md")
+    path = os.path.join(ROOT, "profiles", name)
     src = os.path.join(ROOT, "ragged_verify_acceptance_amd", "csrc", "attention.hip")
     if not os.path.exists(path):
         return None
     fields = {}
     for line in open(path):
-        if ":" in line and not line.startswith(("|", "#", "*", "cd ")):
+        if ":" in line and not line.startswith(("|", "#", "*", "cd ", " ")):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
     sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if fields.get("attention_source_sha256") != sha or "traffic_bytes_per_launch" not in fields:
+    return fields if fields.get("attention_source_sha256") == sha else None
+
+
+def counter_traffic(workload):
+    """HBM bytes per launch of rva_verify_attention from the committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE passes, each scaled by the copy calibration), or None."""
+    f = profile_fields(f"verify_attention_{workload}_hbm_counters.md")
+    return float(f["traffic_bytes_per_launch"]) if f and "traffic_bytes_per_launch" in f else None
+
+
+def counter_mfma(workload):
+    """MFMA utilisation of attn_sk_kernel from the committed rocprofv3 counter summary
+    (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE x SIMDs; MFMA ops x 512 over the
+    dispatch time), or None."""
+    f = profile_fields(f"verify_attention_{workload}_mfma_counters.md")
+    if not f or "mfma_util_pct" not in f:
         return None
-    return float(fields["traffic_bytes_per_launch"])
+    return {"mfma_busy_pct": float(f["mfma_util_pct"]), "mfma_TFLOPs": float(f["mfma_tflops"]),
+            "mfma_flops_per_launch": float(f["mfma_flops_per_launch"]),
+            "source": f"profiles/verify_attention_{workload}_mfma_counters.md"}
 
 
 def cpu_model() -> str:
@@ -468,6 +484,8 @@ def main():
     ap.add_argument("--flush-mall", action="store_true",
                     help="touch 1 GiB before every timed step (working sets under the 256 MB "
                          "Infinity Cache); each step is then timed alone and the median reported")
+    ap.add_argument("--no-static", action="store_true",
+                    help="skip the static full-block arm of the default run (profiling runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
@@ -636,7 +654,7 @@ def main():
         "roofline": {"kernel": "rva_verify_attention (attn_sk_kernel + attn_merge_kernel)",
                      "bound": "hbm", "achieved": attn_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": attn_gbs / PEAK_HBM_GBS, "traffic": counter_traffic(wl.name),
-                     "algorithmic_bytes": attn_b},
+                     "algorithmic_bytes": attn_b, "mfma_counters": counter_mfma(wl.name)},
         "device_status": status,
         "committed_tokens_per_step": int(ds.accept_len.sum().item()) + inp.B,
         "goodput_committed_tokens_per_s": (int(ds.accept_len.sum().item()) + inp.B) / (ms_step * 1e-3),
@@ -653,7 +671,7 @@ def main():
         res["cap_accept"] = {"accepted_drafts_capped": acc, "accepted_drafts_uncapped": full,
                              "utilisation": acc / max(1, full),
                              "mean_cap_window": float(caps.mean())}
-    if args.mode == "compact" and graph is None and flush is None:
+    if args.mode == "compact" and graph is None and flush is None and not args.no_static:
         res["static"] = static_arm(inp, args.steps, args.warmup, stream)
     if args.cpu_sample > 0:
         results, res["cpu_baseline"] = cpu_baseline(inp, windows, min(args.cpu_sample, inp.B))
