@@ -12,9 +12,10 @@
 //   schedule_kernel   ONE workgroup (256 to 1024 threads, by batch size) for the whole batch:
 //                     (1) one lane per request forms the survival product left to right
 //                         in float32 (bit-identical to a sequential definition);
-//                     (2) a bitonic sort in LDS of 64-bit keys (inverted survival bits,
-//                         candidate index) gives the rank order "survival desc, request
-//                         asc, position asc" in one comparison;
+//                     (2) 64-bit keys (inverted survival bits, candidate index) order
+//                         "survival desc, request asc, position asc" in one comparison;
+//                         each request's keys are already in order, so the rank order is
+//                         a merge of B sorted runs (log2 B rounds, a binary search per key);
 //                     (3) a workgroup scan in float64 gives S_K for every K;
 //                     (4) a workgroup argmax of (B + S_K) / T(B, K), smallest K on ties;
 //                     (5) LDS counters turn the first K* ranks into per-request windows.
@@ -77,71 +78,61 @@ __device__ __forceinline__ double block_exclusive_scan_f64(double v, double* lds
   return wave_off + x - v;
 }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int d) {
-  const uint32_t lo = __shfl_xor(uint32_t(v), d), hi = __shfl_xor(uint32_t(v >> 32), d);
-  return (uint64_t(hi) << 32) | lo;
-}
-
-// One compare-exchange step of a bitonic sort for the element with index i holding x and
-// partner value y (index i ^ j): the lower index of an ascending (i & k == 0) pair keeps the
-// minimum.
-__device__ __forceinline__ uint64_t bitonic_keep(uint64_t x, uint64_t y, int i, int j, int k) {
-  const bool keep_min = ((i & j) == 0) == ((i & k) == 0);
-  return keep_min ? (x < y ? x : y) : (x > y ? x : y);
-}
-
-// Ascending bitonic sort of Npad (a power of two, <= E * NT) keys; thread t holds
-// the E consecutive elements t*E .. t*E + E - 1 in x.  Partners in the same thread are swapped
-// in registers, partners in the same wave by lane shuffles, and only partners in other waves
-// go through LDS (two barriers per such step).
-template <int E>
-__device__ __forceinline__ void bitonic_sort(uint64_t (&x)[E], uint64_t* lds, int Npad) {
+// Rank order of the candidates by merging sorted runs.  Each request's keys are already in
+// ascending order along its draft positions (survival never grows along a prefix, and the
+// candidate index breaks ties), so the B runs of G keys are merged pairwise, log2(B) rounds:
+// a key finds its place in the partner run by binary search (keys are unique), and lands at
+// pair start + its index in its own run + the partner keys below it.  One barrier a round.
+// `buf` holds two arrays of kMaxCand keys; returns the one that ends up sorted.  With invalid
+// confidences (a run not in order) the positions may collide; both arrays start with the keys,
+// so every slot still holds some candidate's key.
+template <int E, int NT>
+__device__ __forceinline__ const uint64_t* merge_runs(const uint64_t (&x)[E], uint64_t* buf, int N, int G) {
   const int tid = threadIdx.x;
-  for (int k = 2; k <= Npad; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      if (j >= kWave * E) {
+  uint64_t* cur = buf;
+  uint64_t* nxt = buf + kMaxCand;
 #pragma unroll
-        for (int e = 0; e < E; ++e) lds[tid * E + e] = x[e];
-        __syncthreads();
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const int i = tid * E + e;
-          x[e] = bitonic_keep(x[e], lds[i ^ j], i, j, k);
-        }
-        __syncthreads();
-      } else if (j >= E) {
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const int i = tid * E + e;
-          x[e] = bitonic_keep(x[e], shfl_xor_u64(x[e], j / E), i, j, k);
-        }
-      } else {
-        uint64_t y[E];
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          // j < E <= 4: j is 1 or 2; the partner index e ^ j is picked without dynamic indexing
-          uint64_t p = x[e];
-#pragma unroll
-          for (int f = 0; f < E; ++f)
-            if (f == (e ^ j)) p = x[f];
-          y[e] = bitonic_keep(x[e], p, tid * E + e, j, k);
-        }
-#pragma unroll
-        for (int e = 0; e < E; ++e) x[e] = y[e];
-      }
-    }
+  for (int e = 0; e < E; ++e) {
+    const int i = tid * E + e;
+    if (i < N) cur[i] = nxt[i] = x[e];
   }
+  __syncthreads();
+  for (int len = G; len < N; len <<= 1) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int i = tid * E + e;
+      if (i >= N) continue;
+      const uint64_t k = cur[i];
+      const int q = i / len, start = q * len;
+      const int ps = (q ^ 1) * len, pe = min(ps + len, N);
+      int pos = i;
+      if (ps < N) {
+        int lo = ps, hi = pe;
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if (cur[mid] < k) lo = mid + 1; else hi = mid;
+        }
+        pos = (q & ~1) * len + (i - start) + (lo - ps);
+      }
+      nxt[pos] = k;
+    }
+    __syncthreads();
+    uint64_t* t = cur;
+    cur = nxt;
+    nxt = t;
+  }
+  return cur;
 }
 
-// E keys per thread, NT threads (small batches take fewer waves: each sort step's shuffles
-// and barriers then involve fewer of them).
+// E keys per thread, NT threads (small batches take fewer waves: each merge round's
+// searches and barrier then involve fewer of them).
 template <int E, int NT>
 __global__ __launch_bounds__(NT) void schedule_kernel(
     int B, int G, int mode, const float* __restrict__ conf, float* __restrict__ conf_out,
     float* __restrict__ surv_out, float bias, const float* __restrict__ alpha,
     const float* __restrict__ theta, int32_t* __restrict__ windows, int32_t* __restrict__ K_out,
     double* __restrict__ ratio_out, int32_t* status) {
-  __shared__ uint64_t keys[kMaxCand];
+  __shared__ uint64_t keybuf[2 * kMaxCand];
   __shared__ float sa[kMaxCand];
   __shared__ int cnt[kMaxCand];
   __shared__ double wave_tot[NT / kWave];
@@ -150,8 +141,6 @@ __global__ __launch_bounds__(NT) void schedule_kernel(
 
   const int tid = threadIdx.x;
   const int N = B * G;
-  int Npad = 2;
-  while (Npad < N) Npad <<= 1;
 
   // the cost table entries this thread needs later (rank r = tid*E + e uses theta[B + r + 1])
   // are loaded now, so their round trip overlaps the survival products and the sort
@@ -195,10 +184,7 @@ __global__ __launch_bounds__(NT) void schedule_kernel(
       x[e] = (uint64_t(~bits) << 32) | uint32_t(i);
     }
   }
-  bitonic_sort<E>(x, keys, Npad);
-#pragma unroll
-  for (int e = 0; e < E; ++e) keys[tid * E + e] = x[e];
-  __syncthreads();
+  const uint64_t* keys = merge_runs<E, NT>(x, keybuf, N, G);
 
   // (3) S_K: each thread owns a contiguous run of ranks
   constexpr int per = E;
@@ -281,7 +267,7 @@ __global__ __launch_bounds__(NT) void schedule_kernel(
   // (5) windows from the first K* ranks
   for (int i = 0; i < per; ++i) {
     const int r = r0 + i;
-    if (r < Kstar && r < N) atomicAdd(&cnt[int(uint32_t(keys[r]) / uint32_t(G))], 1);
+    if (r < Kstar && r < N) atomicAdd(&cnt[min(int(uint32_t(keys[r]) / uint32_t(G)), B - 1)], 1);
   }
   __syncthreads();
   for (int b = tid; b < B; b += NT) windows[b] = 1 + cnt[b];
