@@ -98,6 +98,30 @@ __device__ __forceinline__ const uint64_t* merge_runs(const uint64_t (&x)[E], ui
   }
   __syncthreads();
   for (int len = G; len < N; len <<= 1) {
+    if constexpr (E > 1) {
+      // merge path: thread c writes kChunk consecutive outputs of one pair of runs, starting
+      // where a binary search along its diagonal puts it, then merges sequentially; far
+      // fewer scattered LDS probes than a search per key
+      constexpr int kChunk = 4;
+      const int per_pair = (2 * len + kChunk - 1) / kChunk;
+      const int pairs = (N + 2 * len - 1) / (2 * len);
+      for (int c = tid; c < pairs * per_pair; c += NT) {
+        const int p = c / per_pair, a0 = p * 2 * len, b0 = a0 + len;
+        const int lenA = min(len, N - a0), lenB = max(0, min(len, N - b0));
+        const int d0 = (c % per_pair) * kChunk, d1 = min(d0 + kChunk, lenA + lenB);
+        if (d0 >= d1) continue;
+        int lo = max(0, d0 - lenB), hi = min(d0, lenA);
+        while (lo < hi) {  // smallest i whose A[i] is not among the first d0 outputs
+          const int mid = (lo + hi) >> 1;
+          if (cur[a0 + mid] < cur[b0 + d0 - mid - 1]) lo = mid + 1; else hi = mid;
+        }
+        int i = lo, j = d0 - lo;
+        for (int d = d0; d < d1; ++d) {
+          const bool takeA = j >= lenB || (i < lenA && cur[a0 + i] < cur[b0 + j]);
+          nxt[a0 + d] = takeA ? cur[a0 + i++] : cur[b0 + j++];
+        }
+      }
+    } else {
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const int i = tid * E + e;
@@ -115,6 +139,7 @@ __device__ __forceinline__ const uint64_t* merge_runs(const uint64_t (&x)[E], ui
         pos = (q & ~1) * len + (i - start) + (lo - ps);
       }
       nxt[pos] = k;
+    }
     }
     __syncthreads();
     uint64_t* t = cur;
