@@ -1,7 +1,7 @@
 """Benchmark of the verify path on one MI355X.
 
-A step is one pass of the whole path over one batch: rva_schedule_windows ->
-rva_pack_ragged -> rva_verify_attention -> rva_accept_and_commit (with the TV labels
+A step is one pass of the whole path over one batch: rva_schedule_and_pack (stages 1
+and 2, one launch) -> rva_verify_attention -> rva_accept_and_commit (with the TV labels
 fused), on the mixed-traffic workload (B = 64, gamma = 8, GQA 32/8 D = 128 bf16 paged KV,
 contexts U[512, 8K], V = 151936 bf16 logits), compact mode.  With --overlap-schedule the
 scheduling call of each step is for the next step and runs on a second stream beside the
@@ -161,11 +161,13 @@ def stage_times(ds, n_ev, stream, capped=False):
     for i in range(n_ev):
         ds.restore()
         ev[i][0].record(stream)
-        ds.schedule()
         if capped:
+            ds.schedule()
             ds.cap_windows.copy_(ds.windows)
             ds.windows.fill_(wl.gamma)
-        ds.pack()
+            ds.pack()
+        else:
+            ds.schedule_pack()
         ev[i][1].record(stream)
         ds.attention()
         ev[i][2].record(stream)

@@ -7,6 +7,7 @@
  *   rva_schedule_windows   stage 1  confidence head + temperature scaling, prefix
  *                                   survival, per-request verify window
  *   rva_pack_ragged        stage 2  ragged packing of the window rows + tier rounding
+ *   rva_schedule_and_pack  stages 1 + 2 in one launch (same outputs)
  *   rva_verify_attention   stage 3  varlen GQA attention over the paged KV cache (+ append)
  *   rva_verify_attention_noalloc  stage 3 with a library-owned scratch (no workspace)
  *   rva_accept_and_commit  stage 4  speculative-sampling acceptance, draw, commit
@@ -153,6 +154,28 @@ rva_status rva_pack_ragged(int B, int gamma, const int32_t* windows,
                            const void* src, size_t row_bytes, void* dst, int max_rows,
                            int32_t* cu_seqlens, int32_t* row_req, int32_t* row_pos,
                            int32_t* total_tier, int32_t* device_status, hipStream_t stream);
+
+/*
+ * Stages 1 + 2 in one call -- rva_schedule_and_pack
+ *
+ * [SGL] "Zero-overhead scheduling 与 kernel", [CSDN] section 4: the scheduling decision is on
+ * the step's critical path, so it should cost as little as possible.  Exactly
+ * rva_schedule_windows followed by rva_pack_ragged with the windows it wrote (same
+ * arguments, same outputs bit for bit, same device-status bits), enqueued as ONE kernel
+ * launch when B*(gamma-1) <= 1024 (plus the head kernel when hidden states are given):
+ * every workgroup of the pack grid runs the scheduling pass itself, so the windows never
+ * make a round trip through memory between the stages.  Larger batches take the two
+ * kernels.  Validation is that of both calls (pack's gamma is this call's gamma).
+ */
+rva_status rva_schedule_and_pack(int B, int gamma, int mode, const void* hidden, int hidden_dtype, int H,
+                                 const float* head_w, float head_b, const float* conf_in,
+                                 const float* sts_T, float bias_ms, const float* alpha_ms, int alpha_len,
+                                 const float* theta_ms, int theta_len, float* conf_out, float* surv_out,
+                                 int32_t* windows, int32_t* K_out, double* ratio_out,
+                                 const int32_t* context_lens, const int32_t* tiers_host, int n_tiers,
+                                 const void* src, size_t row_bytes, void* dst, int max_rows,
+                                 int32_t* cu_seqlens, int32_t* row_req, int32_t* row_pos,
+                                 int32_t* total_tier, int32_t* device_status, hipStream_t stream);
 
 /*
  * Stage 3 -- rva_verify_attention

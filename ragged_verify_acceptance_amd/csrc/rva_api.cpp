@@ -47,13 +47,15 @@ const char* rva_last_error(void) { return g_last_error.c_str(); }
 
 int rva_version(void) { return RVA_VERSION; }
 
-rva_status rva_schedule_windows(int B, int gamma, int mode, const void* hidden, int hidden_dtype,
-                                int H, const float* head_w, float head_b, const float* conf_in,
-                                const float* sts_T, float bias_ms, const float* alpha_ms,
-                                int alpha_len, const float* theta_ms, int theta_len,
-                                float* conf_out, float* surv_out, int32_t* windows,
-                                int32_t* K_out, double* ratio_out, int32_t* device_status,
-                                hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+rva_status check_schedule(int B, int gamma, int mode, const void* hidden, int hidden_dtype, int H,
+                          const float* head_w, const float* conf_in, const float* sts_T,
+                          const float* alpha_ms, int alpha_len, const float* theta_ms, int theta_len,
+                          float* conf_out, float* surv_out, int32_t* windows, int32_t* K_out,
+                          double* ratio_out) {
   REQUIRE(B >= 1, "B must be >= 1 (got %d)", B);
   REQUIRE(gamma >= 2 && gamma <= 64, "gamma must be in [2, 64] (got %d)", gamma);
   REQUIRE((long long)B * (gamma - 1) <= 4096, "B*(gamma-1) must be <= 4096 (got %lld)",
@@ -72,6 +74,48 @@ rva_status rva_schedule_windows(int B, int gamma, int mode, const void* hidden, 
   REQUIRE(alpha_len > B, "alpha_len must be > B (got %d, B = %d)", alpha_len, B);
   REQUIRE((long long)theta_len > (long long)B * gamma, "theta_len must be > B*gamma (got %d)", theta_len);
   REQUIRE(conf_out && surv_out && windows && K_out && ratio_out, "an output pointer is NULL");
+  return RVA_OK;
+}
+
+rva_status check_pack(int B, int gamma, const int32_t* windows, const int32_t* context_lens,
+                      const int32_t* tiers_host, int n_tiers, const void* src, size_t row_bytes,
+                      void* dst, int max_rows, int32_t* cu_seqlens, int32_t* row_req, int32_t* row_pos,
+                      int32_t* total_tier, rva::TierTable* tt) {
+  REQUIRE(B >= 1 && B <= 4096, "B must be in [1, 4096] (got %d)", B);
+  REQUIRE(gamma >= 1 && gamma <= 4096, "gamma must be in [1, 4096] (got %d)", gamma);
+  REQUIRE(windows && context_lens, "windows and context_lens are required");
+  REQUIRE(tiers_host != nullptr, "tiers_host is NULL");
+  REQUIRE(n_tiers >= 1 && n_tiers <= 512, "n_tiers must be in [1, 512] (got %d)", n_tiers);
+  tt->n = n_tiers;
+  for (int i = 0; i < n_tiers; ++i) {
+    REQUIRE(tiers_host[i] >= 1, "tiers must be positive");
+    REQUIRE(i == 0 || tiers_host[i] > tiers_host[i - 1], "tiers must be strictly ascending");
+    tt->t[i] = tiers_host[i];
+  }
+  REQUIRE((long long)tiers_host[n_tiers - 1] >= (long long)B * gamma,
+          "largest tier %d is below B*gamma = %lld", tiers_host[n_tiers - 1], (long long)B * gamma);
+  REQUIRE(max_rows >= tiers_host[n_tiers - 1], "max_rows %d is below the largest tier %d", max_rows,
+          tiers_host[n_tiers - 1]);
+  REQUIRE((src == nullptr) == (dst == nullptr), "src and dst must both be given or both NULL");
+  REQUIRE(src == nullptr || row_bytes >= 1, "row_bytes must be >= 1");
+  REQUIRE(cu_seqlens && row_req && row_pos && total_tier, "an output pointer is NULL");
+  return RVA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+rva_status rva_schedule_windows(int B, int gamma, int mode, const void* hidden, int hidden_dtype,
+                                int H, const float* head_w, float head_b, const float* conf_in,
+                                const float* sts_T, float bias_ms, const float* alpha_ms,
+                                int alpha_len, const float* theta_ms, int theta_len,
+                                float* conf_out, float* surv_out, int32_t* windows,
+                                int32_t* K_out, double* ratio_out, int32_t* device_status,
+                                hipStream_t stream) {
+  rva_status st = check_schedule(B, gamma, mode, hidden, hidden_dtype, H, head_w, conf_in, sts_T, alpha_ms,
+                                 alpha_len, theta_ms, theta_len, conf_out, surv_out, windows, K_out, ratio_out);
+  if (st != RVA_OK) return st;
   return hip_result(rva::launch_schedule(B, gamma, mode, hidden, hidden_dtype, H, head_w, head_b,
                                          conf_in, sts_T, bias_ms, alpha_ms, theta_ms, conf_out,
                                          surv_out, windows, K_out, ratio_out, device_status, stream),
@@ -83,29 +127,37 @@ rva_status rva_pack_ragged(int B, int gamma, const int32_t* windows, const int32
                            size_t row_bytes, void* dst, int max_rows, int32_t* cu_seqlens,
                            int32_t* row_req, int32_t* row_pos, int32_t* total_tier,
                            int32_t* device_status, hipStream_t stream) {
-  REQUIRE(B >= 1 && B <= 4096, "B must be in [1, 4096] (got %d)", B);
-  REQUIRE(gamma >= 1 && gamma <= 4096, "gamma must be in [1, 4096] (got %d)", gamma);
-  REQUIRE(windows && context_lens, "windows and context_lens are required");
-  REQUIRE(tiers_host != nullptr, "tiers_host is NULL");
-  REQUIRE(n_tiers >= 1 && n_tiers <= 512, "n_tiers must be in [1, 512] (got %d)", n_tiers);
   rva::TierTable tt;
-  tt.n = n_tiers;
-  for (int i = 0; i < n_tiers; ++i) {
-    REQUIRE(tiers_host[i] >= 1, "tiers must be positive");
-    REQUIRE(i == 0 || tiers_host[i] > tiers_host[i - 1], "tiers must be strictly ascending");
-    tt.t[i] = tiers_host[i];
-  }
-  REQUIRE((long long)tiers_host[n_tiers - 1] >= (long long)B * gamma,
-          "largest tier %d is below B*gamma = %lld", tiers_host[n_tiers - 1], (long long)B * gamma);
-  REQUIRE(max_rows >= tiers_host[n_tiers - 1], "max_rows %d is below the largest tier %d", max_rows,
-          tiers_host[n_tiers - 1]);
-  REQUIRE((src == nullptr) == (dst == nullptr), "src and dst must both be given or both NULL");
-  REQUIRE(src == nullptr || row_bytes >= 1, "row_bytes must be >= 1");
-  REQUIRE(cu_seqlens && row_req && row_pos && total_tier, "an output pointer is NULL");
+  rva_status st = check_pack(B, gamma, windows, context_lens, tiers_host, n_tiers, src, row_bytes, dst, max_rows,
+                             cu_seqlens, row_req, row_pos, total_tier, &tt);
+  if (st != RVA_OK) return st;
   return hip_result(rva::launch_pack(B, gamma, windows, context_lens, tt, src, row_bytes, dst,
                                      max_rows, cu_seqlens, row_req, row_pos, total_tier,
                                      device_status, stream),
                     "rva_pack_ragged launch");
+}
+
+rva_status rva_schedule_and_pack(int B, int gamma, int mode, const void* hidden, int hidden_dtype, int H,
+                                 const float* head_w, float head_b, const float* conf_in, const float* sts_T,
+                                 float bias_ms, const float* alpha_ms, int alpha_len, const float* theta_ms,
+                                 int theta_len, float* conf_out, float* surv_out, int32_t* windows,
+                                 int32_t* K_out, double* ratio_out, const int32_t* context_lens,
+                                 const int32_t* tiers_host, int n_tiers, const void* src, size_t row_bytes,
+                                 void* dst, int max_rows, int32_t* cu_seqlens, int32_t* row_req,
+                                 int32_t* row_pos, int32_t* total_tier, int32_t* device_status,
+                                 hipStream_t stream) {
+  rva_status st = check_schedule(B, gamma, mode, hidden, hidden_dtype, H, head_w, conf_in, sts_T, alpha_ms,
+                                 alpha_len, theta_ms, theta_len, conf_out, surv_out, windows, K_out, ratio_out);
+  if (st != RVA_OK) return st;
+  rva::TierTable tt;
+  st = check_pack(B, gamma, windows, context_lens, tiers_host, n_tiers, src, row_bytes, dst, max_rows, cu_seqlens,
+                  row_req, row_pos, total_tier, &tt);
+  if (st != RVA_OK) return st;
+  return hip_result(rva::launch_schedule_pack(B, gamma, mode, hidden, hidden_dtype, H, head_w, head_b, conf_in,
+                                              sts_T, bias_ms, alpha_ms, theta_ms, conf_out, surv_out, windows,
+                                              K_out, ratio_out, context_lens, tt, src, row_bytes, dst, max_rows,
+                                              cu_seqlens, row_req, row_pos, total_tier, device_status, stream),
+                    "rva_schedule_and_pack launch");
 }
 
 size_t rva_verify_attention_workspace_size(int B, int max_window, int Hq, int Hkv, int D,

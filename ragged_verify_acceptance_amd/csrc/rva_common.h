@@ -75,6 +75,14 @@ hipError_t launch_pack(int B, int gamma, const int32_t* windows, const int32_t* 
                        int max_rows, int32_t* cu, int32_t* row_req, int32_t* row_pos,
                        int32_t* total_tier, int32_t* status, hipStream_t stream);
 
+hipError_t launch_schedule_pack(int B, int gamma, int mode, const void* hidden, int hidden_dtype, int H,
+                                const float* head_w, float head_b, const float* conf_in, const float* sts_T,
+                                float bias, const float* alpha, const float* theta, float* conf_out,
+                                float* surv_out, int32_t* windows, int32_t* K_out, double* ratio_out,
+                                const int32_t* context_lens, const TierTable& tiers, const void* src,
+                                size_t row_bytes, void* dst, int max_rows, int32_t* cu, int32_t* row_req,
+                                int32_t* row_pos, int32_t* total_tier, int32_t* status, hipStream_t stream);
+
 struct AttnArgs {
   int B, max_window, max_rows, Hq, Hkv, D, page_size, num_pages, max_pages;
   int log2_page;  // log2(page_size) when it is a power of two, else -1

@@ -19,6 +19,7 @@
 //                     (3) a workgroup scan in float64 gives S_K for every K;
 //                     (4) a workgroup argmax of (B + S_K) / T(B, K), smallest K on ties;
 //                     (5) LDS counters turn the first K* ranks into per-request windows.
+#include "pack_block.h"
 #include "rva_common.h"
 
 namespace rva {
@@ -78,92 +79,120 @@ __device__ __forceinline__ double block_exclusive_scan_f64(double v, double* lds
   return wave_off + x - v;
 }
 
-// Rank order of the candidates by merging sorted runs.  Each request's keys are already in
-// ascending order along its draft positions (survival never grows along a prefix, and the
-// candidate index breaks ties), so the B runs of G keys are merged pairwise, log2(B) rounds:
-// a key finds its place in the partner run by binary search (keys are unique), and lands at
-// pair start + its index in its own run + the partner keys below it.  One barrier a round.
-// `buf` holds two arrays of kMaxCand keys; returns the one that ends up sorted.  With invalid
-// confidences (a run not in order) the positions may collide; both arrays start with the keys,
-// so every slot still holds some candidate's key.
-template <int E, int NT>
-__device__ __forceinline__ const uint64_t* merge_runs(const uint64_t (&x)[E], uint64_t* buf, int N, int G) {
+// Rank order of the candidates by merging sorted runs.  A candidate's key is (h, i): h the
+// inverted bits of its survival, i its index; ascending keys are "survival desc, request asc,
+// position asc".  Each request's keys are already in order along its draft positions
+// (survival never grows along a prefix), so the B runs of G keys are merged pairwise,
+// log2(B) rounds, one barrier each.  In every round a run holds a contiguous range of
+// requests, so all of a left run's indices are below its right partner's: comparing h alone,
+// with ties going to the left run, gives the order of the full keys, and the searches read
+// 4-byte words.  Per key (one key a thread): a binary search in the partner run, then the
+// key lands at pair start + its index in its own run + the partner keys before it.  Several
+// keys a thread: merge path (a search along the diagonal, then a few outputs merged in
+// sequence).  Returns the set holding the sorted h and i arrays (`buf` holds two sets).
+// With invalid confidences (a run not in order) per-key positions may collide; both sets
+// start with the keys, so every slot still holds some candidate.
+template <int CAP>
+struct MergeBuf {
+  alignas(16) uint32_t h[2][CAP];
+  uint32_t i[2][CAP];
+};
+
+template <int E, int NT, int CAP>
+__device__ __forceinline__ int merge_runs(const uint32_t (&xh)[E], const uint32_t (&xi)[E], MergeBuf<CAP>& buf,
+                                          int N, int G) {
   const int tid = threadIdx.x;
-  uint64_t* cur = buf;
-  uint64_t* nxt = buf + kMaxCand;
+  int c = 0;  // current set
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int i = tid * E + e;
-    if (i < N) cur[i] = nxt[i] = x[e];
+    if (i < N) {
+      buf.h[0][i] = buf.h[1][i] = xh[e];
+      buf.i[0][i] = buf.i[1][i] = xi[e];
+    }
   }
   __syncthreads();
   for (int len = G; len < N; len <<= 1) {
+    const uint32_t* ch = buf.h[c];
+    const uint32_t* ci = buf.i[c];
+    uint32_t* nh = buf.h[c ^ 1];
+    uint32_t* ni = buf.i[c ^ 1];
     if constexpr (E > 1) {
-      // merge path: thread c writes kChunk consecutive outputs of one pair of runs, starting
-      // where a binary search along its diagonal puts it, then merges sequentially; far
-      // fewer scattered LDS probes than a search per key
       constexpr int kChunk = 4;
       const int per_pair = (2 * len + kChunk - 1) / kChunk;
       const int pairs = (N + 2 * len - 1) / (2 * len);
-      for (int c = tid; c < pairs * per_pair; c += NT) {
-        const int p = c / per_pair, a0 = p * 2 * len, b0 = a0 + len;
+      for (int t = tid; t < pairs * per_pair; t += NT) {
+        const int p = t / per_pair, a0 = p * 2 * len, b0 = a0 + len;
         const int lenA = min(len, N - a0), lenB = max(0, min(len, N - b0));
-        const int d0 = (c % per_pair) * kChunk, d1 = min(d0 + kChunk, lenA + lenB);
+        const int d0 = (t % per_pair) * kChunk, d1 = min(d0 + kChunk, lenA + lenB);
         if (d0 >= d1) continue;
         int lo = max(0, d0 - lenB), hi = min(d0, lenA);
         while (lo < hi) {  // smallest i whose A[i] is not among the first d0 outputs
           const int mid = (lo + hi) >> 1;
-          if (cur[a0 + mid] < cur[b0 + d0 - mid - 1]) lo = mid + 1; else hi = mid;
+          if (ch[a0 + mid] <= ch[b0 + d0 - mid - 1]) lo = mid + 1; else hi = mid;
         }
         int i = lo, j = d0 - lo;
         for (int d = d0; d < d1; ++d) {
-          const bool takeA = j >= lenB || (i < lenA && cur[a0 + i] < cur[b0 + j]);
-          nxt[a0 + d] = takeA ? cur[a0 + i++] : cur[b0 + j++];
+          const bool takeA = j >= lenB || (i < lenA && ch[a0 + i] <= ch[b0 + j]);
+          const int from = takeA ? a0 + i++ : b0 + j++;
+          nh[a0 + d] = ch[from];
+          ni[a0 + d] = ci[from];
         }
       }
     } else {
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const int i = tid * E + e;
-      if (i >= N) continue;
-      const uint64_t k = cur[i];
-      const int q = i / len, start = q * len;
-      const int ps = (q ^ 1) * len, pe = min(ps + len, N);
-      int pos = i;
-      if (ps < N) {
-        int lo = ps, hi = pe;
-        while (lo < hi) {
-          const int mid = (lo + hi) >> 1;
-          if (cur[mid] < k) lo = mid + 1; else hi = mid;
+      const int i = tid;
+      if (i < N) {
+        const uint32_t kh = ch[i], ki = ci[i];
+        const int q = i / len, start = q * len;
+        const int ps = (q ^ 1) * len, pe = min(ps + len, N);
+        int pos = i;
+        if (ps < N) {
+          const bool right = q & 1;  // partner keys with the same h come first
+          int lo = ps, hi = pe;
+          while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            const uint32_t v = ch[mid];
+            if (v < kh || (right && v == kh)) lo = mid + 1; else hi = mid;
+          }
+          pos = (q & ~1) * len + (i - start) + (lo - ps);
         }
-        pos = (q & ~1) * len + (i - start) + (lo - ps);
+        nh[pos] = kh;
+        ni[pos] = ki;
       }
-      nxt[pos] = k;
-    }
     }
     __syncthreads();
-    uint64_t* t = cur;
-    cur = nxt;
-    nxt = t;
+    c ^= 1;
   }
-  return cur;
+  return c;
 }
 
-// E keys per thread, NT threads (small batches take fewer waves: each merge round's
-// searches and barrier then involve fewer of them).
-template <int E, int NT>
-__global__ __launch_bounds__(NT) void schedule_kernel(
-    int B, int G, int mode, const float* __restrict__ conf, float* __restrict__ conf_out,
-    float* __restrict__ surv_out, float bias, const float* __restrict__ alpha,
-    const float* __restrict__ theta, int32_t* __restrict__ windows, int32_t* __restrict__ K_out,
-    double* __restrict__ ratio_out, int32_t* status) {
-  __shared__ uint64_t keybuf[2 * kMaxCand];
-  __shared__ float sa[kMaxCand];
-  __shared__ int cnt[kMaxCand];
-  __shared__ double wave_tot[NT / kWave];
-  __shared__ double red_ratio[NT / kWave];
-  __shared__ int red_K[NT / kWave];
+// LDS of one scheduling pass over up to CAP candidates.
+template <int NT, int CAP>
+struct SchedShared {
+  MergeBuf<CAP> mb;
+  float sa[CAP];
+  int cnt[CAP];  // per request: drafts in the window, then the window itself
+  double wave_tot[NT / kWave];
+  double red_ratio[NT / kWave];
+  int red_K[NT / kWave];
+};
 
+// The whole scheduling pass by one workgroup (E keys per thread, NT threads; small batches
+// take fewer waves, so each merge round's searches and barrier involve fewer of them).  On
+// return sh.cnt[b] holds request b's window.  `publish`: this workgroup writes the outputs
+// (conf echo, survival, windows, K*, ratio) and raises the status bits.
+template <int E, int NT, int CAP>
+__device__ __forceinline__ void schedule_block(SchedShared<NT, CAP>& sh, int B, int G, int mode,
+                                               const float* __restrict__ conf, float* __restrict__ conf_out,
+                                               float* __restrict__ surv_out, float bias,
+                                               const float* __restrict__ alpha, const float* __restrict__ theta,
+                                               int32_t* __restrict__ windows, int32_t* __restrict__ K_out,
+                                               double* __restrict__ ratio_out, int32_t* status, bool publish) {
+  float* sa = sh.sa;
+  int* cnt = sh.cnt;
+  double* wave_tot = sh.wave_tot;
+  double* red_ratio = sh.red_ratio;
+  int* red_K = sh.red_K;
   const int tid = threadIdx.x;
   const int N = B * G;
 
@@ -181,8 +210,8 @@ __global__ __launch_bounds__(NT) void schedule_kernel(
   // request forms the float32 products left to right
   for (int i = tid; i < N; i += NT) {
     const float c = conf[i];
-    if (!(c >= 0.f && c <= 1.f)) flag(status, RVA_DEV_BAD_CONF);
-    if (conf_out) conf_out[i] = c;
+    if (publish && !(c >= 0.f && c <= 1.f)) flag(status, RVA_DEV_BAD_CONF);
+    if (publish && conf_out) conf_out[i] = c;
     sa[i] = c;
   }
   __syncthreads();
@@ -197,19 +226,22 @@ __global__ __launch_bounds__(NT) void schedule_kernel(
   __syncthreads();
   // (2) sort keys (inverted survival bits, candidate index): ascending key order is
   // "survival desc, request asc, position asc"
-  uint64_t x[E];
+  uint32_t xh[E], xi[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int i = tid * E + e;
-    x[e] = ~0ull;
+    xh[e] = ~0u;
+    xi[e] = uint32_t(i);
     if (i < N) {
       const float a = sa[i];
-      surv_out[i] = a;
+      if (publish) surv_out[i] = a;
       const uint32_t bits = (a == 0.f) ? 0u : __float_as_uint(a);
-      x[e] = (uint64_t(~bits) << 32) | uint32_t(i);
+      xh[e] = ~bits;
     }
   }
-  const uint64_t* keys = merge_runs<E, NT>(x, keybuf, N, G);
+  const int set = merge_runs<E, NT, CAP>(xh, xi, sh.mb, N, G);
+  const uint32_t* key_h = sh.mb.h[set];
+  const uint32_t* key_i = sh.mb.i[set];
 
   // (3) S_K: each thread owns a contiguous run of ranks
   constexpr int per = E;
@@ -217,7 +249,7 @@ __global__ __launch_bounds__(NT) void schedule_kernel(
   double run = 0.0;
   for (int i = 0; i < per; ++i) {
     const int r = r0 + i;
-    if (r < N) run += double(__uint_as_float(~uint32_t(keys[r] >> 32)));
+    if (r < N) run += double(__uint_as_float(~key_h[r]));
   }
   double total;
   double prefix = block_exclusive_scan_f64<NT>(run, wave_tot, &total);
@@ -228,7 +260,7 @@ __global__ __launch_bounds__(NT) void schedule_kernel(
   int bestK = 0x7fffffff;
   if (tid == 0) {
     const double T0 = ba + double(theta_0);
-    if (!(T0 > 0.0)) flag(status, RVA_DEV_BAD_COST);
+    if (publish && !(T0 > 0.0)) flag(status, RVA_DEV_BAD_COST);
     best = T0 > 0.0 ? double(B) / T0 : -INFINITY;
     bestK = 0;
   }
@@ -237,9 +269,9 @@ __global__ __launch_bounds__(NT) void schedule_kernel(
   for (int i = 0; i < per; ++i) {
     const int r = r0 + i;
     if (r < N) {
-      S += double(__uint_as_float(~uint32_t(keys[r] >> 32)));
+      S += double(__uint_as_float(~key_h[r]));
       const double T = ba + double(th[i]);
-      if (!(T > 0.0)) flag(status, RVA_DEV_BAD_COST);
+      if (publish && !(T > 0.0)) flag(status, RVA_DEV_BAD_COST);
       const double ratio = T > 0.0 ? (double(B) + S) / T : -INFINITY;
       if (ratio > best) {
         best = ratio;
@@ -292,14 +324,87 @@ __global__ __launch_bounds__(NT) void schedule_kernel(
   // (5) windows from the first K* ranks
   for (int i = 0; i < per; ++i) {
     const int r = r0 + i;
-    if (r < Kstar && r < N) atomicAdd(&cnt[min(int(uint32_t(keys[r]) / uint32_t(G)), B - 1)], 1);
+    if (r < Kstar && r < N) atomicAdd(&cnt[min(int(key_i[r] / uint32_t(G)), B - 1)], 1);
   }
   __syncthreads();
-  for (int b = tid; b < B; b += NT) windows[b] = 1 + cnt[b];
-  if (tid == 0) {
+  for (int b = tid; b < B; b += NT) {
+    const int w = 1 + cnt[b];
+    cnt[b] = w;
+    if (publish) windows[b] = w;
+  }
+  if (publish && tid == 0) {
     *K_out = Kstar;
     *ratio_out = ratio;
   }
+  __syncthreads();
+}
+
+template <int E, int NT>
+__global__ __launch_bounds__(NT) void schedule_kernel(
+    int B, int G, int mode, const float* __restrict__ conf, float* __restrict__ conf_out,
+    float* __restrict__ surv_out, float bias, const float* __restrict__ alpha,
+    const float* __restrict__ theta, int32_t* __restrict__ windows, int32_t* __restrict__ K_out,
+    double* __restrict__ ratio_out, int32_t* status) {
+  __shared__ SchedShared<NT, kMaxCand> sh;
+  schedule_block<E, NT, kMaxCand>(sh, B, G, mode, conf, conf_out, surv_out, bias, alpha, theta, windows,
+                                  K_out, ratio_out, status, true);
+}
+
+// Stages 1 and 2 in one launch for batches of at most NT candidates: every workgroup runs
+// the (deterministic) scheduling pass itself, so all of them hold the same windows without
+// exchanging anything; workgroup 0 publishes the schedule, and each workgroup then packs its
+// own kRowsPerBlock(NT) destination rows.
+template <int NT>
+__global__ __launch_bounds__(NT) void schedule_pack_kernel(
+    int B, int G, int mode, const float* __restrict__ conf, float* __restrict__ conf_out,
+    float* __restrict__ surv_out, float bias, const float* __restrict__ alpha,
+    const float* __restrict__ theta, int32_t* __restrict__ windows, int32_t* __restrict__ K_out,
+    double* __restrict__ ratio_out, const int32_t* __restrict__ context_lens, TierTable tiers,
+    const uint8_t* __restrict__ src, size_t row_bytes, uint8_t* __restrict__ dst, int max_rows,
+    int32_t* __restrict__ cu_out, int32_t* __restrict__ row_req, int32_t* __restrict__ row_pos,
+    int32_t* __restrict__ total_tier, int32_t* status) {
+  __shared__ SchedShared<NT, NT> sh;
+  __shared__ PackShared<NT, NT> psh;
+  __shared__ int ctx[NT];
+  const bool first = blockIdx.x == 0;
+  // the context lengths (row positions) are requested now and land during the scheduling pass
+  const int ctx_v = int(threadIdx.x) < B ? context_lens[threadIdx.x] : 0;
+  schedule_block<1, NT, NT>(sh, B, G, mode, conf, conf_out, surv_out, bias, alpha, theta, windows, K_out,
+                            ratio_out, status, first);
+  if (int(threadIdx.x) < B) ctx[threadIdx.x] = ctx_v;  // published by pack_block's barrier
+  pack_block<NT, NT, kPackRows>(psh, B, G + 1, sh.cnt, false, ctx, tiers, src, row_bytes, dst, max_rows,
+                                cu_out, row_req, row_pos, total_tier, status, blockIdx.x, first);
+}
+
+}  // namespace
+
+namespace {
+
+// Stage 1's confidences: the head kernel's output when hidden states are given, else the
+// caller's; `echo` is where the schedule kernel copies caller confidences (nullptr when the
+// head wrote conf_out itself).
+hipError_t confidences(int B, int G, const void* hidden, int hidden_dtype, int H, const float* head_w,
+                       float head_b, const float* conf_in, const float* sts_T, float* conf_out,
+                       int32_t* status, hipStream_t stream, const float** conf, float** echo) {
+  const int rows = B * G;
+  *conf = conf_in;
+  *echo = conf_in ? conf_out : nullptr;
+  if (conf_in) return hipSuccess;
+  const dim3 grid((rows + 3) / 4), block(256);
+  if (hidden_dtype == RVA_BF16)
+    hipLaunchKernelGGL(conf_head_kernel<uint16_t>, grid, block, 0, stream, static_cast<const uint16_t*>(hidden),
+                       rows, G, H, head_w, head_b, sts_T, conf_out, status);
+  else
+    hipLaunchKernelGGL(conf_head_kernel<float>, grid, block, 0, stream, static_cast<const float*>(hidden), rows,
+                       G, H, head_w, head_b, sts_T, conf_out, status);
+  *conf = conf_out;
+  return hipGetLastError();
+}
+
+int pad_pow2(int n) {
+  int p = 2;
+  while (p < n) p <<= 1;
+  return p;
 }
 
 }  // namespace
@@ -311,26 +416,12 @@ hipError_t launch_schedule(int B, int gamma, int mode, const void* hidden, int h
                            int32_t* windows, int32_t* K_out, double* ratio_out,
                            int32_t* status, hipStream_t stream) {
   const int G = gamma - 1;
-  const int rows = B * G;
-  const float* conf = conf_in;
-  if (!conf_in) {
-    const dim3 grid((rows + 3) / 4), block(256);
-    if (hidden_dtype == RVA_BF16)
-      hipLaunchKernelGGL(conf_head_kernel<uint16_t>, grid, block, 0, stream,
-                         static_cast<const uint16_t*>(hidden), rows, G, H, head_w, head_b, sts_T,
-                         conf_out, status);
-    else
-      hipLaunchKernelGGL(conf_head_kernel<float>, grid, block, 0, stream,
-                         static_cast<const float*>(hidden), rows, G, H, head_w, head_b, sts_T,
-                         conf_out, status);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    conf = conf_out;
-  }
-  // conf_in is echoed into conf_out by the schedule kernel itself
-  float* echo = conf_in ? conf_out : nullptr;
-  int Npad = 2;
-  while (Npad < rows) Npad <<= 1;
+  const float* conf = nullptr;
+  float* echo = nullptr;
+  hipError_t e = confidences(B, G, hidden, hidden_dtype, H, head_w, head_b, conf_in, sts_T, conf_out, status,
+                             stream, &conf, &echo);
+  if (e != hipSuccess) return e;
+  const int Npad = pad_pow2(B * G);
   if (Npad <= 256)
     hipLaunchKernelGGL((schedule_kernel<1, 256>), dim3(1), dim3(256), 0, stream, B, G, mode,
                        conf, echo, surv_out, bias, alpha, theta, windows, K_out, ratio_out, status);
@@ -346,6 +437,45 @@ hipError_t launch_schedule(int B, int gamma, int mode, const void* hidden, int h
   else
     hipLaunchKernelGGL((schedule_kernel<4, kSchedThreads>), dim3(1), dim3(kSchedThreads), 0, stream, B, G,
                        mode, conf, echo, surv_out, bias, alpha, theta, windows, K_out, ratio_out, status);
+  return hipGetLastError();
+}
+
+hipError_t launch_schedule_pack(int B, int gamma, int mode, const void* hidden, int hidden_dtype, int H,
+                                const float* head_w, float head_b, const float* conf_in, const float* sts_T,
+                                float bias, const float* alpha, const float* theta, float* conf_out,
+                                float* surv_out, int32_t* windows, int32_t* K_out, double* ratio_out,
+                                const int32_t* context_lens, const TierTable& tiers, const void* src,
+                                size_t row_bytes, void* dst, int max_rows, int32_t* cu, int32_t* row_req,
+                                int32_t* row_pos, int32_t* total_tier, int32_t* status, hipStream_t stream) {
+  const int G = gamma - 1;
+  const int Npad = pad_pow2(B * G);
+  if (Npad > kSchedThreads) {  // more candidates than one workgroup's threads: two launches
+    hipError_t e = launch_schedule(B, gamma, mode, hidden, hidden_dtype, H, head_w, head_b, conf_in, sts_T, bias,
+                                   alpha, theta, conf_out, surv_out, windows, K_out, ratio_out, status, stream);
+    if (e != hipSuccess) return e;
+    return launch_pack(B, gamma, windows, context_lens, tiers, src, row_bytes, dst, max_rows, cu, row_req,
+                       row_pos, total_tier, status, stream);
+  }
+  const float* conf = nullptr;
+  float* echo = nullptr;
+  hipError_t e = confidences(B, G, hidden, hidden_dtype, H, head_w, head_b, conf_in, sts_T, conf_out, status,
+                             stream, &conf, &echo);
+  if (e != hipSuccess) return e;
+  const dim3 grid((max_rows + kPackRows - 1) / kPackRows);
+  const uint8_t* s8 = static_cast<const uint8_t*>(src);
+  uint8_t* d8 = static_cast<uint8_t*>(dst);
+  if (Npad <= 256)
+    hipLaunchKernelGGL(schedule_pack_kernel<256>, grid, dim3(256), 0, stream, B, G, mode, conf, echo, surv_out,
+                       bias, alpha, theta, windows, K_out, ratio_out, context_lens, tiers, s8, row_bytes, d8,
+                       max_rows, cu, row_req, row_pos, total_tier, status);
+  else if (Npad <= 512)
+    hipLaunchKernelGGL(schedule_pack_kernel<512>, grid, dim3(512), 0, stream, B, G, mode, conf, echo, surv_out,
+                       bias, alpha, theta, windows, K_out, ratio_out, context_lens, tiers, s8, row_bytes, d8,
+                       max_rows, cu, row_req, row_pos, total_tier, status);
+  else
+    hipLaunchKernelGGL(schedule_pack_kernel<kSchedThreads>, grid, dim3(kSchedThreads), 0, stream, B, G, mode,
+                       conf, echo, surv_out, bias, alpha, theta, windows, K_out, ratio_out, context_lens, tiers,
+                       s8, row_bytes, d8, max_rows, cu, row_req, row_pos, total_tier, status);
   return hipGetLastError();
 }
 

@@ -32,7 +32,7 @@ _STATUS = {0: "RVA_OK", 1: "RVA_ERR_INVALID_ARGUMENT", 2: "RVA_ERR_UNSUPPORTED",
            3: "RVA_ERR_WORKSPACE_TOO_SMALL", 4: "RVA_ERR_HIP"}
 
 EXPORTED = [
-    "rva_schedule_windows", "rva_pack_ragged", "rva_verify_attention",
+    "rva_schedule_windows", "rva_pack_ragged", "rva_schedule_and_pack", "rva_verify_attention",
     "rva_verify_attention_workspace_size", "rva_verify_attention_noalloc", "rva_accept_and_commit",
     "rva_accept_workspace_size", "rva_confidence_labels", "rva_accept_capped", "rva_sts_fit",
     "rva_sts_fit_workspace_size", "rva_calibration_ece", "rva_calibration_ece_workspace_size",
@@ -54,6 +54,8 @@ _SIGS = {
     "rva_schedule_windows": [_i, _i, _i, _p, _i, _i, _p, _f, _p, _p, _f, _p, _i, _p, _i,
                              _p, _p, _p, _p, _p, _p, _p],
     "rva_pack_ragged": [_i, _i, _p, _p, _p, _i, _p, _z, _p, _i, _p, _p, _p, _p, _p, _p],
+    "rva_schedule_and_pack": [_i, _i, _i, _p, _i, _i, _p, _f, _p, _p, _f, _p, _i, _p, _i, _p, _p, _p,
+                              _p, _p, _p, _p, _i, _p, _z, _p, _i, _p, _p, _p, _p, _p, _p],
     "rva_verify_attention": [_i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p,
                              _p, _p, _f, _p, _p, _p, _z, _p],
     "rva_verify_attention_workspace_size": [_i, _i, _i, _i, _i, _i, _i, _i],
@@ -146,18 +148,39 @@ def schedule_windows(B, gamma, mode, hidden, H, head_w, head_b, conf_in, sts_T, 
 def pack_ragged(B, gamma, windows, context_lens, tiers, src, dst, max_rows, cu_seqlens,
                 row_req, row_pos, total_tier, device_status=None, stream=None):
     t = (ctypes.c_int32 * len(tiers))(*[int(x) for x in tiers])
-    row_bytes = 0
-    if src is not None:
-        # src is [>= B, gamma, ...] (only the first B blocks are read); a row is one block
-        # position's trailing elements
-        if src.dim() < 2 or src.shape[0] < B or src.shape[1] != gamma or not src.is_contiguous():
-            raise ValueError(f"pack source must be contiguous [>= {B}, {gamma}, ...], "
-                             f"got {tuple(src.shape)}")
-        row_bytes = src.element_size() * (src.numel() // (src.shape[0] * gamma))
-        if dst is None or dst.element_size() * (dst.numel() // max(1, dst.shape[0])) != row_bytes:
-            raise ValueError("pack destination rows must have the source's row size")
+    row_bytes = _pack_row_bytes(B, gamma, src, dst)
     _check("rva_pack_ragged", lib().rva_pack_ragged(
         B, gamma, _ptr(windows), _ptr(context_lens), ctypes.cast(t, ctypes.c_void_p), len(tiers),
+        _ptr(src), row_bytes, _ptr(dst), max_rows, _ptr(cu_seqlens), _ptr(row_req),
+        _ptr(row_pos), _ptr(total_tier), _ptr(device_status), _stream(stream)))
+
+
+def _pack_row_bytes(B, gamma, src, dst):
+    if src is None:
+        return 0
+    # src is [>= B, gamma, ...] (only the first B blocks are read); a row is one block
+    # position's trailing elements
+    if src.dim() < 2 or src.shape[0] < B or src.shape[1] != gamma or not src.is_contiguous():
+        raise ValueError(f"pack source must be contiguous [>= {B}, {gamma}, ...], "
+                         f"got {tuple(src.shape)}")
+    row_bytes = src.element_size() * (src.numel() // (src.shape[0] * gamma))
+    if dst is None or dst.element_size() * (dst.numel() // max(1, dst.shape[0])) != row_bytes:
+        raise ValueError("pack destination rows must have the source's row size")
+    return row_bytes
+
+
+def schedule_and_pack(B, gamma, mode, hidden, H, head_w, head_b, conf_in, sts_T, bias_ms,
+                      alpha_ms, theta_ms, conf_out, surv_out, windows, K_out, ratio_out,
+                      context_lens, tiers, src, dst, max_rows, cu_seqlens, row_req, row_pos,
+                      total_tier, device_status=None, stream=None):
+    hd = dtype_code(hidden) if hidden is not None else BF16
+    t = (ctypes.c_int32 * len(tiers))(*[int(x) for x in tiers])
+    row_bytes = _pack_row_bytes(B, gamma, src, dst)
+    _check("rva_schedule_and_pack", lib().rva_schedule_and_pack(
+        B, gamma, mode, _ptr(hidden), hd, H, _ptr(head_w), float(head_b), _ptr(conf_in),
+        _ptr(sts_T), float(bias_ms), _ptr(alpha_ms), alpha_ms.numel(), _ptr(theta_ms),
+        theta_ms.numel(), _ptr(conf_out), _ptr(surv_out), _ptr(windows), _ptr(K_out),
+        _ptr(ratio_out), _ptr(context_lens), ctypes.cast(t, ctypes.c_void_p), len(tiers),
         _ptr(src), row_bytes, _ptr(dst), max_rows, _ptr(cu_seqlens), _ptr(row_req),
         _ptr(row_pos), _ptr(total_tier), _ptr(device_status), _stream(stream)))
 

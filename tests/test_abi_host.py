@@ -29,7 +29,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     L = rva.lib()
     names = declared_functions()
-    assert "rva_verify_attention" in names and len(names) == 17
+    assert "rva_verify_attention" in names and len(names) == 18
     for n in names:
         assert hasattr(L, n), f"{n} declared in rva.h but not exported"
     assert set(names) == set(rva.EXPORTED)
@@ -85,6 +85,31 @@ def _pack(B=3, gamma=6, tiers=(4, 8, 12, 18), max_rows=18, src=None, dst=None, w
 ])
 def test_pack_validation(kw, code):
     assert _pack(**kw) == code
+
+
+def _sched_pack(B=3, gamma=6, mode=0, conf_in=FAKE, alpha_len=4, theta_len=19, tiers=(4, 8, 12, 18),
+                max_rows=18, src=None, dst=None, windows=FAKE):
+    t = (ctypes.c_int32 * len(tiers))(*tiers)
+    return rva.lib().rva_schedule_and_pack(B, gamma, mode, None, 1, 0, None, 0.0, conf_in, None, 20.0, FAKE,
+                                           alpha_len, FAKE, theta_len, FAKE, FAKE, windows, FAKE, FAKE, FAKE,
+                                           ctypes.cast(t, ctypes.c_void_p), len(tiers), src, 16 if src else 0,
+                                           dst, max_rows, FAKE, FAKE, FAKE, FAKE, None, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), INVALID),                      # both stages reject it
+    (dict(gamma=65), INVALID),                 # the schedule's limit
+    (dict(mode=3), INVALID),
+    (dict(conf_in=None), INVALID),             # neither hidden nor conf_in
+    (dict(alpha_len=3), INVALID),              # alpha_len must exceed B
+    (dict(tiers=(4, 12, 8, 18)), INVALID),     # the pack's checks: tiers not ascending
+    (dict(max_rows=17), INVALID),
+    (dict(src=FAKE), INVALID),                 # src without dst
+    (dict(windows=None), INVALID),
+])
+def test_schedule_and_pack_validation(kw, code):
+    assert _sched_pack(**kw) == code
+    assert rva.lib().rva_last_error().decode() != ""
 
 
 def _attn(B=2, max_window=6, max_rows=16, Hq=32, Hkv=8, D=128, page=64, num_pages=10, max_pages=5,

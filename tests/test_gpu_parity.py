@@ -112,6 +112,44 @@ def test_pack(ds, mode):
     assert _status(ds) == 0
 
 
+@pytest.mark.parametrize("mode", ["compact", "static"])
+def test_schedule_and_pack(ds, mode):
+    """The one-launch stages 1 + 2 write exactly what the two calls write (every output, bit
+    for bit, status included), and the packed rows follow the oracle."""
+    name = ds.wl.name
+    print(f"[schedule+pack] {name} {mode}", flush=True)
+    ds.mode = 1 if mode == "static" else 0
+    ds.restore()
+    outs = [ds.conf_out, ds.surv_out, ds.windows, ds.K_out, ds.ratio_out, ds.cu, ds.row_req,
+            ds.row_pos, ds.total_tier, ds.pack_dst, ds.status]
+    ds.status.zero_()
+    ds.pack_dst.fill_(7)
+    ds.schedule()
+    ds.pack()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outs]
+    for t in outs[:-2]:
+        t.fill_(3 if t.dtype != torch.bfloat16 else 5)
+    ds.pack_dst.fill_(7)
+    ds.status.zero_()
+    ds.schedule_pack()
+    torch.cuda.synchronize()
+    ds.mode = 0
+    for t, r in zip(outs, ref):
+        assert torch.equal(t.view(torch.uint8) if t.dtype == torch.bfloat16 else t,
+                           r.view(torch.uint8) if r.dtype == torch.bfloat16 else r), t.shape
+    w = to_np(ds.windows)
+    res = oracle.pack_ragged(w, ds.inp.context_lens, ds.tiers,
+                             ds.pack_src.cpu().view(torch.int16).numpy(), max_rows=ds.max_rows)
+    assert np.array_equal(to_np(ds.cu), res["cu_seqlens"])
+    got = ds.pack_dst.cpu().view(torch.int16).numpy()
+    assert np.array_equal(got[: res["tier"]], res["dst"][: res["tier"]])
+    ref_s = oracle_schedule(ds.inp, static=(mode == "static"))
+    if not ref_s["near_tie"]:
+        assert np.array_equal(w, ref_s["windows"])
+    assert _status(ds) == 0
+
+
 def _check_attention(ds, windows, reqs, out):
     ref, app, _ = oracle_attention(ds.inp, windows, reqs)
     cu = to_np(ds.cu)

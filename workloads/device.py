@@ -125,6 +125,17 @@ class DeviceStep:
                         dst, self.max_rows, self.cu, self.row_req, self.row_pos,
                         self.total_tier, self.status)
 
+    def schedule_pack(self):
+        """Stages 1 and 2 in one call (rva_schedule_and_pack): the same outputs as
+        schedule() followed by pack()."""
+        wl = self.wl
+        rva.schedule_and_pack(self.B, wl.gamma, self.mode, self.hidden, wl.head_H, self.head_w,
+                              self.head_b, self.conf_in, None, self.bias, self.alpha, self.theta,
+                              self.conf_out, self.surv_out, self.windows, self.K_out,
+                              self.ratio_out, self.context_lens, self.tiers, self.pack_src,
+                              self.pack_dst, self.max_rows, self.cu, self.row_req, self.row_pos,
+                              self.total_tier, self.status)
+
     def attention(self):
         wl, inp = self.wl, self.inp
         rva.verify_attention(self.B, wl.gamma, self.max_rows, wl.Hq, wl.Hkv, wl.D, wl.page,
@@ -205,9 +216,8 @@ class DeviceStep:
         self.windows, self.windows_next = self.windows_next, self.windows
 
     def step(self, labels=True):
-        """One pass of the whole path: stages 1, 2, 3 and 4 (+5)."""
-        self.schedule()
-        self.pack()
+        """One pass of the whole path: stages 1 + 2 (one call), 3 and 4 (+5)."""
+        self.schedule_pack()
         self.attention()
         self.accept(labels=labels)
 
