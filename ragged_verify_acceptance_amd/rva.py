@@ -87,7 +87,8 @@ def lib(path: str | None = None):
     global _lib
     if _lib is not None:
         return _lib
-    path = path or LIB_PATH
+    # RVA_LIBRARY: another build of the same library (the host-sanitizer build of the tests)
+    path = path or os.environ.get("RVA_LIBRARY") or LIB_PATH
     if not os.path.exists(path):
         raise RuntimeError(f"librva.so not found at {path}: build it first "
                            "(python -c 'import __graft_entry__ as g; g.build()')")
