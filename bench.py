@@ -673,6 +673,12 @@ def main():
         res["cap_accept"] = {"accepted_drafts_capped": acc, "accepted_drafts_uncapped": full,
                              "utilisation": acc / max(1, full),
                              "mean_cap_window": float(caps.mean())}
+    # windows per traffic class (requests are assigned to classes round-robin)
+    hist = {}
+    for ci, cl in enumerate(wl.classes):
+        ws = windows[np.asarray(inp.classes) == ci]
+        hist[f"class{ci} Beta({cl.a:g},{cl.b:g})"] = [int((ws == w).sum()) for w in range(1, wl.gamma + 1)]
+    res["window_histogram"] = {"windows": list(range(1, wl.gamma + 1)), "per_class": hist}
     if args.mode == "compact" and graph is None and flush is None and not args.no_static:
         res["static"] = static_arm(inp, args.steps, args.warmup, stream)
     if args.cpu_sample > 0:

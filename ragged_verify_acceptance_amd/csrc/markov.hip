@@ -36,7 +36,9 @@ namespace rva {
 namespace {
 
 constexpr int kMkThreads = 256;
-constexpr int kTileV = 128;          // vocabulary entries per workgroup
+constexpr int kCB = 2;               // 16-token column blocks per wave
+constexpr int kTileV = 4 * kCB * 16;  // vocabulary entries per workgroup (4 waves)
+constexpr int kLaneTok = kTileV / kWave;  // tokens per lane in the draw's tile rescan
 constexpr int kReqGroup = 64;        // requests per MFMA pass (4 row blocks of 16)
 constexpr int kSampleThreads = 256;
 
@@ -120,10 +122,10 @@ __global__ __launch_bounds__(kMkThreads, VEC ? 4 : 1) void markov_logits_kernel(
 
   // this wave's two 16-token column blocks of q2 as the MFMA's A operand: lane row c16 is
   // token v0 + 16 (2 wave + cb) + c16, 64 bytes of r per lane (quarter g)
-  long afrag[2][kSteps];
+  long afrag[kCB][kSteps];
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
-    const int v = min(v0 + (2 * wave + cb) * 16 + c16, a.V - 1);
+  for (int cb = 0; cb < kCB; ++cb) {
+    const int v = min(v0 + (kCB * wave + cb) * 16 + c16, a.V - 1);
     const int8_t* row = a.w2 + size_t(v) * R + g * kQ;
 #pragma unroll
     for (int s = 0; s < kSteps; s += 2) {
@@ -138,10 +140,10 @@ __global__ __launch_bounds__(kMkThreads, VEC ? 4 : 1) void markov_logits_kernel(
   float* tmax = reinterpret_cast<float*>(static_cast<char*>(a.ws) + l.off_max);
   double* tsum = reinterpret_cast<double*>(static_cast<char*>(a.ws) + l.off_sum);
   // the scales of this lane's 8 tokens (4 per column block)
-  float s2v[2][4];
+  float s2v[kCB][4];
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
-    const int vb = v0 + (2 * wave + cb) * 16 + 4 * g;
+  for (int cb = 0; cb < kCB; ++cb) {
+    const int vb = v0 + (kCB * wave + cb) * 16 + 4 * g;
     if constexpr (VEC) {
       const float4 w = *reinterpret_cast<const float4*>(a.s2 + min(vb, a.V - 4));
       s2v[cb][0] = w.x; s2v[cb][1] = w.y; s2v[cb][2] = w.z; s2v[cb][3] = w.w;
@@ -157,12 +159,12 @@ __global__ __launch_bounds__(kMkThreads, VEC ? 4 : 1) void markov_logits_kernel(
     // the epilogue's base logits, requested before the MFMA and kept in their storage
     // format (bf16 pairs stay packed: half the registers)
     constexpr int kU = sizeof(T) == 2 ? 2 : 4;
-    uint32_t uv[4][2][kU];
+    uint32_t uv[4][kCB][kU];
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        const int rl = rb * 16 + c16, vb = v0 + (2 * wave + cb) * 16 + 4 * g;
+      for (int cb = 0; cb < kCB; ++cb) {
+        const int rl = rb * 16 + c16, vb = v0 + (kCB * wave + cb) * 16 + 4 * g;
         if constexpr (VEC) {
           // rows past the batch and tokens past V read a valid place; their values are unused
           const size_t base = (size_t(b0 + min(rl, nb - 1)) * a.G1 + k) * a.V + min(vb, a.V - 4);
@@ -205,22 +207,25 @@ __global__ __launch_bounds__(kMkThreads, VEC ? 4 : 1) void markov_logits_kernel(
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
       const int rl = rb * 16 + c16;
-      v4i acc[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+      v4i acc[kCB];
+#pragma unroll
+      for (int cb = 0; cb < kCB; ++cb) acc[cb] = v4i{0, 0, 0, 0};
       const int8_t* erow = sE + rl * kEPitch + g * kQ;
 #pragma unroll
       for (int s = 0; s < kSteps; ++s) {
         const long bv = *reinterpret_cast<const long*>(erow + s * 8);
-        acc[0] = __builtin_amdgcn_mfma_i32_16x16x32_i8(afrag[0][s], bv, acc[0], 0, 0, 0);
-        acc[1] = __builtin_amdgcn_mfma_i32_16x16x32_i8(afrag[1][s], bv, acc[1], 0, 0, 0);
+#pragma unroll
+        for (int cb = 0; cb < kCB; ++cb)
+          acc[cb] = __builtin_amdgcn_mfma_i32_16x16x32_i8(afrag[cb][s], bv, acc[cb], 0, 0, 0);
       }
       // logits of request rl at this lane's 8 tokens, and their (max, mass) summary
       const double s1 = double(sS1[rl]);
       const size_t base = (size_t(b0 + rl) * a.G1 + k) * a.V;
-      float lv[2][4];
+      float lv[kCB][4];
       float m = -INFINITY;
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        const int vb = v0 + (2 * wave + cb) * 16 + 4 * g;
+      for (int cb = 0; cb < kCB; ++cb) {
+        const int vb = v0 + (kCB * wave + cb) * 16 + 4 * g;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int v = vb + i;
@@ -257,7 +262,7 @@ __global__ __launch_bounds__(kMkThreads, VEC ? 4 : 1) void markov_logits_kernel(
       double sum = 0.0;
       if (m != -INFINITY) {
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
+        for (int cb = 0; cb < kCB; ++cb)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             if (lv[cb][i] != -INFINITY) sum += exp2_tab(P, tab, (double(lv[cb][i]) - double(m)) * kLog2eF64);
@@ -346,13 +351,18 @@ __global__ __launch_bounds__(kSampleThreads) void markov_sample_kernel(MarkovArg
   }
   __syncthreads();
   if (wave != 0) return;
-  // rescan the tile: lane j takes tokens 2j, 2j+1
+  // rescan the tile: lane j takes its kLaneTok consecutive tokens
   const int t = s_tile;
   const T* O = static_cast<const T*>(a.out);
   const size_t base = (size_t(b) * a.G1 + k) * a.V;
-  const int v = t * kTileV + 2 * lane;
-  const double e0 = v < a.V ? ex(Out<T>::load(O, base + v), M) : 0.0;
-  const double e1 = v + 1 < a.V ? ex(Out<T>::load(O, base + v + 1), M) : 0.0;
+  const int v = t * kTileV + kLaneTok * lane;
+  double e[kLaneTok];
+  double own = 0.0;
+#pragma unroll
+  for (int i = 0; i < kLaneTok; ++i) {
+    e[i] = v + i < a.V ? ex(Out<T>::load(O, base + v + i), M) : 0.0;
+    own += e[i];
+  }
   double c0;
   if (s_before >= 0.0) {
     c0 = s_before;
@@ -360,17 +370,20 @@ __global__ __launch_bounds__(kSampleThreads) void markov_sample_kernel(MarkovArg
     // the last tile after a rounding overshoot: its start is S minus its own mass
     c0 = S - tsum[t] * ex(tmax[t], M);
   }
-  double pinc = e0 + e1;
+  double pinc = own;
 #pragma unroll
   for (int o = 1; o < kWave; o <<= 1) {
     const double vv = __shfl_up(pinc, o);
     if (lane >= o) pinc += vv;
   }
-  const double cA = c0 + (pinc - e0 - e1) + e0;  // cumulative through token v
-  const double cB = c0 + pinc;                   // through token v + 1
+  // cumulative mass through each of this lane's tokens, in token order
+  double cum = c0 + (pinc - own);
   int cand = a.V;                                 // smallest token whose cumulative passes
-  if (v < a.V && cA > target) cand = v;
-  else if (v + 1 < a.V && cB > target) cand = v + 1;
+#pragma unroll
+  for (int i = 0; i < kLaneTok; ++i) {
+    cum += e[i];
+    if (cand == a.V && v + i < a.V && cum > target) cand = v + i;
+  }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) cand = min(cand, __shfl_xor(cand, o));
   if (cand == a.V) {

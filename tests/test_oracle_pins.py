@@ -302,6 +302,77 @@ def test_attention_against_torch_sdpa(page, lens):
     assert np.all(out[int(case["cu_seqlens"][-1]):] == 0)
 
 
+@pytest.mark.parametrize("page", [32, 64, 16])
+def test_attention_cache_layout_from_logical(page):
+    """The cache layout pinned from the other side: logical context K/V [L, D] per (request,
+    kv head) are written into pages by whole-page reshapes (K page = the [page, D] block of
+    its positions; V page = that block cut into column blocks of VB slots and transposed
+    to [page/VB, D, VB], as the header states the layout), never by the oracle's element
+    index.  The oracle's output must equal torch SDPA on the logical K/V, and the window
+    it appends must read back, by the inverse reshape, at positions L .. L+w-1."""
+    rng = np.random.default_rng(13)
+    B, Hq, Hkv, D = 3, 4, 2, 8
+    lens, windows = (0, 40, 77), (2, 3, 4)
+    VB = oracle.attention.v_block(page)
+    need = [(L + w + page - 1) // page for L, w in zip(lens, windows)]
+    P = sum(need) + 2
+    perm = rng.permutation(P)
+    bt = np.zeros((B, max(need)), np.int32)
+    k = 0
+    for b in range(B):
+        for j in range(need[b]):
+            bt[b, j] = perm[k]
+            k += 1
+    k_cache = rng.standard_normal((P, Hkv, page, D))   # untouched slots keep noise
+    v_cache = rng.standard_normal((P, Hkv, page // VB, D, VB))
+    logical = {}
+    for b in range(B):
+        for g in range(Hkv):
+            Kl = rng.standard_normal((lens[b], D))
+            Vl = rng.standard_normal((lens[b], D))
+            logical[b, g] = (Kl, Vl)
+            for j in range((lens[b] + page - 1) // page):
+                n = min(page, lens[b] - j * page)
+                kb = k_cache[bt[b, j], g].copy()
+                kb[:n] = Kl[j * page: j * page + n]
+                k_cache[bt[b, j], g] = kb
+                vb = v_cache[bt[b, j], g].transpose(0, 2, 1).reshape(page, D).copy()  # [slot, d]
+                vb[:n] = Vl[j * page: j * page + n]
+                v_cache[bt[b, j], g] = vb.reshape(page // VB, VB, D).transpose(0, 2, 1)
+    cu = np.concatenate([[0], np.cumsum(windows)]).astype(np.int32)
+    R = int(cu[-1])
+    q = rng.standard_normal((R, Hq, D))
+    k_new = rng.standard_normal((R, Hkv, D))
+    v_new = rng.standard_normal((R, Hkv, D))
+    scale = np.float32(1 / math.sqrt(D))
+    out, kc, vc = oracle.verify_attention(q, k_new, v_new, k_cache.copy(), v_cache.copy(), bt,
+                                          np.array(lens, np.int32), cu, R, scale)
+    G = Hq // Hkv
+    for b in range(B):
+        r0, r1 = int(cu[b]), int(cu[b + 1])
+        w = r1 - r0
+        for h in range(Hq):
+            g = h // G
+            Kl, Vl = logical[b, g]
+            K = np.concatenate([Kl, k_new[r0:r1, g]])
+            V = np.concatenate([Vl, v_new[r0:r1, g]])
+            mask = np.ones((w, lens[b] + w), bool)
+            for i in range(w):
+                mask[i, lens[b] + i + 1:] = False
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                torch.from_numpy(q[r0:r1, h][None]), torch.from_numpy(K[None]), torch.from_numpy(V[None]),
+                attn_mask=torch.from_numpy(mask[None]), scale=float(scale))[0].numpy()
+            assert np.allclose(out[r0:r1, h], ref, rtol=1e-10, atol=1e-12), (page, b, h)
+        # the appended window, read back page by page with the inverse reshape
+        for g in range(Hkv):
+            for i in range(w):
+                p = lens[b] + i
+                pg, s = bt[b, p // page], p % page
+                vpage = vc[pg, g].transpose(0, 2, 1).reshape(page, D)
+                assert np.array_equal(kc[pg, g, s], k_new[r0 + i, g])
+                assert np.array_equal(vpage[s], v_new[r0 + i, g])
+
+
 def test_attention_special_cases():
     """Single visible key -> its value; zero query -> mean of the visible values;
     GQA equals MHA with every kv head repeated; physical page order is irrelevant."""
