@@ -366,14 +366,54 @@ __global__ __launch_bounds__(NT) void schedule_pack_kernel(
   __shared__ SchedShared<NT, NT> sh;
   __shared__ PackShared<NT, NT> psh;
   __shared__ int ctx[NT];
+  const int tid = threadIdx.x, gamma = G + 1;
   const bool first = blockIdx.x == 0;
   // the context lengths (row positions) are requested now and land during the scheduling pass
-  const int ctx_v = int(threadIdx.x) < B ? context_lens[threadIdx.x] : 0;
+  const int ctx_v = tid < B ? context_lens[tid] : 0;
+  // So are this block's kPackRows SOURCE rows (request-major, row s = b gamma + i; the
+  // grid covers max_rows >= B gamma of them): once the windows are known, row s goes to
+  // destination row cu[b] + i when i < w_b.  Rows of up to 2 NT x 16 bytes, 16-byte aligned;
+  // others are copied destination-first after the pass (pack_block).
+  const int n16 = int(row_bytes / 16);
+  const bool pre = src && row_bytes % 16 == 0 && n16 <= 2 * NT &&
+                   ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) % 16 == 0);
+  uint4 v[kPackRows][2];
+#pragma unroll
+  for (int rr = 0; rr < kPackRows; ++rr)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int srow = blockIdx.x * kPackRows + rr, k = h * NT + tid;
+      v[rr][h] = (pre && srow < B * gamma && k < n16)
+                     ? reinterpret_cast<const uint4*>(src + size_t(srow) * row_bytes)[k]
+                     : make_uint4(0, 0, 0, 0);
+    }
   schedule_block<1, NT, NT>(sh, B, G, mode, conf, conf_out, surv_out, bias, alpha, theta, windows, K_out,
                             ratio_out, status, first);
-  if (int(threadIdx.x) < B) ctx[threadIdx.x] = ctx_v;  // published by pack_block's barrier
-  pack_block<NT, NT, kPackRows>(psh, B, G + 1, sh.cnt, false, ctx, tiers, src, row_bytes, dst, max_rows,
-                                cu_out, row_req, row_pos, total_tier, status, blockIdx.x, first);
+  if (tid < B) ctx[tid] = ctx_v;  // published by pack_block's barrier
+  pack_block<NT, NT, kPackRows>(psh, B, gamma, sh.cnt, false, ctx, tiers, pre ? nullptr : src, row_bytes,
+                                pre ? nullptr : dst, max_rows, cu_out, row_req, row_pos, total_tier, status,
+                                blockIdx.x, first);
+  if (!pre) return;
+  const int M = psh.s_M, tier = psh.s_tier;
+#pragma unroll
+  for (int rr = 0; rr < kPackRows; ++rr) {
+    const int srow = blockIdx.x * kPackRows + rr;
+    const int b = srow / gamma, i = srow % gamma;
+    if (srow < B * gamma && i < psh.cu[b + 1] - psh.cu[b]) {
+      uint4* d = reinterpret_cast<uint4*>(dst + size_t(psh.cu[b] + i) * row_bytes);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        if (h * NT + tid < n16) d[h * NT + tid] = v[rr][h];
+    }
+    // this block's destination rows in [M, tier) are pad rows: zero
+    const int r = blockIdx.x * kPackRows + rr;
+    if (r >= M && r < tier && r < max_rows) {
+      uint4* d = reinterpret_cast<uint4*>(dst + size_t(r) * row_bytes);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        if (h * NT + tid < n16) d[h * NT + tid] = make_uint4(0, 0, 0, 0);
+    }
+  }
 }
 
 }  // namespace
