@@ -112,7 +112,10 @@ typedef enum { RVA_MODE_COMPACT = 0, RVA_MODE_STATIC = 1 } rva_mode;
  *   sts_T           [gamma-1] float32 temperatures (> 0) or NULL.
  *   bias_ms         float32 scalar; alpha_ms [alpha_len] with alpha_len > B;
  *                   theta_ms [theta_len] with theta_len > B*gamma (device, float32).
- *   conf_out, surv_out  [B, gamma-1] float32 outputs (c and a).
+ *   conf_out, surv_out  [B, gamma-1] float32 outputs (c and a).  Above 1024 candidates the
+ *                   call is two launches and surv_out carries the candidates' ranks (as bits)
+ *                   from the first to the second, which then writes a: like every output, it
+ *                   holds its result once the call's work on `stream` is done.
  *   windows         [B] int32 output; K_out [1] int32; ratio_out [1] float64 (E over T at K*).
  *   device_status   optional int32 word (RVA_DEV_BAD_CONF, RVA_DEV_BAD_COST).
  */

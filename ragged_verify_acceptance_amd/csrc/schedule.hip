@@ -5,17 +5,22 @@
 // throughput-maximising prefix scheduler); the devpress.csdn.net DSpark-in-SGLang article,
 // section 4 (additive step cost T(bs, K) = bias + alpha(bs) + theta(bs + K)).
 //
-// Two kernels:
+// Kernels:
 //   conf_head_kernel  one wave per (request, draft position): float64 dot product of the
 //                     hidden state with the head weights, + bias, / T_k, logistic in
 //                     float64, rounded to float32.  Skipped when the caller supplies c.
+//   rank_kernel       batches of more than 1024 candidates only: the rank order of (2)
+//                     below, one workgroup per request, each key ranked by binary searches
+//                     in the other requests' runs (the ordering work of one workgroup
+//                     would bound the whole pass on one compute unit).
 //   schedule_kernel   ONE workgroup (256 to 1024 threads, by batch size) for the whole batch:
 //                     (1) one lane per request forms the survival product left to right
 //                         in float32 (bit-identical to a sequential definition);
-//                     (2) 64-bit keys (inverted survival bits, candidate index) order
-//                         "survival desc, request asc, position asc" in one comparison;
-//                         each request's keys are already in order, so the rank order is
-//                         a merge of B sorted runs (log2 B rounds, a binary search per key);
+//                     (2) keys (inverted survival bits, candidate index) order "survival
+//                         desc, request asc, position asc"; each request's keys are already
+//                         in order, so the rank order is a merge of B sorted runs (log2 B
+//                         rounds, a binary search per key), or, after rank_kernel, the
+//                         keys are stored at their ranks;
 //                     (3) a workgroup scan in float64 gives S_K for every K;
 //                     (4) a workgroup argmax of (B + S_K) / T(B, K), smallest K on ties;
 //                     (5) LDS counters turn the first K* ranks into per-request windows.
@@ -26,6 +31,7 @@ namespace rva {
 namespace {
 
 constexpr int kSchedThreads = 1024;
+constexpr int kRankThreads = 1024;
 constexpr int kMaxCand = 4096;
 
 template <typename T>
@@ -51,33 +57,81 @@ __global__ __launch_bounds__(256) void conf_head_kernel(const T* __restrict__ hi
   }
 }
 
+// Cross-lane moves inside a wave by DPP (no LDS round trip): row_shr:n moves each lane's
+// value n lanes up inside its row of 16; row_bcast:15 hands the last lane of rows 0 and 2 to
+// rows 1 and 3, row_bcast:31 hands lane 31 to rows 2 and 3 (GFX9 controls).  Lanes with no
+// source, and rows outside ROW_MASK, get `id`.
+constexpr int kDppRowShr = 0x110, kDppBcast15 = 0x142, kDppBcast31 = 0x143;
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_i32(int id, int x) {
+  return __builtin_amdgcn_update_dpp(id, x, CTRL, ROW_MASK, 0xf, false);
+}
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ double dpp_f64(double id, double x) {
+  const int lo = dpp_i32<CTRL, ROW_MASK>(__double2loint(id), __double2loint(x));
+  const int hi = dpp_i32<CTRL, ROW_MASK>(__double2hiint(id), __double2hiint(x));
+  return __hiloint2double(hi, lo);
+}
+
+// Inclusive float64 prefix sum over the wave's lanes: log steps inside each row, then the
+// two row broadcasts.  Lane 63 ends with the wave's total.
+__device__ __forceinline__ double wave_inclusive_sum_f64(double x) {
+  x += dpp_f64<kDppRowShr + 1, 0xf>(0.0, x);
+  x += dpp_f64<kDppRowShr + 2, 0xf>(0.0, x);
+  x += dpp_f64<kDppRowShr + 4, 0xf>(0.0, x);
+  x += dpp_f64<kDppRowShr + 8, 0xf>(0.0, x);
+  x += dpp_f64<kDppBcast15, 0xa>(0.0, x);
+  x += dpp_f64<kDppBcast31, 0xc>(0.0, x);
+  return x;
+}
+
+// One step of the argmax prefix: the moved (ratio, K) replaces this lane's when its ratio is
+// larger, or equal with a smaller K.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ void argmax_step(double& best, int& bestK) {
+  const double o = dpp_f64<CTRL, ROW_MASK>(-INFINITY, best);
+  const int ok = dpp_i32<CTRL, ROW_MASK>(0x7fffffff, bestK);
+  if (o > best || (o == best && ok < bestK)) {
+    best = o;
+    bestK = ok;
+  }
+}
+
+// Wave argmax in the same pattern; lane 63 ends with the wave's best (ratio, K).
+__device__ __forceinline__ void wave_argmax(double& best, int& bestK) {
+  argmax_step<kDppRowShr + 1, 0xf>(best, bestK);
+  argmax_step<kDppRowShr + 2, 0xf>(best, bestK);
+  argmax_step<kDppRowShr + 4, 0xf>(best, bestK);
+  argmax_step<kDppRowShr + 8, 0xf>(best, bestK);
+  argmax_step<kDppBcast15, 0xa>(best, bestK);
+  argmax_step<kDppBcast31, 0xc>(best, bestK);
+}
+
+// Exclusive float64 prefix sum over the workgroup (one barrier): a DPP scan inside each wave,
+// then every thread adds the totals of the waves before its own, in wave order, from LDS.
+// *total: the sum of all wave totals (same order for every thread).
 template <int NT>
 __device__ __forceinline__ double block_exclusive_scan_f64(double v, double* lds_waves,
                                                            double* total) {
-  // Inclusive scan inside the wave, then across the NT / 64 wave totals.
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  double x = v;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const double y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
+  const double x = wave_inclusive_sum_f64(v);
   if (lane == kWave - 1) lds_waves[wave] = x;
   __syncthreads();
-  if (wave == 0) {
-    double t = lane < NT / kWave ? lds_waves[lane] : 0.0;
+  double off = 0.0, tot = 0.0;
 #pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const double y = __shfl_up(t, o);
-      if (lane >= o) t += y;
-    }
-    if (lane < NT / kWave) lds_waves[lane] = t;  // inclusive wave prefix
+  for (int k = 0; k < NT / kWave; ++k) {
+    if (k == wave) off = tot;
+    tot += lds_waves[k];
   }
-  __syncthreads();
-  const double wave_off = wave > 0 ? lds_waves[wave - 1] : 0.0;
-  *total = lds_waves[NT / kWave - 1];
-  return wave_off + x - v;
+  *total = tot;
+  return off + x - v;
 }
+
+// Sort key of a survival: its bits inverted (+0 for -0), so that ascending keys are
+// descending survivals.
+__device__ __forceinline__ uint32_t sort_key(float a) { return ~((a == 0.f) ? 0u : __float_as_uint(a)); }
 
 // Rank order of the candidates by merging sorted runs.  A candidate's key is (h, i): h the
 // inverted bits of its survival, i its index; ascending keys are "survival desc, request asc,
@@ -86,10 +140,9 @@ __device__ __forceinline__ double block_exclusive_scan_f64(double v, double* lds
 // log2(B) rounds, one barrier each.  In every round a run holds a contiguous range of
 // requests, so all of a left run's indices are below its right partner's: comparing h alone,
 // with ties going to the left run, gives the order of the full keys, and the searches read
-// 4-byte words.  Per key (one key a thread): a binary search in the partner run, then the
-// key lands at pair start + its index in its own run + the partner keys before it.  Several
-// keys a thread: merge path (a search along the diagonal, then a few outputs merged in
-// sequence).  Returns the set holding the sorted h and i arrays (`buf` holds two sets).
+// 4-byte words.  One key a thread (N <= NT): a binary search in the partner run, then the
+// key lands at pair start + its index in its own run + the partner keys before it.  Returns
+// the set holding the sorted h and i arrays (`buf` holds two sets).
 // With invalid confidences (a run not in order) per-key positions may collide; both sets
 // start with the keys, so every slot still holds some candidate.
 template <int CAP>
@@ -98,18 +151,13 @@ struct MergeBuf {
   uint32_t i[2][CAP];
 };
 
-template <int E, int NT, int CAP>
-__device__ __forceinline__ int merge_runs(const uint32_t (&xh)[E], const uint32_t (&xi)[E], MergeBuf<CAP>& buf,
-                                          int N, int G) {
+template <int CAP>
+__device__ __forceinline__ int merge_runs(uint32_t xh, uint32_t xi, MergeBuf<CAP>& buf, int N, int G) {
   const int tid = threadIdx.x;
   int c = 0;  // current set
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int i = tid * E + e;
-    if (i < N) {
-      buf.h[0][i] = buf.h[1][i] = xh[e];
-      buf.i[0][i] = buf.i[1][i] = xi[e];
-    }
+  if (tid < N) {
+    buf.h[0][tid] = buf.h[1][tid] = xh;
+    buf.i[0][tid] = buf.i[1][tid] = xi;
   }
   __syncthreads();
   for (int len = G; len < N; len <<= 1) {
@@ -117,48 +165,24 @@ __device__ __forceinline__ int merge_runs(const uint32_t (&xh)[E], const uint32_
     const uint32_t* ci = buf.i[c];
     uint32_t* nh = buf.h[c ^ 1];
     uint32_t* ni = buf.i[c ^ 1];
-    if constexpr (E > 1) {
-      constexpr int kChunk = 4;
-      const int per_pair = (2 * len + kChunk - 1) / kChunk;
-      const int pairs = (N + 2 * len - 1) / (2 * len);
-      for (int t = tid; t < pairs * per_pair; t += NT) {
-        const int p = t / per_pair, a0 = p * 2 * len, b0 = a0 + len;
-        const int lenA = min(len, N - a0), lenB = max(0, min(len, N - b0));
-        const int d0 = (t % per_pair) * kChunk, d1 = min(d0 + kChunk, lenA + lenB);
-        if (d0 >= d1) continue;
-        int lo = max(0, d0 - lenB), hi = min(d0, lenA);
-        while (lo < hi) {  // smallest i whose A[i] is not among the first d0 outputs
+    const int i = tid;
+    if (i < N) {
+      const uint32_t kh = ch[i], ki = ci[i];
+      const int q = i / len, start = q * len;
+      const int ps = (q ^ 1) * len, pe = min(ps + len, N);
+      int pos = i;
+      if (ps < N) {
+        const bool right = q & 1;  // partner keys with the same h come first
+        int lo = ps, hi = pe;
+        while (lo < hi) {
           const int mid = (lo + hi) >> 1;
-          if (ch[a0 + mid] <= ch[b0 + d0 - mid - 1]) lo = mid + 1; else hi = mid;
+          const uint32_t v = ch[mid];
+          if (v < kh || (right && v == kh)) lo = mid + 1; else hi = mid;
         }
-        int i = lo, j = d0 - lo;
-        for (int d = d0; d < d1; ++d) {
-          const bool takeA = j >= lenB || (i < lenA && ch[a0 + i] <= ch[b0 + j]);
-          const int from = takeA ? a0 + i++ : b0 + j++;
-          nh[a0 + d] = ch[from];
-          ni[a0 + d] = ci[from];
-        }
+        pos = (q & ~1) * len + (i - start) + (lo - ps);
       }
-    } else {
-      const int i = tid;
-      if (i < N) {
-        const uint32_t kh = ch[i], ki = ci[i];
-        const int q = i / len, start = q * len;
-        const int ps = (q ^ 1) * len, pe = min(ps + len, N);
-        int pos = i;
-        if (ps < N) {
-          const bool right = q & 1;  // partner keys with the same h come first
-          int lo = ps, hi = pe;
-          while (lo < hi) {
-            const int mid = (lo + hi) >> 1;
-            const uint32_t v = ch[mid];
-            if (v < kh || (right && v == kh)) lo = mid + 1; else hi = mid;
-          }
-          pos = (q & ~1) * len + (i - start) + (lo - ps);
-        }
-        nh[pos] = kh;
-        ni[pos] = ki;
-      }
+      nh[pos] = kh;
+      ni[pos] = ki;
     }
     __syncthreads();
     c ^= 1;
@@ -177,11 +201,15 @@ struct SchedShared {
   int red_K[NT / kWave];
 };
 
-// The whole scheduling pass by one workgroup (E keys per thread, NT threads; small batches
-// take fewer waves, so each merge round's searches and barrier involve fewer of them).  On
-// return sh.cnt[b] holds request b's window.  `publish`: this workgroup writes the outputs
-// (conf echo, survival, windows, K*, ratio) and raises the status bits.
-template <int E, int NT, int CAP>
+// The whole scheduling pass by one workgroup over N = B G candidates, E a thread (NT threads;
+// small batches take fewer waves, so each merge round's searches and barrier involve fewer of
+// them).  kRanked = false (N <= NT, E = 1): the rank order comes from merge_runs.  kRanked =
+// true: rank_kernel ran first and left every candidate's rank in surv_out (as bits), and has
+// validated and echoed the confidences; the keys are stored at their ranks and surv_out is
+// overwritten with the survivals.  On return sh.cnt[b] holds request b's window.  `publish`:
+// this workgroup writes the outputs (conf echo, survival, windows, K*, ratio) and raises the
+// status bits.
+template <int E, int NT, int CAP, bool kRanked>
 __device__ __forceinline__ void schedule_block(SchedShared<NT, CAP>& sh, int B, int G, int mode,
                                                const float* __restrict__ conf, float* __restrict__ conf_out,
                                                float* __restrict__ surv_out, float bias,
@@ -195,7 +223,18 @@ __device__ __forceinline__ void schedule_block(SchedShared<NT, CAP>& sh, int B, 
   int* red_K = sh.red_K;
   const int tid = threadIdx.x;
   const int N = B * G;
+  static_assert(kRanked || E == 1, "the merge takes one key a thread");
 
+  // ranks from rank_kernel, requested now (this thread's own candidates, read before it
+  // writes their survivals)
+  uint32_t rk[E];
+  if constexpr (kRanked) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int i = tid * E + e;
+      rk[e] = i < N ? __float_as_uint(surv_out[i]) : 0u;
+    }
+  }
   // the cost table entries this thread needs later (rank r = tid*E + e uses theta[B + r + 1])
   // are loaded now, so their round trip overlaps the survival products and the sort
   float th[E];
@@ -210,8 +249,8 @@ __device__ __forceinline__ void schedule_block(SchedShared<NT, CAP>& sh, int B, 
   // request forms the float32 products left to right
   for (int i = tid; i < N; i += NT) {
     const float c = conf[i];
-    if (publish && !(c >= 0.f && c <= 1.f)) flag(status, RVA_DEV_BAD_CONF);
-    if (publish && conf_out) conf_out[i] = c;
+    if (!kRanked && publish && !(c >= 0.f && c <= 1.f)) flag(status, RVA_DEV_BAD_CONF);
+    if (!kRanked && publish && conf_out) conf_out[i] = c;
     sa[i] = c;
   }
   __syncthreads();
@@ -226,31 +265,56 @@ __device__ __forceinline__ void schedule_block(SchedShared<NT, CAP>& sh, int B, 
   __syncthreads();
   // (2) sort keys (inverted survival bits, candidate index): ascending key order is
   // "survival desc, request asc, position asc"
-  uint32_t xh[E], xi[E];
+  int set = 0;
+  if constexpr (kRanked) {
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int i = tid * E + e;
-    xh[e] = ~0u;
-    xi[e] = uint32_t(i);
+    for (int e = 0; e < E; ++e) {
+      const int i = tid * E + e;
+      if (i < N) {
+        const float a = sa[i];
+        if (publish) surv_out[i] = a;
+        const uint32_t r = rk[e];
+        if (r < uint32_t(N)) {  // a permutation of [0, N) for valid confidences
+          sh.mb.h[0][r] = sort_key(a);
+          sh.mb.i[0][r] = uint32_t(i);
+        }
+      }
+    }
+    __syncthreads();
+  } else {
+    const int i = tid;
+    uint32_t xh = ~0u;
     if (i < N) {
       const float a = sa[i];
       if (publish) surv_out[i] = a;
-      const uint32_t bits = (a == 0.f) ? 0u : __float_as_uint(a);
-      xh[e] = ~bits;
+      xh = sort_key(a);
     }
+    set = merge_runs<CAP>(xh, uint32_t(i), sh.mb, N, G);
   }
-  const int set = merge_runs<E, NT, CAP>(xh, xi, sh.mb, N, G);
   const uint32_t* key_h = sh.mb.h[set];
   const uint32_t* key_i = sh.mb.i[set];
 
-  // (3) S_K: each thread owns a contiguous run of ranks
+  // (3) S_K: each thread owns a contiguous run of ranks, read as 16-byte words when it can
   constexpr int per = E;
   const int r0 = tid * per;
-  double run = 0.0;
-  for (int i = 0; i < per; ++i) {
-    const int r = r0 + i;
-    if (r < N) run += double(__uint_as_float(~key_h[r]));
+  uint32_t kh[per];
+  if (per % 4 == 0 && r0 + per <= N) {
+#pragma unroll
+    for (int i = 0; i < per; i += 4) {
+      const uint4 q = *reinterpret_cast<const uint4*>(&key_h[r0 + i]);
+      kh[i] = q.x;
+      kh[i + 1] = q.y;
+      kh[i + 2] = q.z;
+      kh[i + 3] = q.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < per; ++i) kh[i] = r0 + i < N ? key_h[r0 + i] : ~0u;
   }
+  double run = 0.0;
+#pragma unroll
+  for (int i = 0; i < per; ++i)
+    if (r0 + i < N) run += double(__uint_as_float(~kh[i]));
   double total;
   double prefix = block_exclusive_scan_f64<NT>(run, wave_tot, &total);
 
@@ -269,7 +333,7 @@ __device__ __forceinline__ void schedule_block(SchedShared<NT, CAP>& sh, int B, 
   for (int i = 0; i < per; ++i) {
     const int r = r0 + i;
     if (r < N) {
-      S += double(__uint_as_float(~key_h[r]));
+      S += double(__uint_as_float(~kh[i]));
       const double T = ba + double(th[i]);
       if (publish && !(T > 0.0)) flag(status, RVA_DEV_BAD_COST);
       const double ratio = T > 0.0 ? (double(B) + S) / T : -INFINITY;
@@ -279,42 +343,28 @@ __device__ __forceinline__ void schedule_block(SchedShared<NT, CAP>& sh, int B, 
       }
     }
   }
-  // workgroup argmax: larger ratio wins, smaller K on equal ratio
+  // workgroup argmax: larger ratio wins, smaller K on equal ratio.  DPP inside each wave,
+  // then every thread folds the per-wave bests itself, in wave order (one barrier)
   const int lane = tid % kWave, wave = tid / kWave;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const double ob = __shfl_xor(best, o);
-    const int ok = __shfl_xor(bestK, o);
-    if (ob > best || (ob == best && ok < bestK)) {
-      best = ob;
-      bestK = ok;
-    }
-  }
-  if (lane == 0) {
+  wave_argmax(best, bestK);
+  if (lane == kWave - 1) {
     red_ratio[wave] = best;
     red_K[wave] = bestK;
   }
   __syncthreads();
-  if (wave == 0) {
-    best = lane < NT / kWave ? red_ratio[lane] : -INFINITY;
-    bestK = lane < NT / kWave ? red_K[lane] : 0x7fffffff;
+  best = -INFINITY;
+  bestK = 0x7fffffff;
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const double ob = __shfl_xor(best, o);
-      const int ok = __shfl_xor(bestK, o);
-      if (ob > best || (ob == best && ok < bestK)) {
-        best = ob;
-        bestK = ok;
-      }
-    }
-    if (lane == 0) {
-      red_ratio[0] = best;
-      red_K[0] = bestK;
+  for (int k = 0; k < NT / kWave; ++k) {
+    const double o = red_ratio[k];
+    const int ok = red_K[k];
+    if (o > best || (o == best && ok < bestK)) {
+      best = o;
+      bestK = ok;
     }
   }
-  __syncthreads();
-  int Kstar = red_K[0];
-  double ratio = red_ratio[0];
+  int Kstar = bestK;
+  double ratio = best;
   if (mode == RVA_MODE_STATIC) {
     Kstar = N;
     const double T = ba + double(theta_N);
@@ -339,15 +389,87 @@ __device__ __forceinline__ void schedule_block(SchedShared<NT, CAP>& sh, int B, 
   __syncthreads();
 }
 
-template <int E, int NT>
+template <int E, int NT, bool kRanked>
 __global__ __launch_bounds__(NT) void schedule_kernel(
     int B, int G, int mode, const float* __restrict__ conf, float* __restrict__ conf_out,
     float* __restrict__ surv_out, float bias, const float* __restrict__ alpha,
     const float* __restrict__ theta, int32_t* __restrict__ windows, int32_t* __restrict__ K_out,
     double* __restrict__ ratio_out, int32_t* status) {
   __shared__ SchedShared<NT, kMaxCand> sh;
-  schedule_block<E, NT, kMaxCand>(sh, B, G, mode, conf, conf_out, surv_out, bias, alpha, theta, windows,
-                                  K_out, ratio_out, status, true);
+  schedule_block<E, NT, kMaxCand, kRanked>(sh, B, G, mode, conf, conf_out, surv_out, bias, alpha, theta,
+                                           windows, K_out, ratio_out, status, true);
+}
+
+// Ranks for batches of more than one workgroup's threads, spread over B workgroups (one per
+// request) so that the ordering work runs on many compute units instead of one.  Every
+// workgroup forms all N survivals in LDS (the float32 products of the single-workgroup pass)
+// and turns them into sort keys.  Key j of this workgroup's request b then has rank
+//   j + sum over requests b' != b of (keys of b' that come before it),
+// each count a binary search in the run of b' (a run is in ascending key order; on equal
+// survival the lower request comes first).  Ranks go to surv_out as bits; schedule_kernel
+// <E, NT, true> stores the keys at their ranks and overwrites surv_out with the survivals.
+// Request b's workgroup also validates and echoes request b's confidences.
+template <int NT>
+__global__ __launch_bounds__(NT) void rank_kernel(int B, int G, const float* __restrict__ conf,
+                                                  float* __restrict__ conf_out, float* __restrict__ surv_out,
+                                                  int32_t* status) {
+  __shared__ uint32_t key[kMaxCand];
+  __shared__ int acc[64];  // G <= 63
+  const int tid = threadIdx.x, b = blockIdx.x, N = B * G;
+  if (tid < G) {
+    acc[tid] = 0;
+    const float c = conf[b * G + tid];
+    if (!(c >= 0.f && c <= 1.f)) flag(status, RVA_DEV_BAD_CONF);
+    if (conf_out) conf_out[b * G + tid] = c;
+  }
+  for (int i = tid; i < N; i += NT) key[i] = __float_as_uint(conf[i]);
+  __syncthreads();
+  for (int r = tid; r < B; r += NT) {
+    float a = 1.f;
+    for (int j = 0; j < G; ++j) {
+      const float c = __uint_as_float(key[r * G + j]);
+      a = (j == 0) ? c : __fmul_rn(a, c);
+      key[r * G + j] = sort_key(a);
+    }
+  }
+  __syncthreads();
+  // thread (group g, position j) counts against the runs g, g + P, ... (P groups of G
+  // threads), four runs at a time so that their searches overlap
+  const int P = NT / G, j = tid % G, g = tid / G;
+  if (g < P) {
+    const uint32_t x = key[b * G + j];
+    int top = 1;  // largest power of two <= G
+    while (2 * top <= G) top *= 2;
+    int count = 0;
+    for (int r0 = g; r0 < B; r0 += 4 * P) {
+      int lo[4], base[4];
+      bool before[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int rr = r0 + u * P;
+        lo[u] = 0;
+        base[u] = min(rr, B - 1) * G;
+        before[u] = rr < b;
+      }
+      // lo = keys of the run before x: a search over powers of two, reads clamped into the run
+      for (int step = top; step > 0; step >>= 1) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int q = lo[u] + step;
+          const uint32_t v = key[base[u] + min(q, G) - 1];
+          if (q <= G && (v < x || (before[u] && v == x))) lo[u] = q;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int rr = r0 + u * P;
+        if (rr < B && rr != b) count += lo[u];
+      }
+    }
+    atomicAdd(&acc[j], count);
+  }
+  __syncthreads();
+  if (tid < G) surv_out[b * G + tid] = __uint_as_float(uint32_t(tid + acc[tid]));
 }
 
 // Stages 1 and 2 in one launch for batches of at most NT candidates: every workgroup runs
@@ -387,7 +509,7 @@ __global__ __launch_bounds__(NT) void schedule_pack_kernel(
                      ? reinterpret_cast<const uint4*>(src + size_t(srow) * row_bytes)[k]
                      : make_uint4(0, 0, 0, 0);
     }
-  schedule_block<1, NT, NT>(sh, B, G, mode, conf, conf_out, surv_out, bias, alpha, theta, windows, K_out,
+  schedule_block<1, NT, NT, false>(sh, B, G, mode, conf, conf_out, surv_out, bias, alpha, theta, windows, K_out,
                             ratio_out, status, first);
   if (tid < B) ctx[tid] = ctx_v;  // published by pack_block's barrier
   pack_block<NT, NT, kPackRows>(psh, B, gamma, sh.cnt, false, ctx, tiers, pre ? nullptr : src, row_bytes,
@@ -463,20 +585,25 @@ hipError_t launch_schedule(int B, int gamma, int mode, const void* hidden, int h
   if (e != hipSuccess) return e;
   const int Npad = pad_pow2(B * G);
   if (Npad <= 256)
-    hipLaunchKernelGGL((schedule_kernel<1, 256>), dim3(1), dim3(256), 0, stream, B, G, mode,
+    hipLaunchKernelGGL((schedule_kernel<1, 256, false>), dim3(1), dim3(256), 0, stream, B, G, mode,
                        conf, echo, surv_out, bias, alpha, theta, windows, K_out, ratio_out, status);
   else if (Npad <= 512)
-    hipLaunchKernelGGL((schedule_kernel<1, 512>), dim3(1), dim3(512), 0, stream, B, G, mode,
+    hipLaunchKernelGGL((schedule_kernel<1, 512, false>), dim3(1), dim3(512), 0, stream, B, G, mode,
                        conf, echo, surv_out, bias, alpha, theta, windows, K_out, ratio_out, status);
   else if (Npad <= kSchedThreads)
-    hipLaunchKernelGGL((schedule_kernel<1, kSchedThreads>), dim3(1), dim3(kSchedThreads), 0, stream, B, G,
-                       mode, conf, echo, surv_out, bias, alpha, theta, windows, K_out, ratio_out, status);
-  else if (Npad <= 2 * kSchedThreads)
-    hipLaunchKernelGGL((schedule_kernel<2, kSchedThreads>), dim3(1), dim3(kSchedThreads), 0, stream, B, G,
-                       mode, conf, echo, surv_out, bias, alpha, theta, windows, K_out, ratio_out, status);
-  else
-    hipLaunchKernelGGL((schedule_kernel<4, kSchedThreads>), dim3(1), dim3(kSchedThreads), 0, stream, B, G,
-                       mode, conf, echo, surv_out, bias, alpha, theta, windows, K_out, ratio_out, status);
+    hipLaunchKernelGGL((schedule_kernel<1, kSchedThreads, false>), dim3(1), dim3(kSchedThreads), 0, stream, B,
+                       G, mode, conf, echo, surv_out, bias, alpha, theta, windows, K_out, ratio_out, status);
+  else {
+    // ranks on B workgroups, then the scan / argmax / windows on one
+    hipLaunchKernelGGL((rank_kernel<kRankThreads>), dim3(B), dim3(kRankThreads), 0, stream, B, G, conf, echo,
+                       surv_out, status);
+    if (Npad <= 2 * kSchedThreads)
+      hipLaunchKernelGGL((schedule_kernel<2, kSchedThreads, true>), dim3(1), dim3(kSchedThreads), 0, stream, B,
+                         G, mode, conf, echo, surv_out, bias, alpha, theta, windows, K_out, ratio_out, status);
+    else
+      hipLaunchKernelGGL((schedule_kernel<4, kSchedThreads, true>), dim3(1), dim3(kSchedThreads), 0, stream, B,
+                         G, mode, conf, echo, surv_out, bias, alpha, theta, windows, K_out, ratio_out, status);
+  }
   return hipGetLastError();
 }
 

@@ -1,7 +1,8 @@
 """GPU edge cases through the C ABI, each against the oracle.
 
-Covers shapes the five workloads do not reach: scheduler candidate counts on every sort
-layout (up to 1024, 2048 and 4096 candidates), heavy survival ties, the confidence head
+Covers shapes the five workloads do not reach: scheduler candidate counts on both ordering
+paths (the one-workgroup merge up to 1024 candidates; the ranking spread over one workgroup
+per request beyond, with 2 and 4 keys a thread after it), heavy survival ties, the confidence head
 with per-position temperatures (bf16 and f32 hidden states), single-draft and
 single-request batches, acceptance batches whose windows are all 1 (no drafts: every
 request takes the bonus draw) or all gamma, cap-accept with caps of 1, random and the whole
@@ -56,7 +57,8 @@ def _schedule_case(B, gamma, conf, theta_per_token, static=False):
                                      (64, 64)])
 @pytest.mark.parametrize("kind", ["beta", "ties"])
 def test_schedule_sizes(B, gamma, kind):
-    """Candidate counts 1 .. 4032 (every register layout of the sort), with and without ties."""
+    """Candidate counts 1 .. 4032 (every ordering path and keys-a-thread layout), with and without
+    ties."""
     print(f"[schedule-size] B={B} gamma={gamma} {kind}", flush=True)
     rng = np.random.default_rng(B * 100 + gamma)
     G = gamma - 1
