@@ -16,14 +16,15 @@
 //
 // Per position, two launches:
 //  * markov_logits_kernel: one workgroup per 128-token vocabulary tile.  Its four waves
-//    hold the tile's q2 rows in registers as the MFMA's A operand (64 contiguous bytes per
-//    lane: lane group g takes the g-th quarter of r, and the B operand -- q1[x_b] of 64
-//    requests at a time, gathered into LDS -- walks r in the same order, so each MFMA pairs
-//    matching k; an integer sum does not care about the order), and run
-//    v_mfma_i32_16x16x32_i8.  With tokens as the MFMA rows each lane ends with 4
-//    consecutive tokens of one request, so the epilogue reads U and writes the logits
-//    straight from the accumulators (U is requested before the MFMA), and each request's
-//    tile max and float64 mass below it are merged over lanes and waves for the draw.
+//    hold the tile's q2 rows in registers as the MFMA's A operand and run
+//    v_mfma_i32_16x16x32_i8 against the B operand, q1[x_b] of 64 requests at a time
+//    gathered into LDS.  Both operands walk r in one permuted order (an integer sum does
+//    not care about the order), chosen so that the four lanes of a q2 row load 64
+//    contiguous bytes per instruction.  The A rows of a wave's column blocks interleave
+//    their tokens so that each lane ends with 8 consecutive tokens of one request: the
+//    epilogue reads U (requested before the MFMA) and writes the logits 16 bytes at a
+//    time straight from the accumulators, and each request's tile max and float64 mass
+//    below it are merged over lanes and waves for the draw.
 //  * markov_sample_kernel: one workgroup per request combines the tile statistics into
 //    the row's maximum and total mass, finds the tile where the cumulative mass passes
 //    u * S (block scan of per-thread tile runs), and rescans that tile with one wave.
@@ -106,8 +107,7 @@ __global__ __launch_bounds__(256) void markov_stage_kernel(MarkovArgs a, MkLayou
 template <typename T, int R, bool VEC>
 __global__ __launch_bounds__(kMkThreads, VEC ? 4 : 1) void markov_logits_kernel(MarkovArgs a, MkLayout l, int k,
                                                                                   Exp2Poly P) {
-  constexpr int kQ = R / 4;            // bytes of r per lane group
-  constexpr int kSteps = kQ / 8;       // MFMA k-steps (8 bytes per lane each)
+  constexpr int kSteps = R / 32;       // MFMA k-steps (8 bytes per lane each)
   constexpr int kEPitch = R + 8;       // LDS row pitch of the gathered embeddings (8-aligned)
   constexpr int kW = kMkThreads / kWave;
   __shared__ __align__(16) int8_t sE[kReqGroup * kEPitch];
@@ -120,16 +120,69 @@ __global__ __launch_bounds__(kMkThreads, VEC ? 4 : 1) void markov_logits_kernel(
   const int v0 = blockIdx.x * kTileV;
   if (tid < 256) tab[tid] = exp2_f64(P, double(tid) / 256.0);  // read after the barriers below
 
-  // this wave's two 16-token column blocks of q2 as the MFMA's A operand: lane row c16 is
-  // token v0 + 16 (2 wave + cb) + c16, 64 bytes of r per lane (quarter g)
+  // The staged q1[x_b] rows (16 bytes per piece) and scales of a request group; rows past
+  // the batch repeat its last row (their results are never used).  The first group's are
+  // requested before anything else: their stores then wait for them alone (the wait
+  // counter drains in order), not for the q2 and U loads behind them.
+  const int8_t* estage = static_cast<const int8_t*>(a.ws) + l.off_e;
+  const float* s1stage = reinterpret_cast<const float*>(static_cast<const char*>(a.ws) + l.off_s1);
+  constexpr int kEIt = kReqGroup * (R / 16) / kMkThreads;  // 16-byte pieces per thread
+  static_assert(kEIt * kMkThreads == kReqGroup * (R / 16), "whole pieces per thread");
+  uint4 ev[kEIt];
+  float s1v;
+  auto stage_load = [&](int b0, int nb) {
+#pragma unroll
+    for (int j = 0; j < kEIt; ++j) {
+      const int it = tid + j * kMkThreads, rl = it / (R / 16), c = it % (R / 16);
+      ev[j] = *reinterpret_cast<const uint4*>(estage + size_t(b0 + min(rl, nb - 1)) * R + c * 16);
+    }
+    s1v = s1stage[b0 + min(tid % kReqGroup, nb - 1)];
+  };
+  auto stage_store = [&]() {
+#pragma unroll
+    for (int j = 0; j < kEIt; ++j) {
+      const int it = tid + j * kMkThreads, rl = it / (R / 16), c = it % (R / 16);
+      uint2* dst = reinterpret_cast<uint2*>(sE + rl * kEPitch + c * 16);
+      dst[0] = make_uint2(ev[j].x, ev[j].y);
+      dst[1] = make_uint2(ev[j].z, ev[j].w);
+    }
+    if (tid < kReqGroup) sS1[tid] = s1v;
+  };
+  stage_load(0, min(kReqGroup, a.B));
+  const int vw = v0 + kCB * 16 * wave;
+  // the scales of this lane's 4 kCB consecutive tokens (4 per column block)
+  const int vl = vw + 4 * kCB * g;  // this lane's first token
+  float s2v[kCB][4];
+#pragma unroll
+  for (int cb = 0; cb < kCB; ++cb) {
+    const int vb = vl + 4 * cb;
+    if constexpr (VEC) {
+      const float4 w = *reinterpret_cast<const float4*>(a.s2 + min(vb, a.V - 4));
+      s2v[cb][0] = w.x; s2v[cb][1] = w.y; s2v[cb][2] = w.z; s2v[cb][3] = w.w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s2v[cb][i] = a.s2[min(vb + i, a.V - 1)];
+    }
+  }
+  // keep the compiler from moving these loads behind the q2 loads (or the s1 load into the
+  // store's branch): the stores, and the scales' conversions, would then wait for q2 too
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+
+  // this wave's kCB 16-token column blocks of q2 as the MFMA's A operand.  Row rho of block
+  // cb is token vw + 4 kCB (rho / 4) + 4 cb + rho % 4 (vw: the wave's first token), so the
+  // result rows 4g..4g+3 of every block are the kCB*4 consecutive tokens vw + 4 kCB g + ...
+  // of one lane.  k order: step s takes bytes 64 (s / 2) + 16 g + 8 (s % 2) of r (every byte
+  // once; the B operand below walks the same order), so lanes g = 0..3 of a row load 64
+  // contiguous bytes per instruction.
   long afrag[kCB][kSteps];
 #pragma unroll
   for (int cb = 0; cb < kCB; ++cb) {
-    const int v = min(v0 + (kCB * wave + cb) * 16 + c16, a.V - 1);
-    const int8_t* row = a.w2 + size_t(v) * R + g * kQ;
+    const int v = min(vw + 4 * kCB * (c16 / 4) + 4 * cb + c16 % 4, a.V - 1);
+    const int8_t* row = a.w2 + size_t(v) * R + g * 16;
 #pragma unroll
     for (int s = 0; s < kSteps; s += 2) {
-      const uint4 w = *reinterpret_cast<const uint4*>(row + s * 8);
+      const uint4 w = *reinterpret_cast<const uint4*>(row + (s / 2) * 64);
       afrag[cb][s] = (long(w.y) << 32) | long(uint32_t(w.x));
       afrag[cb][s + 1] = (long(w.w) << 32) | long(uint32_t(w.z));
     }
@@ -139,39 +192,41 @@ __global__ __launch_bounds__(kMkThreads, VEC ? 4 : 1) void markov_logits_kernel(
   T* O = static_cast<T*>(a.out);
   float* tmax = reinterpret_cast<float*>(static_cast<char*>(a.ws) + l.off_max);
   double* tsum = reinterpret_cast<double*>(static_cast<char*>(a.ws) + l.off_sum);
-  // the scales of this lane's 8 tokens (4 per column block)
-  float s2v[kCB][4];
-#pragma unroll
-  for (int cb = 0; cb < kCB; ++cb) {
-    const int vb = v0 + (kCB * wave + cb) * 16 + 4 * g;
-    if constexpr (VEC) {
-      const float4 w = *reinterpret_cast<const float4*>(a.s2 + min(vb, a.V - 4));
-      s2v[cb][0] = w.x; s2v[cb][1] = w.y; s2v[cb][2] = w.z; s2v[cb][3] = w.w;
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s2v[cb][i] = a.s2[min(vb + i, a.V - 1)];
-    }
-  }
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  stage_store();
   // output element of (row block rb, column block cb, i): request rb*16 + c16, token
-  // v0 + 16 (2 wave + cb) + 4 g + i (the MFMA result layout: lane column c16, rows 4g + i)
+  // vl + 4 cb + i (the MFMA result layout: lane column c16, rows 4g + i)
   for (int b0 = 0; b0 < a.B; b0 += kReqGroup) {
     const int nb = min(kReqGroup, a.B - b0);
+    if (b0 > 0) {
+      __syncthreads();  // the previous group's LDS is no longer read
+      stage_load(b0, nb);
+      stage_store();
+    }
     // the epilogue's base logits, requested before the MFMA and kept in their storage
     // format (bf16 pairs stay packed: half the registers)
     constexpr int kU = sizeof(T) == 2 ? 2 : 4;
+    static_assert(kCB % 2 == 0, "bf16 tokens are loaded and stored 8 at a time");
     uint32_t uv[4][kCB][kU];
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
       for (int cb = 0; cb < kCB; ++cb) {
-        const int rl = rb * 16 + c16, vb = v0 + (kCB * wave + cb) * 16 + 4 * g;
+        const int rl = rb * 16 + c16, vb = vl + 4 * cb;
         if constexpr (VEC) {
           // rows past the batch and tokens past V read a valid place; their values are unused
+          // (V is a multiple of 8 and vl of 8, so a run of 8 is all in or all out)
           const size_t base = (size_t(b0 + min(rl, nb - 1)) * a.G1 + k) * a.V + min(vb, a.V - 4);
           if constexpr (sizeof(T) == 2) {
-            const uint2 w = *reinterpret_cast<const uint2*>(U + base);
-            uv[rb][cb][0] = w.x;
-            uv[rb][cb][1] = w.y;
+            if (cb % 2 == 0) {  // 8 tokens: this block's 4 and the next one's
+              const size_t b8 = (size_t(b0 + min(rl, nb - 1)) * a.G1 + k) * a.V + min(vb, a.V - 8);
+              const uint4 w = *reinterpret_cast<const uint4*>(U + b8);
+              uv[rb][cb][0] = w.x;
+              uv[rb][cb][1] = w.y;
+              uv[rb][cb + 1][0] = w.z;
+              uv[rb][cb + 1][1] = w.w;
+            }
           } else {
             const uint4 w = *reinterpret_cast<const uint4*>(U + base);
             uv[rb][cb][0] = w.x; uv[rb][cb][1] = w.y; uv[rb][cb][2] = w.z; uv[rb][cb][3] = w.w;
@@ -190,19 +245,6 @@ __global__ __launch_bounds__(kMkThreads, VEC ? 4 : 1) void markov_logits_kernel(
           }
         }
       }
-    __syncthreads();  // the previous group's LDS is no longer read
-    // the staged q1[x_b] rows (16 bytes per thread per step) and scales; no lookup chain
-    const int8_t* estage = static_cast<const int8_t*>(a.ws) + l.off_e;
-    const float* s1stage = reinterpret_cast<const float*>(static_cast<const char*>(a.ws) + l.off_s1);
-    for (int it = tid; it < kReqGroup * (R / 16); it += kMkThreads) {
-      const int rl = it / (R / 16), c = it % (R / 16);
-      uint4 w = *reinterpret_cast<const uint4*>(estage + size_t(b0 + min(rl, nb - 1)) * R + c * 16);
-      if (rl >= nb) w = make_uint4(0, 0, 0, 0);
-      uint2* dst = reinterpret_cast<uint2*>(sE + rl * kEPitch + c * 16);
-      dst[0] = make_uint2(w.x, w.y);
-      dst[1] = make_uint2(w.z, w.w);
-    }
-    if (tid < kReqGroup) sS1[tid] = s1stage[b0 + min(tid, nb - 1)];
     __syncthreads();
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
@@ -210,10 +252,10 @@ __global__ __launch_bounds__(kMkThreads, VEC ? 4 : 1) void markov_logits_kernel(
       v4i acc[kCB];
 #pragma unroll
       for (int cb = 0; cb < kCB; ++cb) acc[cb] = v4i{0, 0, 0, 0};
-      const int8_t* erow = sE + rl * kEPitch + g * kQ;
+      const int8_t* erow = sE + rl * kEPitch + g * 16;
 #pragma unroll
       for (int s = 0; s < kSteps; ++s) {
-        const long bv = *reinterpret_cast<const long*>(erow + s * 8);
+        const long bv = *reinterpret_cast<const long*>(erow + (s / 2) * 64 + (s % 2) * 8);
 #pragma unroll
         for (int cb = 0; cb < kCB; ++cb)
           acc[cb] = __builtin_amdgcn_mfma_i32_16x16x32_i8(afrag[cb][s], bv, acc[cb], 0, 0, 0);
@@ -225,7 +267,7 @@ __global__ __launch_bounds__(kMkThreads, VEC ? 4 : 1) void markov_logits_kernel(
       float m = -INFINITY;
 #pragma unroll
       for (int cb = 0; cb < kCB; ++cb) {
-        const int vb = v0 + (kCB * wave + cb) * 16 + 4 * g;
+        const int vb = vl + 4 * cb;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int v = vb + i;
@@ -243,9 +285,12 @@ __global__ __launch_bounds__(kMkThreads, VEC ? 4 : 1) void markov_logits_kernel(
         if (rl < nb) {
           if (VEC && vb < a.V) {
             if constexpr (sizeof(T) == 2) {
-              *reinterpret_cast<uint2*>(O + base + vb) =
-                  make_uint2(f32_to_bf16(lv[cb][0]) | (uint32_t(f32_to_bf16(lv[cb][1])) << 16),
-                             f32_to_bf16(lv[cb][2]) | (uint32_t(f32_to_bf16(lv[cb][3])) << 16));
+              if (cb % 2 == 1)  // 8 tokens: the previous block's 4 and this one's
+                *reinterpret_cast<uint4*>(O + base + vb - 4) =
+                    make_uint4(f32_to_bf16(lv[cb - 1][0]) | (uint32_t(f32_to_bf16(lv[cb - 1][1])) << 16),
+                               f32_to_bf16(lv[cb - 1][2]) | (uint32_t(f32_to_bf16(lv[cb - 1][3])) << 16),
+                               f32_to_bf16(lv[cb][0]) | (uint32_t(f32_to_bf16(lv[cb][1])) << 16),
+                               f32_to_bf16(lv[cb][2]) | (uint32_t(f32_to_bf16(lv[cb][3])) << 16));
             } else {
               *reinterpret_cast<float4*>(O + base + vb) = make_float4(lv[cb][0], lv[cb][1], lv[cb][2], lv[cb][3]);
             }

@@ -60,6 +60,7 @@ CASES = [
     ("small-f32", 5, 4, 1000, 64, "f32", None),
     ("small-bf16-r128", 3, 6, 4096, 128, "bf16", None),
     ("ragged-vocab", 70, 3, 1003, 256, "bf16", None),     # V not a multiple of 8, B > 64
+    ("two-groups-vec", 80, 2, 4096, 256, "bf16", None),   # B > 64 on the 16-byte path
     ("mixed-b64", 64, 7, 151936, 256, "bf16", [0, 17, 40, 63]),
     ("one-request-one-draft", 1, 1, 333, 128, "bf16", None),  # B = 1, G1 = 1, V < 3 tiles
 ]
