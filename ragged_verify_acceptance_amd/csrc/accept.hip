@@ -115,9 +115,10 @@ struct Ctx {
 };
 
 // Request b's packed rows [cu[b], cu[b] + w) lie inside [0, max_rows) and w in [1, gamma].
+// Both offsets are loaded before either is tested (no short-circuit: one round trip).
 __device__ __forceinline__ bool req_ok(const Ctx& c, int b) {
   const int r0 = c.a.cu[b], r1 = c.a.cu[b + 1];
-  return r0 >= 0 && r1 - r0 >= 1 && r1 - r0 <= c.a.gamma && r1 <= c.a.max_rows;
+  return (r0 >= 0) & (r1 - r0 >= 1) & (r1 - r0 <= c.a.gamma) & (r1 <= c.a.max_rows);
 }
 
 template <typename T>
@@ -307,20 +308,24 @@ __device__ __forceinline__ int decide_row_id(const Ctx& c, int b, int r0, int w,
   return rr < w ? r0 + rr : c.a.max_rows + b * (c.a.gamma - 1) + (rr - w);
 }
 
-template <typename T>
-__global__ __launch_bounds__(kDecideThreads) void decide_kernel(Ctx c, int commit) {
+template <typename T, bool commit>
+__global__ __launch_bounds__(kDecideThreads) void decide_kernel(Ctx c) {
   __shared__ float sM[2 * 64];
   __shared__ double sS[2 * 64];
   const int b = blockIdx.x;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int G1 = c.a.gamma - 1;
   // wave 0, lane k: the drafted token and its uniform are loaded before the window is known
-  // (they do not depend on it), so that only the logit loads wait for cu_seqlens
+  // (they do not depend on it), so that only the logit loads wait for cu_seqlens.  Every
+  // lane of every wave loads (lanes past G1 repeat the last draft; wave 0's are used): a
+  // load into a register that other lanes set on another path would be waited for where
+  // the paths join, and the compiler cannot tell that a wave test is uniform.
   int x = 0;
   float u = 0.f;
-  if (commit && wave == 0 && lane < G1) {
-    x = c.a.tokens[size_t(b) * G1 + lane];
-    u = c.a.u_acc[size_t(b) * G1 + lane];
+  if (commit) {
+    const int k = min(lane, G1 - 1);
+    x = c.a.tokens[size_t(b) * G1 + k];
+    u = c.a.u_acc[size_t(b) * G1 + k];
   }
   if (!req_ok(c, b)) {
     if (tid == 0) {
@@ -331,28 +336,40 @@ __global__ __launch_bounds__(kDecideThreads) void decide_kernel(Ctx c, int commi
   }
   const int r0 = c.a.cu[b];
   const int w = c.a.cu[b + 1] - r0;
-  // wave 0, lane k < w-1: issue the drafted token's logit loads before the stats sweep
-  float lt = 0.f, ld = 0.f;
-  if (commit && wave == 0 && lane < w - 1) {
-    const size_t o = size_t(b) * G1 + lane;
-    if (x < 0 || x >= c.a.V) {
-      flag(c.a.status, RVA_DEV_BAD_TOKEN);
-      x = x < 0 ? 0 : c.a.V - 1;
-    }
-    lt = Elem<T>::load(row_ptr<T>(c, r0 + lane), x);
-    ld = Elem<T>::load(row_ptr<T>(c, c.a.max_rows + int(o)), x);
-  }
-  // row normalisers: one wave per row, lanes over segments
+  // row normalisers: one wave per row, lanes over segments.  A wave's first row (every row
+  // when nseg <= 64) has its segment maxima and sums requested at once, before the drafted
+  // tokens' logits, so that waiting for them does not also wait for those (the wait counter
+  // drains in order).
   const int nrows = 2 * w - 1;
+  const int nseg = c.L.nseg;
+  float m0 = -INFINITY;
+  double s0 = 0.0;
+  if (wave < nrows && lane < nseg) {
+    const int id = decide_row_id(c, b, r0, w, wave);
+    m0 = c.st_m[size_t(id) * nseg + lane];
+    s0 = c.st_s[size_t(id) * nseg + lane];
+  }
+  // lane k < w-1 of wave 0: the drafted token's logits, kept raw until the decision (every
+  // lane loads, from a clamped draft: see above)
+  T lt_raw = T(0), ld_raw = T(0);
+  if (commit) {
+    const int k = min(lane, max(w - 2, 0));
+    const bool bad = x < 0 || x >= c.a.V;
+    if (bad && wave == 0 && lane < w - 1) flag(c.a.status, RVA_DEV_BAD_TOKEN);
+    x = x < 0 ? 0 : (x >= c.a.V ? c.a.V - 1 : x);
+    lt_raw = row_ptr<T>(c, r0 + k)[x];
+    ld_raw = row_ptr<T>(c, c.a.max_rows + b * G1 + k)[x];
+  }
   for (int rr = wave; rr < nrows; rr += kDecideThreads / kWave) {
     const int id = decide_row_id(c, b, r0, w, rr);
-    const float* rm = c.st_m + size_t(id) * c.L.nseg;
-    const double* rs = c.st_s + size_t(id) * c.L.nseg;
-    float m = -INFINITY;
-    for (int s = lane; s < c.L.nseg; s += kWave) m = fmaxf(m, rm[s]);
+    const float* rm = c.st_m + size_t(id) * nseg;
+    const double* rs = c.st_s + size_t(id) * nseg;
+    const bool first = rr == wave;
+    float m = first ? m0 : -INFINITY;
+    for (int s = lane + (first ? kWave : 0); s < nseg; s += kWave) m = fmaxf(m, rm[s]);
     m = wave_max(m);
-    double acc = 0.0;
-    for (int s = lane; s < c.L.nseg; s += kWave) acc += rs[s] * exp_shift_f64(c.P, rm[s], m);
+    double acc = (first && lane < nseg) ? s0 * exp_shift_f64(c.P, m0, m) : 0.0;
+    for (int s = lane + (first ? kWave : 0); s < nseg; s += kWave) acc += rs[s] * exp_shift_f64(c.P, rm[s], m);
     acc = wave_sum_f64(acc);
     if (lane == 0) {
       sM[rr] = m;
@@ -368,6 +385,7 @@ __global__ __launch_bounds__(kDecideThreads) void decide_kernel(Ctx c, int commi
   if (lane < G1) {
     const size_t o = size_t(b) * G1 + lane;
     if (lane < w - 1) {
+      const float lt = Elem<T>::load(&lt_raw, 0), ld = Elem<T>::load(&ld_raw, 0);
       const double pt = exp_shift_f64(c.P, lt, sM[lane]) / sS[lane];
       const double pd = exp_shift_f64(c.P, ld, sM[w + lane]) / sS[w + lane];
       if (c.a.pt_at) c.a.pt_at[o] = float(pt);
@@ -755,7 +773,10 @@ hipError_t launch_typed(const Ctx& c, bool commit, hipStream_t stream) {
   hipLaunchKernelGGL(stats_kernel<T>, dim3(nseg, c.L.n_ids), dim3(kThreads), 0, stream, c);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decide_kernel<T>, dim3(a.B), dim3(kDecideThreads), 0, stream, c, int(commit));
+  if (commit)
+    hipLaunchKernelGGL((decide_kernel<T, true>), dim3(a.B), dim3(kDecideThreads), 0, stream, c);
+  else
+    hipLaunchKernelGGL((decide_kernel<T, false>), dim3(a.B), dim3(kDecideThreads), 0, stream, c);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int draw_slots = commit ? a.B : 0;
   const int slots = draw_slots + (with_labels ? a.B * G1 : 0);

@@ -5,6 +5,7 @@
 
 #include <cstddef>
 #include <cstdint>
+#include <type_traits>
 
 #include "../../include/rva.h"
 
@@ -35,20 +36,56 @@ template <> struct Elem<uint16_t> {
 };
 
 // ---------------------------------------------------------------- wave reductions
+// By DPP, without an LDS round trip: row_shr:n moves each lane's value n lanes up inside
+// its row of 16; row_bcast:15 hands the last lane of rows 0 and 2 to rows 1 and 3, and
+// row_bcast:31 hands lane 31 to rows 2 and 3 (GFX9 controls).  Lanes with no source, and
+// rows outside ROW_MASK, get `id`.  Every lane of the wave must be active: a disabled lane
+// still serves its stale register as a source.
+constexpr int kDppRowShr = 0x110, kDppBcast15 = 0x142, kDppBcast31 = 0x143;
+
+template <int CTRL, int ROW_MASK, typename T>
+__device__ __forceinline__ T dpp_move(T id, T x) {
+  if constexpr (sizeof(T) == 8) {
+    const int lo = __builtin_amdgcn_update_dpp(__double2loint(id), __double2loint(x), CTRL, ROW_MASK, 0xf, false);
+    const int hi = __builtin_amdgcn_update_dpp(__double2hiint(id), __double2hiint(x), CTRL, ROW_MASK, 0xf, false);
+    return __hiloint2double(hi, lo);
+  } else if constexpr (std::is_same_v<T, float>) {
+    return __int_as_float(
+        __builtin_amdgcn_update_dpp(__float_as_int(id), __float_as_int(x), CTRL, ROW_MASK, 0xf, false));
+  } else {
+    return __builtin_amdgcn_update_dpp(id, x, CTRL, ROW_MASK, 0xf, false);
+  }
+}
+
+// Inclusive prefix of `op` (associative, identity id) over the wave's lanes: log steps
+// inside each row, then the two row broadcasts.  Lane 63 ends with the whole wave.
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_inclusive(T x, T id, Op op) {
+  x = op(x, dpp_move<kDppRowShr + 1, 0xf>(id, x));
+  x = op(x, dpp_move<kDppRowShr + 2, 0xf>(id, x));
+  x = op(x, dpp_move<kDppRowShr + 4, 0xf>(id, x));
+  x = op(x, dpp_move<kDppRowShr + 8, 0xf>(id, x));
+  x = op(x, dpp_move<kDppBcast15, 0xa>(id, x));
+  x = op(x, dpp_move<kDppBcast31, 0xc>(id, x));
+  return x;
+}
+
+// Lane 63's value, the same in every lane.
+__device__ __forceinline__ float lane63(float x) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63)); }
+__device__ __forceinline__ double lane63(double x) {
+  return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(x), 63),
+                          __builtin_amdgcn_readlane(__double2loint(x), 63));
+}
+
+// Whole-wave results, the same value in every lane (one summation order for all of them).
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+  return lane63(wave_inclusive(v, -INFINITY, [](float a, float b) { return fmaxf(a, b); }));
 }
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  return lane63(wave_inclusive(v, 0.f, [](float a, float b) { return a + b; }));
 }
 __device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  return lane63(wave_inclusive(v, 0.0, [](double a, double b) { return a + b; }));
 }
 
 __device__ __forceinline__ void flag(int32_t* status, int bits) {

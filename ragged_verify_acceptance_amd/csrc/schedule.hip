@@ -57,42 +57,17 @@ __global__ __launch_bounds__(256) void conf_head_kernel(const T* __restrict__ hi
   }
 }
 
-// Cross-lane moves inside a wave by DPP (no LDS round trip): row_shr:n moves each lane's
-// value n lanes up inside its row of 16; row_bcast:15 hands the last lane of rows 0 and 2 to
-// rows 1 and 3, row_bcast:31 hands lane 31 to rows 2 and 3 (GFX9 controls).  Lanes with no
-// source, and rows outside ROW_MASK, get `id`.
-constexpr int kDppRowShr = 0x110, kDppBcast15 = 0x142, kDppBcast31 = 0x143;
-
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ int dpp_i32(int id, int x) {
-  return __builtin_amdgcn_update_dpp(id, x, CTRL, ROW_MASK, 0xf, false);
-}
-
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ double dpp_f64(double id, double x) {
-  const int lo = dpp_i32<CTRL, ROW_MASK>(__double2loint(id), __double2loint(x));
-  const int hi = dpp_i32<CTRL, ROW_MASK>(__double2hiint(id), __double2hiint(x));
-  return __hiloint2double(hi, lo);
-}
-
-// Inclusive float64 prefix sum over the wave's lanes: log steps inside each row, then the
-// two row broadcasts.  Lane 63 ends with the wave's total.
+// Inclusive float64 prefix sum over the wave's lanes (DPP); lane 63 ends with the total.
 __device__ __forceinline__ double wave_inclusive_sum_f64(double x) {
-  x += dpp_f64<kDppRowShr + 1, 0xf>(0.0, x);
-  x += dpp_f64<kDppRowShr + 2, 0xf>(0.0, x);
-  x += dpp_f64<kDppRowShr + 4, 0xf>(0.0, x);
-  x += dpp_f64<kDppRowShr + 8, 0xf>(0.0, x);
-  x += dpp_f64<kDppBcast15, 0xa>(0.0, x);
-  x += dpp_f64<kDppBcast31, 0xc>(0.0, x);
-  return x;
+  return wave_inclusive(x, 0.0, [](double p, double q) { return p + q; });
 }
 
 // One step of the argmax prefix: the moved (ratio, K) replaces this lane's when its ratio is
 // larger, or equal with a smaller K.
 template <int CTRL, int ROW_MASK>
 __device__ __forceinline__ void argmax_step(double& best, int& bestK) {
-  const double o = dpp_f64<CTRL, ROW_MASK>(-INFINITY, best);
-  const int ok = dpp_i32<CTRL, ROW_MASK>(0x7fffffff, bestK);
+  const double o = dpp_move<CTRL, ROW_MASK>(double(-INFINITY), best);
+  const int ok = dpp_move<CTRL, ROW_MASK>(int(0x7fffffff), bestK);
   if (o > best || (o == best && ok < bestK)) {
     best = o;
     bestK = ok;
