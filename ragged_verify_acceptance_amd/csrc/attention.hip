@@ -611,48 +611,54 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, SkShared<D, NBMAX
 // kernel, which took those keys from k_new / v_new).  A pass moves kThreads 4-element K
 // pieces (consecutive threads: consecutive pieces of one key row, a contiguous cache row) and
 // 4 kThreads V elements (consecutive threads: consecutive slots of one d, contiguous in the
-// transposed column blocks); every load of a pass is issued before its first store, so a
-// window of up to 8 rows at D = 128 costs one round trip.
+// transposed column blocks).  A pass's loads are unconditional (indices clamped into the
+// window; the stores check them), so they all go out before its first store: a window of up
+// to 8 rows at D = 128 is one pass, one round trip.
+struct AppendPass {
+  uint2 kval;
+  int kpg;
+  int vpg[4];
+  uint16_t vval[4];
+};
+
 template <int D>
-__device__ __forceinline__ void append_window(const AttnArgs& a, int b, int g, int L, int r0, int w) {
-  const int Hkv = a.Hkv, P = a.page_size;
-  const uint16_t* kn = static_cast<const uint16_t*>(a.k_new);
-  const uint16_t* vn = static_cast<const uint16_t*>(a.v_new);
+__device__ __forceinline__ void append_load(const AttnArgs& a, int b, int g, int L, int r0, int w, int base,
+                                            AppendPass& ap) {
+  const int Hkv = a.Hkv, P = a.page_size, n = w * D, tid = threadIdx.x;
+  const int* bt = a.block_table + size_t(b) * a.max_pages;
+  const int ik = min(base / 4 + tid, n / 4 - 1);
+  const int kj = ik / (D / 4), kd = (ik % (D / 4)) * 4;
+  ap.kpg = bt[(L + kj) / P];
+  ap.kval = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.k_new) + (size_t(r0 + kj) * Hkv + g) * D + kd);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int iv = min(base + e * kThreads + tid, n - 1);
+    const int vj = iv % w, vd = iv / w;
+    ap.vpg[e] = bt[(L + vj) / P];
+    ap.vval[e] = static_cast<const uint16_t*>(a.v_new)[(size_t(r0 + vj) * Hkv + g) * D + vd];
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void append_store(const AttnArgs& a, int g, int L, int w, int base, const AppendPass& ap) {
+  const int Hkv = a.Hkv, P = a.page_size, n = w * D, tid = threadIdx.x;
   uint16_t* kcw = static_cast<uint16_t*>(a.k_cache);
   uint16_t* vcw = static_cast<uint16_t*>(a.v_cache);
-  const int* bt = a.block_table + size_t(b) * a.max_pages;
-  const int tid = threadIdx.x, n = w * D;
-  for (int base = 0; base < n; base += 4 * kThreads) {
-    const int ik = base / 4 + tid;
-    const bool kok = ik < n / 4;
-    const int kj = kok ? ik / (D / 4) : 0, kd = (ik % (D / 4)) * 4;
-    const int kpg = kok ? bt[(L + kj) / P] : 0;
-    const uint2 kval =
-        kok ? *reinterpret_cast<const uint2*>(kn + (size_t(r0 + kj) * Hkv + g) * D + kd) : make_uint2(0, 0);
-    int vpg[4];
-    uint16_t vval[4];
+  const int ik = base / 4 + tid;
+  if (ik < n / 4) {
+    if (ap.kpg < 0 || ap.kpg >= a.num_pages) {
+      flag(a.status, RVA_DEV_BAD_PAGE);
+    } else {
+      const int kj = ik / (D / 4), kd = (ik % (D / 4)) * 4, p = L + kj;
+      *reinterpret_cast<uint2*>(kcw + ((size_t(ap.kpg) * Hkv + g) * P + p % P) * D + kd) = ap.kval;
+    }
+  }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int iv = base + e * kThreads + tid;
-      const int vj = iv % w, vd = iv / w;
-      vpg[e] = iv < n ? bt[(L + vj) / P] : -1;
-      vval[e] = iv < n ? vn[(size_t(r0 + vj) * Hkv + g) * D + vd] : 0;
-    }
-    if (kok) {
-      if (kpg < 0 || kpg >= a.num_pages) {
-        flag(a.status, RVA_DEV_BAD_PAGE);
-      } else {
-        const int p = L + kj;
-        *reinterpret_cast<uint2*>(kcw + ((size_t(kpg) * Hkv + g) * P + p % P) * D + kd) = kval;
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int iv = base + e * kThreads + tid;
-      if (iv >= n || vpg[e] < 0 || vpg[e] >= a.num_pages) continue;  // a bad page is reported above
-      const int p = L + iv % w;
-      vcw[v_index(vpg[e], g, Hkv, P, D, p % P, iv / w)] = vval[e];
-    }
+  for (int e = 0; e < 4; ++e) {
+    const int iv = base + e * kThreads + tid;
+    if (iv >= n || ap.vpg[e] < 0 || ap.vpg[e] >= a.num_pages) continue;  // a bad page is reported above
+    const int p = L + iv % w;
+    vcw[v_index(ap.vpg[e], g, Hkv, P, D, p % P, iv / w)] = ap.vval[e];
   }
 }
 
@@ -733,11 +739,27 @@ __global__ __launch_bounds__(kThreads) void attn_merge_kernel(AttnArgs a, int P,
   const float* ws_o = static_cast<const float*>(a.ws);
   const float* ws_lse = ws_o + size_t(P) * 2 * ROWS * D;
   // Every load is issued before any store, so the whole merge costs about one round trip:
-  // the partials of a cut segment (kItems output items of 4 d per thread, up to 4 shares)...
-  constexpr int kItems = (ROWS * D / 4 + kThreads - 1) / kThreads;
-  float lse[kItems][4];
-  float4 po[kItems][4];
+  // the first pass of the window K/V append (positions L .. L+w-1) goes first, so that its
+  // stores wait for it alone (the wait counter drains in order)...
+  AppendPass ap;
+  append_load<D>(a, b, g, ri.L, ri.r0, ri.w, 0, ap);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  // ...then the partials of a cut segment (kItems output items of 4 d per thread, up to 4
+  // shares).  Those loads are unconditional too (column and share clamped into the segment;
+  // the masks are applied after the compiler barrier), so that the append's stores wait for
+  // an exact count of later loads.  Each branch has its own copy of the append's stores.
+  auto append_rest = [&]() {
+    append_store<D>(a, g, ri.L, ri.w, 0, ap);
+    for (int base = 4 * kThreads; base < ri.w * D; base += 4 * kThreads) {  // windows of more than 8 rows
+      append_load<D>(a, b, g, ri.L, ri.r0, ri.w, base, ap);
+      append_store<D>(a, g, ri.L, ri.w, base, ap);
+    }
+  };
   if (cut) {
+    constexpr int kItems = (ROWS * D / 4 + kThreads - 1) / kThreads;
+    float lse[kItems][4];
+    float4 po[kItems][4];
 #pragma unroll
     for (int i = 0; i < kItems; ++i) {
       const int it = tid + i * kThreads;
@@ -746,22 +768,21 @@ __global__ __launch_bounds__(kThreads) void attn_merge_kernel(AttnArgs a, int P,
       for (int u = 0; u < 4; ++u) {
         const int p = min(pa + u, pb);
         const size_t sl = p == pa ? first_slot : size_t(p) * 2;
-        const bool live = pa + u <= pb && it < nq * (D / 4);
-        lse[i][u] = live ? ws_lse[sl * ROWS + col] : -INFINITY;
-        po[i][u] = live ? reinterpret_cast<const float4*>(ws_o + (sl * ROWS + col) * D)[c4]
-                        : make_float4(0.f, 0.f, 0.f, 0.f);
+        lse[i][u] = ws_lse[sl * ROWS + col];
+        po[i][u] = reinterpret_cast<const float4*>(ws_o + (sl * ROWS + col) * D)[c4];
       }
     }
-  }
-  // ...and the window K/V with its page numbers (appended at positions L .. L+w-1)
-  append_window<D>(a, b, g, ri.L, ri.r0, ri.w);
-  if (pa == pb) return;  // finished inside one share
-  if (cut) {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    append_rest();
 #pragma unroll
     for (int i = 0; i < kItems; ++i) {
       const int it = tid + i * kThreads;
       if (it >= nq * (D / 4)) break;
       const int col = it / (D / 4), c4 = it % (D / 4);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (pa + u > pb) lse[i][u] = -INFINITY;  // past the segment's last share
       float M = -INFINITY;
 #pragma unroll
       for (int u = 0; u < 4; ++u) M = fmaxf(M, lse[i][u]);
@@ -783,6 +804,8 @@ __global__ __launch_bounds__(kThreads) void attn_merge_kernel(AttnArgs a, int P,
     }
     return;
   }
+  append_rest();
+  if (pa == pb) return;  // finished inside one share
   // a segment spread over more than 4 shares: the general loop, 4 shares at a time
   for (int it = tid; it < nq * (D / 4); it += kThreads) {
     const int col = it / (D / 4), c4 = it % (D / 4);
