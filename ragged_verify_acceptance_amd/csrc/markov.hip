@@ -348,27 +348,51 @@ __global__ __launch_bounds__(kSampleThreads) void markov_sample_kernel(MarkovArg
   const double* tsum = reinterpret_cast<const double*>(static_cast<const char*>(a.ws) + l.off_sum) + size_t(b) * l.ntiles;
   const int nt = l.ntiles, per = (nt + kSampleThreads - 1) / kSampleThreads;
   const int t0 = min(tid * per, nt), t1 = min(t0 + per, nt);
+  // Loads that depend on nothing else go out first: the draw's uniform and this thread's run
+  // of tile statistics, held in registers when the run is at most kRun tiles (V up to
+  // kRun x 256 x 128 tokens; longer runs take the loops below).
+  const float uu = a.u[size_t(b) * a.G1 + k];
+  constexpr int kRun = 8;
+  const bool regs = per <= kRun;
+  float tm[kRun];
+  double ts[kRun];
+  if (regs) {
+#pragma unroll
+    for (int i = 0; i < kRun; ++i) {
+      const int t = min(t0 + i, nt - 1);
+      tm[i] = tmax[t];
+      ts[i] = tsum[t];
+    }
+  }
+  asm volatile("" ::: "memory");  // keep the uniform's load here, ahead of its use
+  __builtin_amdgcn_sched_barrier(0);
   // row maximum
   float m = -INFINITY;
-  for (int t = t0; t < t1; ++t) m = fmaxf(m, tmax[t]);
+  if (regs) {
+#pragma unroll
+    for (int i = 0; i < kRun; ++i)
+      if (t0 + i < t1) m = fmaxf(m, tm[i]);
+  } else {
+    for (int t = t0; t < t1; ++t) m = fmaxf(m, tmax[t]);
+  }
   m = wave_max(m);
   if (lane == 0) smax[wave] = m;
   __syncthreads();
   float M = smax[0];
   for (int w = 1; w < kSampleThreads / kWave; ++w) M = fmaxf(M, smax[w]);
   // this thread's run of tile masses, then a scan over threads (tile order).  Thread i
-  // owns [off + excl_i, off + inc_i); the next thread's lower end is the same expression,
-  // so the runs tile [0, S) without gaps or overlaps.
+  // owns [off + excl_i, off + inc_i); the next thread's lower end is the same value moved
+  // one lane up, so the runs tile [0, S) without gaps or overlaps.
   double part = 0.0;
-  for (int t = t0; t < t1; ++t) part += tsum[t] * ex(tmax[t], M);
-  double inc = part;
+  if (regs) {
 #pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const double v = __shfl_up(inc, o);
-    if (lane >= o) inc += v;
+    for (int i = 0; i < kRun; ++i)
+      if (t0 + i < t1) part += ts[i] * ex(tm[i], M);
+  } else {
+    for (int t = t0; t < t1; ++t) part += tsum[t] * ex(tmax[t], M);
   }
-  const double excl_up = __shfl_up(inc, 1);
-  const double excl = lane == 0 ? 0.0 : excl_up;
+  const double inc = wave_inclusive(part, 0.0, [](double x, double y) { return x + y; });
+  const double excl = dpp_move<kDppWaveShr1, 0xf>(0.0, inc);
   if (lane == kWave - 1) sc[wave] = inc;
   __syncthreads();
   double off = 0.0;
@@ -376,7 +400,7 @@ __global__ __launch_bounds__(kSampleThreads) void markov_sample_kernel(MarkovArg
   double S = 0.0;
   for (int w = 0; w < kSampleThreads / kWave; ++w) S += sc[w];
   const double before = off + excl, upper = off + inc;
-  const double target = double(a.u[size_t(b) * a.G1 + k]) * S;
+  const double target = double(uu) * S;
   if (tid == 0) {
     s_tile = nt - 1;  // rounding can leave u * S at or past the last edge: the last tile
     s_before = -1.0;
@@ -386,10 +410,21 @@ __global__ __launch_bounds__(kSampleThreads) void markov_sample_kernel(MarkovArg
   if (t1 > t0 && before <= target && target < upper) {
     double c = before;
     int t = t0;
-    for (; t < t1 - 1; ++t) {
-      const double mt = tsum[t] * ex(tmax[t], M);
-      if (target < c + mt) break;
-      c += mt;
+    if (regs) {
+#pragma unroll
+      for (int i = 0; i < kRun; ++i) {
+        if (t0 + i >= t1 - 1) break;
+        const double mt = ts[i] * ex(tm[i], M);
+        if (target < c + mt) break;
+        c += mt;
+        ++t;
+      }
+    } else {
+      for (; t < t1 - 1; ++t) {
+        const double mt = tsum[t] * ex(tmax[t], M);
+        if (target < c + mt) break;
+        c += mt;
+      }
     }
     s_tile = t;
     s_before = c;
@@ -415,12 +450,7 @@ __global__ __launch_bounds__(kSampleThreads) void markov_sample_kernel(MarkovArg
     // the last tile after a rounding overshoot: its start is S minus its own mass
     c0 = S - tsum[t] * ex(tmax[t], M);
   }
-  double pinc = own;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const double vv = __shfl_up(pinc, o);
-    if (lane >= o) pinc += vv;
-  }
+  const double pinc = wave_inclusive(own, 0.0, [](double x, double y) { return x + y; });
   // cumulative mass through each of this lane's tokens, in token order
   double cum = c0 + (pinc - own);
   int cand = a.V;                                 // smallest token whose cumulative passes
@@ -429,17 +459,28 @@ __global__ __launch_bounds__(kSampleThreads) void markov_sample_kernel(MarkovArg
     cum += e[i];
     if (cand == a.V && v + i < a.V && cum > target) cand = v + i;
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) cand = min(cand, __shfl_xor(cand, o));
+  cand = lane63(wave_inclusive(cand, int(a.V), [](int x, int y) { return min(x, y); }));
+  bool in_tile = true;
   if (cand == a.V) {
     // nothing in the tile passes: past the last edge (u * S >= S after rounding) the inverse
     // CDF clamps to the last token; otherwise the tile's recomputed mass fell short of its
     // summary by a rounding step, and its last token is the edge within that rounding
     cand = s_before >= 0.0 ? min(a.V - 1, t * kTileV + kTileV - 1) : a.V - 1;
+    in_tile = cand >= t * kTileV && cand < t * kTileV + kTileV;
   }
-  if (lane == 0) {
-    a.tokens[size_t(b) * a.G1 + k] = cand;
-    if (a.p_at) a.p_at[size_t(b) * a.G1 + k] = float(ex(Out<T>::load(O, base + cand), M) / s_S);
+  if (lane == 0) a.tokens[size_t(b) * a.G1 + k] = cand;
+  if (a.p_at) {
+    // p(token) from the rescan's own weight of it (the same expression), when it has one
+    const int rel = cand - t * kTileV;
+    if (in_tile && lane == rel / kLaneTok) {
+      double et = e[0];
+#pragma unroll
+      for (int i = 1; i < kLaneTok; ++i)
+        if (rel % kLaneTok == i) et = e[i];
+      a.p_at[size_t(b) * a.G1 + k] = float(et / s_S);
+    } else if (!in_tile && lane == 0) {
+      a.p_at[size_t(b) * a.G1 + k] = float(ex(Out<T>::load(O, base + cand), M) / s_S);
+    }
   }
   if (k + 1 < a.G1) {
     if (a.r == 256) stage_row<256>(a, l, b, cand, lane);

@@ -42,6 +42,7 @@ template <> struct Elem<uint16_t> {
 // rows outside ROW_MASK, get `id`.  Every lane of the wave must be active: a disabled lane
 // still serves its stale register as a source.
 constexpr int kDppRowShr = 0x110, kDppBcast15 = 0x142, kDppBcast31 = 0x143;
+constexpr int kDppWaveShr1 = 0x138;  // the whole wave up by one lane (lane 0 gets id)
 
 template <int CTRL, int ROW_MASK, typename T>
 __device__ __forceinline__ T dpp_move(T id, T x) {
@@ -71,6 +72,7 @@ __device__ __forceinline__ T wave_inclusive(T x, T id, Op op) {
 }
 
 // Lane 63's value, the same in every lane.
+__device__ __forceinline__ int lane63(int x) { return __builtin_amdgcn_readlane(x, 63); }
 __device__ __forceinline__ float lane63(float x) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63)); }
 __device__ __forceinline__ double lane63(double x) {
   return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(x), 63),
