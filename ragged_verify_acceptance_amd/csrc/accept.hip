@@ -574,27 +574,21 @@ __device__ __forceinline__ void locate(double t, double start, int n, F mass, in
   for (int i0 = 0; i0 < n && found < 0; i0 += kWave) {
     const int i = i0 + lane;
     const double m = i < n ? mass(i) : 0.0;
-    double inc = m;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const double x = __shfl_up(inc, o);
-      if (lane >= o) inc += x;
-    }
-    inc += carry;
+    const double inc = wave_inclusive(m, 0.0, [](double x, double y) { return x + y; }) + carry;
     const double exc = inc - m;
     const unsigned long long hit = __ballot(m > 0.0 && inc > t);
     const unsigned long long pos = __ballot(m > 0.0);
     if (pos) {
       const int l = 63 - __clzll(pos);
       last = i0 + l;
-      base_last = __shfl(exc, l);
+      base_last = readlane_f64(exc, l);
     }
     if (hit) {
       const int l = __ffsll(hit) - 1;
       found = i0 + l;
-      base = __shfl(exc, l);
+      base = readlane_f64(exc, l);
     }
-    carry = __shfl(inc, kWave - 1);
+    carry = lane63(inc);
   }
   if (found < 0) {
     found = last;
@@ -602,8 +596,8 @@ __device__ __forceinline__ void locate(double t, double start, int n, F mass, in
   }
 }
 
-template <typename T>
-__global__ __launch_bounds__(kPickThreads) void pick_kernel(Ctx c, int commit) {
+template <typename T, bool commit>
+__global__ __launch_bounds__(kPickThreads) void pick_kernel(Ctx c) {
   __shared__ double s_t, s_base, s_rho;
   __shared__ int s_pos, s_residual;
   __shared__ double s_wave[kPickThreads / kWave];
@@ -725,21 +719,22 @@ __global__ __launch_bounds__(kPickThreads) void pick_kernel(Ctx c, int commit) {
   __syncthreads();
   const bool residual = s_residual;
   const int v = s_pos + tid;
+  // both rows' entries requested together (the draft row's from the target row for a bonus
+  // draw, and past V from the last entry), then weighed
+  const int vc = min(v, c.a.V - 1);
+  const T xt = row_ptr<T>(c, d.id_t)[vc];
+  const T xd = row_ptr<T>(c, residual ? d.id_d : d.id_t)[vc];
+  asm volatile("" ::: "memory");  // keeps both loads here, ahead of the branches that use them
   double wgt = 0.0;
   if (v < c.a.V) {
-    wgt = exp_shift_tab(c.P, tab, Elem<T>::load(row_ptr<T>(c, d.id_t), v), d.Mt);
+    wgt = exp_shift_tab(c.P, tab, Elem<T>::load(&xt, 0), d.Mt);
     if (residual) {
-      wgt -= s_rho * exp_shift_tab(c.P, tab, Elem<T>::load(row_ptr<T>(c, d.id_d), v), d.Md);
+      wgt -= s_rho * exp_shift_tab(c.P, tab, Elem<T>::load(&xd, 0), d.Md);
       wgt = wgt > 0.0 ? wgt : 0.0;
     }
   }
-  // inclusive prefix in index order: wave scan, then the wave totals
-  double inc = wgt;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const double x = __shfl_up(inc, o);
-    if (lane >= o) inc += x;
-  }
+  // inclusive prefix in index order: wave scan (DPP), then the wave totals
+  const double inc = wave_inclusive(wgt, 0.0, [](double x, double y) { return x + y; });
   if (lane == kWave - 1) s_wave[wave] = inc;
   __syncthreads();
   double cum = s_base;
@@ -789,7 +784,10 @@ hipError_t launch_typed(const Ctx& c, bool commit, hipStream_t stream) {
                          draw_slots, int(with_labels));
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(pick_kernel<T>, dim3(a.B), dim3(kPickThreads), 0, stream, c, int(commit));
+  if (commit)
+    hipLaunchKernelGGL((pick_kernel<T, true>), dim3(a.B), dim3(kPickThreads), 0, stream, c);
+  else
+    hipLaunchKernelGGL((pick_kernel<T, false>), dim3(a.B), dim3(kPickThreads), 0, stream, c);
   return hipGetLastError();
 }
 

@@ -71,6 +71,12 @@ __device__ __forceinline__ T wave_inclusive(T x, T id, Op op) {
   return x;
 }
 
+// Lane l's value (l the same in every lane), in every lane.
+__device__ __forceinline__ double readlane_f64(double x, int l) {
+  return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(x), l),
+                          __builtin_amdgcn_readlane(__double2loint(x), l));
+}
+
 // Lane 63's value, the same in every lane.
 __device__ __forceinline__ int lane63(int x) { return __builtin_amdgcn_readlane(x, 63); }
 __device__ __forceinline__ float lane63(float x) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63)); }
