@@ -184,11 +184,44 @@ struct SchedShared {
 // overwritten with the survivals.  On return sh.cnt[b] holds request b's window.  `publish`:
 // this workgroup writes the outputs (conf echo, survival, windows, K*, ratio) and raises the
 // status bits.
+// The pass's global loads, issued first by schedule_loads() (a caller may issue its own
+// loads behind them before schedule_block() waits for these: the wait counter drains in
+// order).  Every load reads a clamped index unconditionally, so that no branch makes the
+// compiler wait for it where the branch joins.
+template <int E>
+struct SchedLoads {
+  uint32_t rk[E];  // ranks from rank_kernel (ranked path)
+  float th[E];     // theta[B + r + 1] for this thread's ranks r = tid*E + e
+  float cv[E];     // confidences tid + e NT
+  float alpha_B, theta_0, theta_N;
+};
+
+template <int E, int NT, bool kRanked>
+__device__ __forceinline__ SchedLoads<E> schedule_loads(int B, int G, const float* __restrict__ conf,
+                                                        const float* __restrict__ surv_out,
+                                                        const float* __restrict__ alpha,
+                                                        const float* __restrict__ theta) {
+  SchedLoads<E> ld;
+  const int tid = threadIdx.x, N = B * G;
+  // ranks: this thread's own candidates, read before it writes their survivals
+#pragma unroll
+  for (int e = 0; e < E; ++e) ld.rk[e] = kRanked ? __float_as_uint(surv_out[min(tid * E + e, N - 1)]) : 0u;
+  // the cost table entries of this thread's ranks: their round trip overlaps the survival
+  // products and the sort
+#pragma unroll
+  for (int e = 0; e < E; ++e) ld.th[e] = theta[B + min(tid * E + e, N - 1) + 1];
+  ld.alpha_B = alpha[B];
+  ld.theta_0 = theta[B];
+  ld.theta_N = theta[B + N];
+#pragma unroll
+  for (int e = 0; e < E; ++e) ld.cv[e] = conf[min(tid + e * NT, N - 1)];
+  return ld;
+}
+
 template <int E, int NT, int CAP, bool kRanked>
 __device__ __forceinline__ void schedule_block(SchedShared<NT, CAP>& sh, int B, int G, int mode,
-                                               const float* __restrict__ conf, float* __restrict__ conf_out,
+                                               const SchedLoads<E>& ld, float* __restrict__ conf_out,
                                                float* __restrict__ surv_out, float bias,
-                                               const float* __restrict__ alpha, const float* __restrict__ theta,
                                                int32_t* __restrict__ windows, int32_t* __restrict__ K_out,
                                                double* __restrict__ ratio_out, int32_t* status, bool publish) {
   float* sa = sh.sa;
@@ -200,33 +233,20 @@ __device__ __forceinline__ void schedule_block(SchedShared<NT, CAP>& sh, int B, 
   const int N = B * G;
   static_assert(kRanked || E == 1, "the merge takes one key a thread");
 
-  // ranks from rank_kernel, requested now (this thread's own candidates, read before it
-  // writes their survivals)
-  uint32_t rk[E];
-  if constexpr (kRanked) {
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const int i = tid * E + e;
-      rk[e] = i < N ? __float_as_uint(surv_out[i]) : 0u;
-    }
-  }
-  // the cost table entries this thread needs later (rank r = tid*E + e uses theta[B + r + 1])
-  // are loaded now, so their round trip overlaps the survival products and the sort
-  float th[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int r = tid * E + e;
-    th[e] = r < N ? theta[B + r + 1] : 0.f;
-  }
-  const float alpha_B = alpha[B], theta_0 = theta[B];
-  const float theta_N = theta[B + N];
+  const uint32_t* rk = ld.rk;
+  const float* th = ld.th;
+  const float alpha_B = ld.alpha_B, theta_0 = ld.theta_0, theta_N = ld.theta_N;
   // (1) survival: the confidences are staged in LDS by one coalesced load, then one lane per
   // request forms the float32 products left to right
-  for (int i = tid; i < N; i += NT) {
-    const float c = conf[i];
-    if (!kRanked && publish && !(c >= 0.f && c <= 1.f)) flag(status, RVA_DEV_BAD_CONF);
-    if (!kRanked && publish && conf_out) conf_out[i] = c;
-    sa[i] = c;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = tid + e * NT;  // < E NT <= CAP: slots past N are written but never read
+    const float c = ld.cv[e];
+    sa[i] = c;  // unconditional, so the load is not sunk into the branch below
+    if (i < N) {
+      if (!kRanked && publish && !(c >= 0.f && c <= 1.f)) flag(status, RVA_DEV_BAD_CONF);
+      if (!kRanked && publish && conf_out) conf_out[i] = c;
+    }
   }
   __syncthreads();
   for (int b = tid; b < B; b += NT) {
@@ -371,8 +391,9 @@ __global__ __launch_bounds__(NT) void schedule_kernel(
     const float* __restrict__ theta, int32_t* __restrict__ windows, int32_t* __restrict__ K_out,
     double* __restrict__ ratio_out, int32_t* status) {
   __shared__ SchedShared<NT, kMaxCand> sh;
-  schedule_block<E, NT, kMaxCand, kRanked>(sh, B, G, mode, conf, conf_out, surv_out, bias, alpha, theta,
-                                           windows, K_out, ratio_out, status, true);
+  const SchedLoads<E> ld = schedule_loads<E, NT, kRanked>(B, G, conf, surv_out, alpha, theta);
+  schedule_block<E, NT, kMaxCand, kRanked>(sh, B, G, mode, ld, conf_out, surv_out, bias, windows, K_out,
+                                           ratio_out, status, true);
 }
 
 // Ranks for batches of more than one workgroup's threads, spread over B workgroups (one per
@@ -451,7 +472,7 @@ __global__ __launch_bounds__(NT) void rank_kernel(int B, int G, const float* __r
 // the (deterministic) scheduling pass itself, so all of them hold the same windows without
 // exchanging anything; workgroup 0 publishes the schedule, and each workgroup then packs its
 // own kRowsPerBlock(NT) destination rows.
-template <int NT>
+template <int NT, bool kPre>
 __global__ __launch_bounds__(NT) void schedule_pack_kernel(
     int B, int G, int mode, const float* __restrict__ conf, float* __restrict__ conf_out,
     float* __restrict__ surv_out, float bias, const float* __restrict__ alpha,
@@ -465,27 +486,29 @@ __global__ __launch_bounds__(NT) void schedule_pack_kernel(
   __shared__ int ctx[NT];
   const int tid = threadIdx.x, gamma = G + 1;
   const bool first = blockIdx.x == 0;
-  // the context lengths (row positions) are requested now and land during the scheduling pass
-  const int ctx_v = tid < B ? context_lens[tid] : 0;
-  // So are this block's kPackRows SOURCE rows (request-major, row s = b gamma + i; the
-  // grid covers max_rows >= B gamma of them): once the windows are known, row s goes to
+  // The context lengths (row positions) and this block's kPackRows SOURCE rows are
+  // requested during the scheduling pass, right behind its own loads (which it then waits
+  // for alone) and land while it runs.  Source rows are request-major, row s = b gamma + i
+  // (the grid covers max_rows >= B gamma of them): once the windows are known, row s goes to
   // destination row cu[b] + i when i < w_b.  Rows of up to 2 NT x 16 bytes, 16-byte aligned;
-  // others are copied destination-first after the pass (pack_block).
+  // others are copied destination-first after the pass (pack_block); the host picks kPre
+  // (pre_ok below).  The loads read clamped rows and pieces unconditionally (the stores
+  // check them), in straight-line code, so that the pass's waits count them exactly.
   const int n16 = int(row_bytes / 16);
-  const bool pre = src && row_bytes % 16 == 0 && n16 <= 2 * NT &&
-                   ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) % 16 == 0);
+  constexpr bool pre = kPre;
+  const SchedLoads<1> ld = schedule_loads<1, NT, false>(B, G, conf, surv_out, alpha, theta);
+  __builtin_amdgcn_sched_barrier(0);
+  const int ctx_v = context_lens[min(tid, B - 1)];
   uint4 v[kPackRows][2];
 #pragma unroll
   for (int rr = 0; rr < kPackRows; ++rr)
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int srow = blockIdx.x * kPackRows + rr, k = h * NT + tid;
-      v[rr][h] = (pre && srow < B * gamma && k < n16)
-                     ? reinterpret_cast<const uint4*>(src + size_t(srow) * row_bytes)[k]
-                     : make_uint4(0, 0, 0, 0);
+      const int srow = min(int(blockIdx.x) * kPackRows + rr, B * gamma - 1), k = min(h * NT + tid, max(n16 - 1, 0));
+      v[rr][h] = kPre ? reinterpret_cast<const uint4*>(src + size_t(srow) * row_bytes)[k] : make_uint4(0, 0, 0, 0);
     }
-  schedule_block<1, NT, NT, false>(sh, B, G, mode, conf, conf_out, surv_out, bias, alpha, theta, windows, K_out,
-                            ratio_out, status, first);
+  schedule_block<1, NT, NT, false>(sh, B, G, mode, ld, conf_out, surv_out, bias, windows, K_out, ratio_out, status,
+                                   first);
   if (tid < B) ctx[tid] = ctx_v;  // published by pack_block's barrier
   pack_block<NT, NT, kPackRows>(psh, B, gamma, sh.cnt, false, ctx, tiers, pre ? nullptr : src, row_bytes,
                                 pre ? nullptr : dst, max_rows, cu_out, row_req, row_pos, total_tier, status,
@@ -606,18 +629,22 @@ hipError_t launch_schedule_pack(int B, int gamma, int mode, const void* hidden, 
   const dim3 grid((max_rows + kPackRows - 1) / kPackRows);
   const uint8_t* s8 = static_cast<const uint8_t*>(src);
   uint8_t* d8 = static_cast<uint8_t*>(dst);
-  if (Npad <= 256)
-    hipLaunchKernelGGL(schedule_pack_kernel<256>, grid, dim3(256), 0, stream, B, G, mode, conf, echo, surv_out,
-                       bias, alpha, theta, windows, K_out, ratio_out, context_lens, tiers, s8, row_bytes, d8,
-                       max_rows, cu, row_req, row_pos, total_tier, status);
-  else if (Npad <= 512)
-    hipLaunchKernelGGL(schedule_pack_kernel<512>, grid, dim3(512), 0, stream, B, G, mode, conf, echo, surv_out,
-                       bias, alpha, theta, windows, K_out, ratio_out, context_lens, tiers, s8, row_bytes, d8,
-                       max_rows, cu, row_req, row_pos, total_tier, status);
-  else
-    hipLaunchKernelGGL(schedule_pack_kernel<kSchedThreads>, grid, dim3(kSchedThreads), 0, stream, B, G, mode,
-                       conf, echo, surv_out, bias, alpha, theta, windows, K_out, ratio_out, context_lens, tiers,
-                       s8, row_bytes, d8, max_rows, cu, row_req, row_pos, total_tier, status);
+  const int NT = Npad <= 256 ? 256 : (Npad <= 512 ? 512 : kSchedThreads);
+  // source rows prefetched during the scheduling pass: 16-byte pieces, at most 2 NT a row
+  const bool pre = s8 && row_bytes % 16 == 0 && row_bytes / 16 <= size_t(2 * NT) &&
+                   ((reinterpret_cast<uintptr_t>(s8) | reinterpret_cast<uintptr_t>(d8)) % 16 == 0);
+#define RVA_SP_LAUNCH(NTV, PRE)                                                                                \
+  hipLaunchKernelGGL((schedule_pack_kernel<NTV, PRE>), grid, dim3(NTV), 0, stream, B, G, mode, conf, echo,      \
+                     surv_out, bias, alpha, theta, windows, K_out, ratio_out, context_lens, tiers, s8, row_bytes, \
+                     d8, max_rows, cu, row_req, row_pos, total_tier, status)
+  if (NT == 256) {
+    if (pre) RVA_SP_LAUNCH(256, true); else RVA_SP_LAUNCH(256, false);
+  } else if (NT == 512) {
+    if (pre) RVA_SP_LAUNCH(512, true); else RVA_SP_LAUNCH(512, false);
+  } else {
+    if (pre) RVA_SP_LAUNCH(kSchedThreads, true); else RVA_SP_LAUNCH(kSchedThreads, false);
+  }
+#undef RVA_SP_LAUNCH
   return hipGetLastError();
 }
 
