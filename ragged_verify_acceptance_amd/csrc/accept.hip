@@ -513,13 +513,17 @@ __device__ __forceinline__ void pair_body(const Ctx& c, int draw_slots, int per_
   }
   const int j = y - draw_slots;
   const int b = j / G1, k = j % G1;
-  if (!req_ok(c, b)) return;
-  if (k >= c.a.cu[b + 1] - c.a.cu[b] - 1) return;
-  if (draw_slots > 0) {
-    const Decision d = c.dec[b];
-    if (d.id_d >= 0 && d.n == k) return;  // done by the draw slot
-  }
-  const int id_t = c.a.cu[b] + k;
+  // the window and the decision record go out together (the record does not depend on
+  // the window), so the row loads wait for one round trip, not two
+  const int r0 = c.a.cu[b], r1 = c.a.cu[b + 1];
+  Decision d;
+  d.id_d = -1;
+  d.n = -1;
+  if (draw_slots > 0) d = c.dec[b];
+  if (!((r0 >= 0) & (r1 - r0 >= 1) & (r1 - r0 <= c.a.gamma) & (r1 <= c.a.max_rows))) return;  // req_ok
+  if (k >= r1 - r0 - 1) return;
+  if (d.id_d >= 0 && d.n == k) return;  // done by the draw slot
+  const int id_t = r0 + k;
   const int id_d = c.a.max_rows + b * G1 + k;
   SegData<T, kWideThreads> xt, xd;
   xt.load(row_ptr<T>(c, id_t), c.a.V, seg);
