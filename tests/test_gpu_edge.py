@@ -54,11 +54,11 @@ def _schedule_case(B, gamma, conf, theta_per_token, static=False):
 
 
 @pytest.mark.parametrize("B,gamma", [(1, 2), (3, 5), (64, 17), (128, 16), (200, 8), (256, 16),
-                                     (64, 64)])
+                                     (64, 64), (2048, 2), (4096, 2), (1100, 3)])
 @pytest.mark.parametrize("kind", ["beta", "ties"])
 def test_schedule_sizes(B, gamma, kind):
-    """Candidate counts 1 .. 4032 (every ordering path and keys-a-thread layout), with and without
-    ties."""
+    """Candidate counts 1 .. 4096 (every ordering path and keys-a-thread layout; runs of one
+    draft on the ranked path), with and without ties."""
     print(f"[schedule-size] B={B} gamma={gamma} {kind}", flush=True)
     rng = np.random.default_rng(B * 100 + gamma)
     G = gamma - 1
