@@ -205,11 +205,12 @@ rva_status rva_schedule_and_pack(int B, int gamma, int mode, const void* hidden,
  *
  * Arguments
  *   B               1 <= B <= 65535.
- *   max_window      upper bound of every window (gamma); max_window * (Hq/Hkv) <= 64
- *                   (otherwise RVA_ERR_UNSUPPORTED).
+ *   max_window      upper bound of every window (gamma); max_window * (Hq/Hkv) <= 4096
+ *                   (otherwise RVA_ERR_UNSUPPORTED).  Above 64 (query columns per kv
+ *                   head) the call takes the generic path.
  *   max_rows        rows of q / k_new / v_new / out (>= the largest tier).
  *   Hq, Hkv, D      Hq % Hkv == 0; D in {64, 128}.
- *   page_size       >= 1 (the bf16 MFMA path needs a multiple of 32; others take the
+ *   page_size       >= 1 (the bf16 MFMA path needs a power of two >= 32; others take the
  *                   generic path).
  *   kv_dtype        RVA_BF16 or RVA_F32: dtype of q, k_new, v_new, caches and out.
  *   q [max_rows, Hq, D], k_new / v_new [max_rows, Hkv, D], out [max_rows, Hq, D].

@@ -41,8 +41,8 @@
 //   * The V cache is transposed in column blocks of 32 slots ([D][32] per block), so each
 //     tile's V^T operand is one contiguous 8 KB block, like its K rows: every load
 //     instruction fetches full cache lines.
-// Any other dtype / shape uses attn_generic_kernel (one wave per query column, one key per
-// lane, online softmax), which is also the float32 path.
+// Any other dtype / shape uses attn_generic_kernel (one workgroup per query column, one
+// key per thread, online softmax), which is also the float32 path.
 #include "rva_common.h"
 
 #include <mutex>
@@ -845,103 +845,182 @@ __global__ __launch_bounds__(kThreads) void attn_merge_kernel(AttnArgs a, int P,
   }
 }
 
-// Generic path: any element type and page size.  One workgroup per (request, kv head);
-// each wave takes query columns in turn; each lane owns one key at a time and keeps a
-// running max, sum and D-wide accumulator; the lanes are merged at the end.
+// Generic path: any element type and page size.  One workgroup per (request b, query
+// column n = i*G + head offset, kv head g), so a request's columns run side by side
+// instead of in turn.  The 256 threads split the keys 0 .. L+i of the column: each owns
+// one key per pass (its K row in 16-byte loads, its V column from the transposed tile)
+// and keeps a running max, sum and D-wide accumulator; the threads are merged at the end
+// through DPP row sums and LDS.  Workgroup ids are dealt so that each XCD gets a
+// contiguous run of (request, column) pairs: the columns of one request then read its
+// K/V through one L2.  The workgroup of column i*G also appends window row i to the
+// caches (no workgroup reads cache positions L and above).
+// One key's D elements in registers, as loaded (bf16 stays packed two to a register and
+// is widened where it is used).
 template <typename T, int D>
-__global__ __launch_bounds__(256) void attn_generic_kernel(AttnArgs a) {
-  __shared__ float sm_q[4][D];
-  const int g = blockIdx.x, b = blockIdx.y;
+struct RowRegs;
+template <int D>
+struct RowRegs<float, D> {
+  float x[D];
+  __device__ __forceinline__ void load_row(const float* r) {
+#pragma unroll
+    for (int j = 0; j < D / 4; ++j) {
+      const float4 v = reinterpret_cast<const float4*>(r)[j];
+      x[4 * j] = v.x, x[4 * j + 1] = v.y, x[4 * j + 2] = v.z, x[4 * j + 3] = v.w;
+    }
+  }
+  __device__ __forceinline__ void load_strided(const float* r, int stride) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) x[d] = r[size_t(d) * stride];
+  }
+  __device__ __forceinline__ float at(int d) const { return x[d]; }
+};
+template <int D>
+struct RowRegs<uint16_t, D> {
+  uint32_t x[D / 2];
+  __device__ __forceinline__ void load_row(const uint16_t* r) {
+#pragma unroll
+    for (int j = 0; j < D / 8; ++j) {
+      const uint4 v = reinterpret_cast<const uint4*>(r)[j];
+      x[4 * j] = v.x, x[4 * j + 1] = v.y, x[4 * j + 2] = v.z, x[4 * j + 3] = v.w;
+    }
+  }
+  __device__ __forceinline__ void load_strided(const uint16_t* r, int stride) {
+#pragma unroll
+    for (int j = 0; j < D / 2; ++j)
+      x[j] = uint32_t(r[size_t(2 * j) * stride]) | (uint32_t(r[size_t(2 * j + 1) * stride]) << 16);
+  }
+  __device__ __forceinline__ float at(int d) const {
+    return __uint_as_float(d % 2 ? x[d / 2] & 0xffff0000u : x[d / 2] << 16);
+  }
+};
+
+// Sum over each row of 16 lanes, in the row's last lane (every lane must be active).
+__device__ __forceinline__ float row_sum(float x) {
+  x += dpp_move<kDppRowShr + 1, 0xf>(0.f, x);
+  x += dpp_move<kDppRowShr + 2, 0xf>(0.f, x);
+  x += dpp_move<kDppRowShr + 4, 0xf>(0.f, x);
+  x += dpp_move<kDppRowShr + 8, 0xf>(0.f, x);
+  return x;
+}
+
+// Zero-fills output rows [M, tier): workgroup x of nx takes rows M + x, M + x + nx, ...
+template <typename T, int D>
+__device__ __forceinline__ void pad_rows(const AttnArgs& a, int x, int nx) {
+  const int M = max(a.total_tier[0], 0);
+  const int tier = min(a.total_tier[1], a.max_rows);
+  const size_t row_elems = size_t(a.Hq) * D;
+  for (int r = M + x; r < tier; r += nx) {
+    T* o = static_cast<T*>(a.out) + size_t(r) * row_elems;
+    for (size_t k = threadIdx.x; k < row_elems; k += 256) Elem<T>::store(o, k, 0.f);
+  }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void attn_generic_kernel(AttnArgs a, int NQ, int per_xcd) {
+  constexpr int kRows = kWaves * 4;  // rows of 16 lanes in the workgroup
+  __shared__ float sq[D];
+  __shared__ float red[kRows][D + 1];
+  __shared__ float red_l[kRows];
+  __shared__ float red_m[kWaves];
+  if (int(blockIdx.y) == a.Hkv) {  // the extra row of workgroups zero-fills the pad rows
+    pad_rows<T, D>(a, blockIdx.x, gridDim.x);
+    return;
+  }
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-  const ReqInfo ri = req_info(a, b, g == 0 && tid == 0);
+  const int lid = int(blockIdx.x % 8) * per_xcd + int(blockIdx.x / 8);
+  const int b = lid / NQ, n = lid % NQ, g = blockIdx.y;
+  if (b >= a.B) return;
+  const ReqInfo ri = req_info(a, b, n == 0 && g == 0 && tid == 0);
   if (!ri.ok) return;
-  const int L = ri.L, r0 = ri.r0, w = ri.w;
-  const int G = a.Hq / a.Hkv, nq = w * G, Hkv = a.Hkv, P = a.page_size;
+  const int G = a.Hq / a.Hkv, Hkv = a.Hkv, P = a.page_size;
+  if (n >= ri.w * G) return;
+  const int L = ri.L, r0 = ri.r0, i = n / G, h = g * G + n % G;
   const T* kc = static_cast<const T*>(a.k_cache);
   const T* vc = static_cast<const T*>(a.v_cache);
   const T* kn = static_cast<const T*>(a.k_new);
   const T* vn = static_cast<const T*>(a.v_new);
+  const T* qrow = static_cast<const T*>(a.q) + (size_t(r0 + i) * a.Hq + h) * D;
+  for (int d = tid; d < D; d += 256) sq[d] = Elem<T>::load(qrow, d) * a.scale;
+  __syncthreads();
+
   bool bad_page = false;
-  for (int n0 = 0; n0 < nq; n0 += 4) {  // same trip count in every wave
-    const int n = n0 + wave;
-    const bool active = n < nq;
-    const int i = active ? n / G : 0, h = g * G + (active ? n % G : 0);
-    const T* qrow = static_cast<const T*>(a.q) + (size_t(r0 + i) * a.Hq + h) * D;
-    if (active)
-      for (int d = lane; d < D; d += kWave) sm_q[wave][d] = Elem<T>::load(qrow, d) * a.scale;
-    __syncthreads();
-    if (active) {
-      float m = -INFINITY, l = 0.f;
-      float acc[D];
+  float m = -INFINITY, l = 0.f, acc[D];
 #pragma unroll
-      for (int d = 0; d < D; ++d) acc[d] = 0.f;
-      for (int p = lane; p <= L + i; p += kWave) {
-        const T* krow;
-        const T* vbase;
-        size_t vstride;
-        if (p < L) {
-          const int pg = page_of(a, b, p, bad_page);
-          if (pg < 0) continue;
-          krow = kc + ((size_t(pg) * Hkv + g) * P + p % P) * D;
-          vbase = vc + v_index(pg, g, Hkv, P, D, p % P, 0);
-          vstride = vblk(P);
-        } else {
-          krow = kn + (size_t(r0 + p - L) * Hkv + g) * D;
-          vbase = vn + (size_t(r0 + p - L) * Hkv + g) * D;
-          vstride = 1;
-        }
-        float s = 0.f;
-#pragma unroll
-        for (int d = 0; d < D; ++d) s += sm_q[wave][d] * Elem<T>::load(krow, d);
-        const float mn = fmaxf(m, s);
-        const float c = __expf(m - mn);
-        const float e = __expf(s - mn);
-        l = l * c + e;
-#pragma unroll
-        for (int d = 0; d < D; ++d) acc[d] = acc[d] * c + e * Elem<T>::load(vbase, size_t(d) * vstride);
-        m = mn;
+  for (int d = 0; d < D; ++d) acc[d] = 0.f;
+  const int nk = L + i + 1;
+  const int* bt = a.block_table + size_t(b) * a.max_pages;
+  int pg_cur = tid < L ? bt[tid / P] : 0;
+  for (int p = tid; p < nk; p += 256) {
+    const T* krow;
+    const T* vbase;
+    int vstride;
+    const int pg = pg_cur;
+    pg_cur = p + 256 < L ? bt[(p + 256) / P] : 0;  // the next pass's page, in flight now
+    if (p < L) {
+      if (pg < 0 || pg >= a.num_pages) {
+        bad_page = true;
+        continue;
       }
-      const float M = wave_max(m);
-      const float f = (m == -INFINITY) ? 0.f : __expf(m - M);
-      const float Ls = wave_sum(l * f);
-      T* orow = static_cast<T*>(a.out) + (size_t(r0 + i) * a.Hq + h) * D;
-#pragma unroll
-      for (int d = 0; d < D; ++d) {
-        const float v = wave_sum(acc[d] * f);
-        if (lane == 0) Elem<T>::store(orow, d, v / Ls);
-      }
+      krow = kc + ((size_t(pg) * Hkv + g) * P + p % P) * D;
+      vbase = vc + v_index(pg, g, Hkv, P, D, p % P, 0);
+      vstride = vblk(P);
+    } else {
+      krow = kn + (size_t(r0 + p - L) * Hkv + g) * D;
+      vbase = vn + (size_t(r0 + p - L) * Hkv + g) * D;
+      vstride = 1;
     }
-    __syncthreads();
+    RowRegs<T, D> kr, vv;
+    kr.load_row(krow);
+    vv.load_strided(vbase, vstride);
+    float s4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int d = 0; d < D; ++d) s4[d % 4] = fmaf(sq[d], kr.at(d), s4[d % 4]);
+    const float s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+    const float mn = fmaxf(m, s);
+    const float c = __expf(m - mn);
+    const float e = __expf(s - mn);
+    l = fmaf(l, c, e);
+#pragma unroll
+    for (int d = 0; d < D; ++d) acc[d] = fmaf(acc[d], c, e * vv.at(d));
+    m = mn;
   }
   if (bad_page) flag(a.status, RVA_DEV_BAD_PAGE);
+
+  // merge: workgroup max, then every thread's share rescaled to it and summed
+  const float mw = wave_max(m);
+  if (lane == 0) red_m[wave] = mw;
   __syncthreads();
-  // append the window K/V (all of this head's work is done; no wave reads the cache again)
-  T* kcw = static_cast<T*>(a.k_cache);
-  T* vcw = static_cast<T*>(a.v_cache);
-  for (int idx = tid; idx < w * D; idx += 256) {
-    const int j = idx / D, d = idx % D;
-    const int p = L + j;
+  const float M = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
+  const float f = (m == -INFINITY) ? 0.f : __expf(m - M);
+  const bool row_last = lane % 16 == 15;
+  const int row = wave * 4 + lane / 16;
+  const float lr = row_sum(l * f);
+  if (row_last) red_l[row] = lr;
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    const float v = row_sum(acc[d] * f);
+    if (row_last) red[row][d] = v;
+  }
+  __syncthreads();
+  if (tid < D) {
+    float o = 0.f, Ls = 0.f;
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) o += red[r][tid], Ls += red_l[r];
+    Elem<T>::store(static_cast<T*>(a.out), (size_t(r0 + i) * a.Hq + h) * D + tid, o / Ls);
+  }
+
+  // append window row i (position L + i) to both caches
+  if (n % G == 0 && tid < D) {
+    const int p = L + i;
     bool badp = false;
     const int pg = page_of(a, b, p, badp);
     if (pg < 0) {
       flag(a.status, RVA_DEV_BAD_PAGE);
-      continue;
+      return;
     }
-    const size_t src = (size_t(r0 + j) * Hkv + g) * D + d;
-    kcw[((size_t(pg) * Hkv + g) * P + p % P) * D + d] = kn[src];
-    vcw[v_index(pg, g, Hkv, P, D, p % P, d)] = vn[src];
-  }
-}
-
-// Zero-fills output rows [M, tier) for the generic path.
-template <typename T, int D>
-__global__ __launch_bounds__(256) void attn_pad_kernel(AttnArgs a) {
-  const int M = max(a.total_tier[0], 0);
-  const int tier = min(a.total_tier[1], a.max_rows);
-  const size_t row_elems = size_t(a.Hq) * D;
-  for (int r = M + int(blockIdx.x); r < tier; r += gridDim.x) {
-    T* o = static_cast<T*>(a.out) + size_t(r) * row_elems;
-    for (size_t k = threadIdx.x; k < row_elems; k += 256) Elem<T>::store(o, k, 0.f);
+    const size_t src = (size_t(r0 + i) * Hkv + g) * D + tid;
+    static_cast<T*>(a.k_cache)[((size_t(pg) * Hkv + g) * P + p % P) * D + tid] = kn[src];
+    static_cast<T*>(a.v_cache)[v_index(pg, g, Hkv, P, D, p % P, tid)] = vn[src];
   }
 }
 
@@ -991,10 +1070,12 @@ hipError_t launch_sk(const AttnArgs& a, hipStream_t stream) {
 
 template <typename T, int D>
 hipError_t launch_generic(const AttnArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_generic_kernel<T, D>), dim3(a.Hkv, a.B), dim3(256), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_pad_kernel<T, D>), dim3(32), dim3(256), 0, stream, a);
+  // (request, column) pairs padded to a multiple of the 8 XCDs, dealt XCD-major; one more
+  // row of workgroups for the pad rows
+  const int NQ = a.max_window * (a.Hq / a.Hkv);
+  const int per_xcd = int((int64_t(a.B) * NQ + 7) / 8);
+  hipLaunchKernelGGL((attn_generic_kernel<T, D>), dim3(8 * per_xcd, a.Hkv + 1), dim3(256), 0, stream, a,
+                     NQ, per_xcd);
   return hipGetLastError();
 }
 

@@ -186,8 +186,9 @@ rva_status attention_call(const char* name, int B, int max_window, int max_rows,
   REQUIRE(Hkv <= 65535, "Hkv must be <= 65535");
   if (D != 64 && D != 128) return fail(RVA_ERR_UNSUPPORTED, "D must be 64 or 128 (got %d)", D);
   REQUIRE(kv_dtype == RVA_BF16 || kv_dtype == RVA_F32, "unknown kv_dtype %d", kv_dtype);
-  if (max_window * (Hq / Hkv) > 64)
-    return fail(RVA_ERR_UNSUPPORTED, "max_window * Hq/Hkv must be <= 64 (got %d)", max_window * (Hq / Hkv));
+  if ((long long)max_window * (Hq / Hkv) > 4096)
+    return fail(RVA_ERR_UNSUPPORTED, "max_window * Hq/Hkv must be <= 4096 (got %lld)",
+                (long long)max_window * (Hq / Hkv));
   REQUIRE(page_size >= 1 && num_pages >= 1 && max_pages >= 1, "page_size, num_pages, max_pages must be >= 1");
   REQUIRE((long long)page_size * max_pages <= (1LL << 30), "page_size * max_pages too large");
   REQUIRE(q && k_new && v_new && k_cache && v_cache && block_table && context_lens && cu_seqlens &&

@@ -124,7 +124,7 @@ def test_attention_validation():
     assert need > 0
     assert _attn(Hq=30) == INVALID                        # Hq % Hkv != 0
     assert _attn(D=96) == UNSUPPORTED
-    assert _attn(max_window=17) == UNSUPPORTED            # 17 * 4 > 64 rows per kv head
+    assert _attn(max_window=1025) == UNSUPPORTED          # 1025 * 4 > 4096 columns per kv head
     assert _attn(dtype=5) == INVALID
     assert _attn(q=None) == INVALID
     assert _attn(q=ctypes.c_void_p(0x100002)) == INVALID  # misaligned
@@ -146,7 +146,7 @@ def test_attention_noalloc_validation():
     scratch, with the same codes as the workspace variant (no GPU needed for these)."""
     assert _attn_noalloc(Hq=30) == INVALID
     assert _attn_noalloc(D=96) == UNSUPPORTED
-    assert _attn_noalloc(max_window=17) == UNSUPPORTED
+    assert _attn_noalloc(max_window=1025) == UNSUPPORTED
     assert _attn_noalloc(dtype=5) == INVALID
     assert _attn_noalloc(q=None) == INVALID
     assert _attn_noalloc(q=ctypes.c_void_p(0x100002)) == INVALID
