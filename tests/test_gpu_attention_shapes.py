@@ -6,7 +6,7 @@ Each case builds a small seeded batch and compares the HIP path with the oracle
 * head dimension 64 on the fast path (bf16), GQA groups of 1, 4 and 8, page sizes 32, 128
   and 256;
 * the generic path: float32 at pages of 16, 24 and 32 (contexts of several 256-key passes),
-  bf16 at a page of 48 slots and at window x group above 64 columns;
+  bf16 at a page of 48 slots, at window x group above 64 columns and at 1030 requests;
 * column blocks NB = 1, 2 and 4 (window rows x group of 16, 32 and 64 columns);
 * contexts of 0, 1, one short of / exactly / one past a 32-key tile and of a page;
 * batches whose weighted work is below the grid size, and one long segment spread over
@@ -48,6 +48,10 @@ CASES = [
     # generic path in bf16: a page of 48 slots, and window x group = 80 columns (> 64)
     ("d64-bf16-p48-generic", "bf16", 64, 8, 2, 48, [47, 48, 200, 1000], [3, 1, 4, 2]),
     ("d128-bf16-wide-generic", "bf16", 128, 32, 2, 64, [100, 2000, 0], [5, 3, 4]),
+    # generic path in bf16: more requests than the MFMA path's table holds (1030 > 1024)
+    ("d128-bf16-b1030-generic", "bf16", 128, 16, 4, 64,
+     [int(x) for x in np.random.default_rng(1030).integers(0, 300, 1030)],
+     [int(x) for x in np.random.default_rng(1031).integers(1, 5, 1030)]),
     # one segment over every workgroup (the merge's loop over more than four shares)
     ("d128-g4-p64-one-long", "bf16", 128, 4, 1, 64, [20000], [3]),
     ("d64-g16-p64-nb4", "bf16", 64, 32, 2, 64, [700, 33, 2000], [4, 2, 3]),
