@@ -420,12 +420,13 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, SkShared<D, NBMAX
     }
     return pg;
   };
-  // register ring of kStages buffers: with two, tile k+1 is in flight while tile k is
-  // computed; NB = 4 reloads one buffer (its accumulators take the registers).  A three-buffer
-  // ring (kStages = 3, two tiles in flight) spills at D = 128.  kC / vC hold the tail tile.
+  // Register double buffer: tile k+1 is in flight while tile k is computed (kStages = 2);
+  // NB = 4 reloads one buffer (kStages = 1: its accumulators take the registers).  A third
+  // buffer spills at D = 128, and a two-stage LDS ring filled by LDS DMA (two tiles in flight
+  // without the registers) measured no faster on HBM data.  kC / vC hold the tail tile.
   // Loads are issued unconditionally (past the end they repeat the last tile), so every
   // path has the same number of loads outstanding and each wait is exact.
-  constexpr int kStages = NB >= 4 ? 1 : 2;  // NB = 4's accumulators leave room for one buffer
+  constexpr int kStages = NB >= 4 ? 1 : 2;
   short8 kA[2][DS], vA[DB], kB[2][DS], vB[DB], kC[2][DS], vC[DB];
   int pg_next = 0;
   auto issue = [&](int k, short8 (&kb)[2][DS], short8 (&vb)[DB]) {
@@ -437,10 +438,10 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, SkShared<D, NBMAX
   };
   auto key_k = [&](int k) { return (t0 + wave + kWaves * k) * kTile; };
   // A tile that reaches past the cached context (at most one per wave) is loaded first, into
-  // ring buffer C, so its loads overlap the first two cached tiles' loads; it is computed
-  // before the ring starts.  Both branches leave the same loads in flight.
+  // buffer C, so its loads overlap the first cached tile's loads; it is computed before the
+  // loop starts.  Both branches leave the same loads in flight.
   const int jt = nfast + ((wave - nfast) % kWaves + kWaves) % kWaves;
-  // NB = 4 keeps too many accumulators for a third buffer: its tail goes after the ring
+  // NB = 4 keeps too many accumulators for a third buffer: its tail goes after the loop
   constexpr bool kTailFirst = NB <= 2;
   const bool has_tail = kTailFirst && jt < n;
   auto tail_compute = [&]() {
@@ -456,24 +457,11 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, SkShared<D, NBMAX
     if (has_tail) {
       load_tail<D>(a, b, g, L, r0, Lw, (t0 + jt) * kTile, lc, lq, kC, vC, bad);
       issue(0, kA, vA);
-      if (kStages == 3) issue(1, kB, vB);
       tail_compute();
     } else {
       issue(0, kA, vA);
-      if (kStages == 3) issue(1, kB, vB);
     }
-    if constexpr (kStages == 3) {
-      for (int k = 0; k < nk; k += 3) {
-        issue(k + 2, kC, vC);
-        tile_compute<D, NB, false>(kA, vA, qop, oacc, m, l, sl2, key_k(k), limit, lq);
-        if (k + 1 >= nk) break;
-        issue(k + 3, kA, vA);
-        tile_compute<D, NB, false>(kB, vB, qop, oacc, m, l, sl2, key_k(k + 1), limit, lq);
-        if (k + 2 >= nk) break;
-        issue(k + 4, kB, vB);
-        tile_compute<D, NB, false>(kC, vC, qop, oacc, m, l, sl2, key_k(k + 2), limit, lq);
-      }
-    } else if constexpr (kStages == 2) {
+    if constexpr (kStages == 2) {
       for (int k = 0; k < nk; k += 2) {
         issue(k + 1, kB, vB);
         tile_compute<D, NB, false>(kA, vA, qop, oacc, m, l, sl2, key_k(k), limit, lq);
