@@ -73,11 +73,17 @@ def _rel_err(o, r):
     return float(np.max(np.max(np.abs(o - r), axis=-1) / np.max(np.abs(r), axis=-1)))
 
 
-def test_attention_bad_page_entry():
-    """A block-table entry past the pool: RVA_DEV_BAD_PAGE; that request reads page 0 in
-    its place, every other request is exact, and the window appends (in valid pages) land."""
-    print("[status] attention bad page", flush=True)
-    x = _attention_batch(51, [300, 700, 90, 500], [3, 4, 2, 4])
+# page 64: the MFMA path; page 48 (not a power of two): the generic path
+PATHS = pytest.mark.parametrize("P", [64, 48], ids=["mfma", "generic"])
+
+
+@PATHS
+def test_attention_bad_page_entry(P):
+    """A block-table entry past the pool: RVA_DEV_BAD_PAGE; that request's keys in the page
+    are replaced (MFMA path: page 0) or left out (generic path), every other request is
+    exact, and the window appends (in valid pages) land."""
+    print(f"[status] attention bad page, page {P}", flush=True)
+    x = _attention_batch(51, [300, 700, 90, 500], [3, 4, 2, 4], P=P)
     bt = x["bt"].copy()
     bt[1, 0] = x["num_pages"] + 5  # request 1, positions 0..63
     st, out, kc = _run_attention(x, bt, x["Ls"])
@@ -89,11 +95,12 @@ def test_attention_bad_page_entry():
     assert np.array_equal(kc, kc_ref)
 
 
-def test_attention_context_past_page_table():
+@PATHS
+def test_attention_context_past_page_table(P):
     """A context that does not fit its page-table row: RVA_DEV_BAD_CONTEXT; the request is
     skipped (no attention, no append), the others are exact."""
-    print("[status] attention bad context", flush=True)
-    x = _attention_batch(52, [300, 700, 90, 500], [3, 4, 2, 4])
+    print(f"[status] attention bad context, page {P}", flush=True)
+    x = _attention_batch(52, [300, 700, 90, 500], [3, 4, 2, 4], P=P)
     Ls = x["Ls"].copy()
     Ls[2] = x["max_pages"] * x["P"]  # L + w beyond the row
     st, out, _ = _run_attention(x, x["bt"], Ls)
