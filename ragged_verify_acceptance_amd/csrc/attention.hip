@@ -45,6 +45,7 @@
 // key per thread, online softmax), which is also the float32 path.
 #include "rva_common.h"
 
+#include <algorithm>
 #include <mutex>
 
 namespace rva {
@@ -833,9 +834,9 @@ __global__ __launch_bounds__(kThreads) void attn_merge_kernel(AttnArgs a, int P,
   }
 }
 
-// Generic path: any element type and page size.  One workgroup per (request b, query
-// column n = i*G + head offset, kv head g), so a request's columns run side by side
-// instead of in turn.  The 256 threads split the keys 0 .. L+i of the column: each owns
+// Generic path: any element type and page size.  One workgroup at a time per (request b,
+// query column n = i*G + head offset, kv head g), so a request's columns run side by side
+// instead of in turn (the grid is capped; workgroups then take several pairs).  The 256 threads split the keys 0 .. L+i of the column: each owns
 // one key per pass (its K row in 16-byte loads, its V column from the transposed tile)
 // and keeps a running max, sum and D-wide accumulator; the threads are merged at the end
 // through DPP row sums and LDS.  Workgroup ids are dealt so that each XCD gets a
@@ -903,20 +904,17 @@ __device__ __forceinline__ void pad_rows(const AttnArgs& a, int x, int nx) {
   }
 }
 
+// One (request, query column) pair lid = b * NQ + n of kv head g; every return is taken by
+// the whole workgroup except the append's bad-page exit.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void attn_generic_kernel(AttnArgs a, int NQ, int per_xcd) {
+__device__ void generic_column(const AttnArgs& a, int lid, int NQ, int g) {
   constexpr int kRows = kWaves * 4;  // rows of 16 lanes in the workgroup
   __shared__ float sq[D];
   __shared__ float red[kRows][D + 1];
   __shared__ float red_l[kRows];
   __shared__ float red_m[kWaves];
-  if (int(blockIdx.y) == a.Hkv) {  // the extra row of workgroups zero-fills the pad rows
-    pad_rows<T, D>(a, blockIdx.x, gridDim.x);
-    return;
-  }
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-  const int lid = int(blockIdx.x % 8) * per_xcd + int(blockIdx.x / 8);
-  const int b = lid / NQ, n = lid % NQ, g = blockIdx.y;
+  const int b = lid / NQ, n = lid % NQ;
   if (b >= a.B) return;
   const ReqInfo ri = req_info(a, b, n == 0 && g == 0 && tid == 0);
   if (!ri.ok) return;
@@ -1012,6 +1010,22 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnArgs a, int NQ, i
   }
 }
 
+// Grid (nx, Hkv + 1): nx a multiple of 8; workgroup x takes the (request, column) slots
+// x, x + nx, ... of 8 * per_xcd, each mapped XCD-major (slot s -> pair (s % 8) * per_xcd
+// + s / 8), so each XCD gets contiguous runs of pairs.  Row Hkv zero-fills the pad rows.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void attn_generic_kernel(AttnArgs a, int NQ, int per_xcd) {
+  if (int(blockIdx.y) == a.Hkv) {
+    pad_rows<T, D>(a, blockIdx.x, gridDim.x);
+    return;
+  }
+  const int slots = 8 * per_xcd;
+  for (int x = blockIdx.x; x < slots; x += gridDim.x) {
+    generic_column<T, D>(a, (x % 8) * per_xcd + x / 8, NQ, blockIdx.y);
+    __syncthreads();  // the next pair rewrites the LDS
+  }
+}
+
 int nbmax_for(int max_window, int G) {
   const int r = max_window * G;
   return r <= 16 ? 1 : r <= 32 ? 2 : 4;
@@ -1062,8 +1076,8 @@ hipError_t launch_generic(const AttnArgs& a, hipStream_t stream) {
   // row of workgroups for the pad rows
   const int NQ = a.max_window * (a.Hq / a.Hkv);
   const int per_xcd = int((int64_t(a.B) * NQ + 7) / 8);
-  hipLaunchKernelGGL((attn_generic_kernel<T, D>), dim3(8 * per_xcd, a.Hkv + 1), dim3(256), 0, stream, a,
-                     NQ, per_xcd);
+  const int nx = 8 * std::min(per_xcd, 2048);  // at most 16384 workgroups per row; they loop
+  hipLaunchKernelGGL((attn_generic_kernel<T, D>), dim3(nx, a.Hkv + 1), dim3(256), 0, stream, a, NQ, per_xcd);
   return hipGetLastError();
 }
 

@@ -48,7 +48,8 @@ CASES = [
     # generic path in bf16: a page of 48 slots, and window x group = 80 columns (> 64)
     ("d64-bf16-p48-generic", "bf16", 64, 8, 2, 48, [47, 48, 200, 1000], [3, 1, 4, 2]),
     ("d128-bf16-wide-generic", "bf16", 128, 32, 2, 64, [100, 2000, 0], [5, 3, 4]),
-    # generic path in bf16: more requests than the MFMA path's table holds (1030 > 1024)
+    # generic path in bf16: more requests than the MFMA path's table holds (1030 > 1024),
+    # and more (request, column) pairs (16480) than the capped grid has workgroups per row
     ("d128-bf16-b1030-generic", "bf16", 128, 16, 4, 64,
      [int(x) for x in np.random.default_rng(1030).integers(0, 300, 1030)],
      [int(x) for x in np.random.default_rng(1031).integers(1, 5, 1030)]),
