@@ -34,7 +34,7 @@ constexpr int kSchedThreads = 1024;
 constexpr int kRankThreads = 1024;
 constexpr int kMaxCand = 4096;
 
-template <typename T>
+template <typename T, bool VEC>
 __global__ __launch_bounds__(256) void conf_head_kernel(const T* __restrict__ hidden, int rows,
                                                         int G, int H,
                                                         const float* __restrict__ w, float b0,
@@ -46,7 +46,53 @@ __global__ __launch_bounds__(256) void conf_head_kernel(const T* __restrict__ hi
   if (row >= rows) return;
   const T* h = hidden + size_t(row) * H;
   double acc = 0.0;
-  for (int i = lane; i < H; i += kWave) acc += double(Elem<T>::load(h, i)) * double(w[i]);
+  if constexpr (VEC) {
+    // 16-byte pieces of the row and of w (H a multiple of the piece, both 16-byte aligned),
+    // kPieces per lane at a time from clamped indices, so that they are all in flight
+    // together (one round trip up to kPieces * 64 pieces); pieces past the row add nothing
+    constexpr int E = 16 / sizeof(T);
+    constexpr int kPieces = 8;
+    const int n = H / E;
+    for (int j0 = 0; j0 < n; j0 += kPieces * kWave) {
+      uint4 hv[kPieces];
+      float4 wq[kPieces][E / 4];
+#pragma unroll
+      for (int k = 0; k < kPieces; ++k) {
+        const int j = min(j0 + k * kWave + lane, n - 1);
+        hv[k] = reinterpret_cast<const uint4*>(h)[j];
+#pragma unroll
+        for (int q = 0; q < E / 4; ++q) wq[k][q] = reinterpret_cast<const float4*>(w + size_t(j) * E)[q];
+      }
+      asm volatile("" ::: "memory");  // every piece is requested before the first is used
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int k = 0; k < kPieces; ++k) {
+        float x[E];
+        if constexpr (sizeof(T) == 2) {
+          const uint32_t u[4] = {hv[k].x, hv[k].y, hv[k].z, hv[k].w};
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            x[2 * t] = __uint_as_float(u[t] << 16);
+            x[2 * t + 1] = __uint_as_float(u[t] & 0xffff0000u);
+          }
+        } else {
+          x[0] = __uint_as_float(hv[k].x), x[1] = __uint_as_float(hv[k].y);
+          x[2] = __uint_as_float(hv[k].z), x[3] = __uint_as_float(hv[k].w);
+        }
+        double part = 0.0;
+#pragma unroll
+        for (int q = 0; q < E / 4; ++q) {
+          part += double(x[4 * q]) * double(wq[k][q].x);
+          part += double(x[4 * q + 1]) * double(wq[k][q].y);
+          part += double(x[4 * q + 2]) * double(wq[k][q].z);
+          part += double(x[4 * q + 3]) * double(wq[k][q].w);
+        }
+        if (j0 + k * kWave + lane < n) acc += part;
+      }
+    }
+  } else {
+    for (int i = lane; i < H; i += kWave) acc += double(Elem<T>::load(h, i)) * double(w[i]);
+  }
   acc = wave_sum_f64(acc);
   if (lane == 0) {
     double z = acc + double(b0);
@@ -551,12 +597,24 @@ hipError_t confidences(int B, int G, const void* hidden, int hidden_dtype, int H
   *echo = conf_in ? conf_out : nullptr;
   if (conf_in) return hipSuccess;
   const dim3 grid((rows + 3) / 4), block(256);
-  if (hidden_dtype == RVA_BF16)
-    hipLaunchKernelGGL(conf_head_kernel<uint16_t>, grid, block, 0, stream, static_cast<const uint16_t*>(hidden),
-                       rows, G, H, head_w, head_b, sts_T, conf_out, status);
-  else
-    hipLaunchKernelGGL(conf_head_kernel<float>, grid, block, 0, stream, static_cast<const float*>(hidden), rows,
-                       G, H, head_w, head_b, sts_T, conf_out, status);
+  const bool aligned16 = (reinterpret_cast<uintptr_t>(hidden) | reinterpret_cast<uintptr_t>(head_w)) % 16 == 0;
+  if (hidden_dtype == RVA_BF16) {
+    const uint16_t* hp = static_cast<const uint16_t*>(hidden);
+    if (aligned16 && H % 8 == 0)
+      hipLaunchKernelGGL((conf_head_kernel<uint16_t, true>), grid, block, 0, stream, hp, rows, G, H, head_w, head_b,
+                         sts_T, conf_out, status);
+    else
+      hipLaunchKernelGGL((conf_head_kernel<uint16_t, false>), grid, block, 0, stream, hp, rows, G, H, head_w, head_b,
+                         sts_T, conf_out, status);
+  } else {
+    const float* hp = static_cast<const float*>(hidden);
+    if (aligned16 && H % 4 == 0)
+      hipLaunchKernelGGL((conf_head_kernel<float, true>), grid, block, 0, stream, hp, rows, G, H, head_w, head_b,
+                         sts_T, conf_out, status);
+    else
+      hipLaunchKernelGGL((conf_head_kernel<float, false>), grid, block, 0, stream, hp, rows, G, H, head_w, head_b,
+                         sts_T, conf_out, status);
+  }
   *conf = conf_out;
   return hipGetLastError();
 }
