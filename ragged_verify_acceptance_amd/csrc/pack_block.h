@@ -11,7 +11,9 @@
 // (one wave's scan of at most a few thousand ints, cheaper than a second launch), picks the
 // tier, and then handles ROWS destination rows: a binary search in LDS finds the owning
 // request, the row is copied with 16-byte vector accesses when alignment allows, rows
-// [M, tier) are zero-filled.  The publishing workgroup writes cu_seqlens and {M, tier}.
+// [M, tier) are zero-filled.  Long rows are cut into `nparts` column parts, one workgroup
+// each (part 0 also writes the row metadata).  The publishing workgroup writes cu_seqlens
+// and {M, tier}.
 #pragma once
 
 #include "rva_common.h"
@@ -36,7 +38,8 @@ __device__ __forceinline__ void pack_block(PackShared<NT, BCAP>& sh, int B, int 
                                            size_t row_bytes, uint8_t* __restrict__ dst, int max_rows,
                                            int32_t* __restrict__ cu_out, int32_t* __restrict__ row_req,
                                            int32_t* __restrict__ row_pos, int32_t* __restrict__ total_tier,
-                                           int32_t* status, int block, bool publish) {
+                                           int32_t* status, int block, bool publish, int part = 0,
+                                           int nparts = 1) {
   int* cu = sh.cu;
   const int tid = threadIdx.x;
 
@@ -107,7 +110,7 @@ __device__ __forceinline__ void pack_block(PackShared<NT, BCAP>& sh, int B, int 
     return lo;
   };
   // row metadata: one thread per row of this block, so the context_lens loads overlap
-  if (tid < ROWS) {
+  if (part == 0 && tid < ROWS) {
     const int r = block * ROWS + tid;
     if (r < max_rows) {
       const int b = r < M ? owner(r) : -1;
@@ -132,11 +135,14 @@ __device__ __forceinline__ void pack_block(PackShared<NT, BCAP>& sh, int B, int 
     }
   }
   uint8_t* drow0 = dst + size_t(block) * ROWS * row_bytes;
+  // this workgroup's part of every row: bytes [c_lo, c_hi), a multiple of 16 bytes apart
+  const size_t chunk = ((row_bytes + nparts - 1) / nparts + 15) / 16 * 16;
+  const size_t c_lo = min(row_bytes, size_t(part) * chunk), c_hi = min(row_bytes, c_lo + chunk);
   if (vec16) {
     // a pass loads 2 vectors of every row before storing any, so the block's copy costs
-    // about one round trip per pass (one pass for rows of up to 2 NT x 16 bytes)
-    const size_t n = row_bytes / 16;
-    for (size_t k0 = 0; k0 < n; k0 += 2 * NT) {
+    // about one round trip per pass (one pass for parts of up to 2 NT x 16 bytes)
+    const size_t n = c_hi / 16;
+    for (size_t k0 = c_lo / 16; k0 < n; k0 += 2 * NT) {
       uint4 v[ROWS][2];
 #pragma unroll
       for (int rr = 0; rr < ROWS; ++rr)
@@ -158,7 +164,7 @@ __device__ __forceinline__ void pack_block(PackShared<NT, BCAP>& sh, int B, int 
     for (int rr = 0; rr < nrows; ++rr) {
       uint8_t* d = drow0 + size_t(rr) * row_bytes;
       const uint8_t* s = srow[rr];
-      for (size_t k = tid; k < row_bytes; k += NT) d[k] = s ? s[k] : uint8_t(0);
+      for (size_t k = c_lo + tid; k < c_hi; k += NT) d[k] = s ? s[k] : uint8_t(0);
     }
   }
 }

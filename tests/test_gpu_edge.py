@@ -157,11 +157,15 @@ def test_accept_vocab_beyond_one_wave_of_segments():
     _accept_case(3, 3, 1_100_000, [3, 1, 2], seed=11)
 
 
-@pytest.mark.parametrize("elems,dtype", [(3, torch.bfloat16), (2050, torch.bfloat16), (5, torch.float32)],
-                         ids=["6-byte-rows", "4100-byte-rows", "20-byte-rows"])
+@pytest.mark.parametrize("elems,dtype", [(3, torch.bfloat16), (2050, torch.bfloat16), (5, torch.float32),
+                                         (20001, torch.bfloat16), (151936, torch.bfloat16)],
+                         ids=["6-byte-rows", "4100-byte-rows", "20-byte-rows", "40002-byte-rows",
+                              "303872-byte-rows"])
 def test_pack_unaligned_rows(elems, dtype):
-    """Row sizes that are not multiples of 16 bytes take the scalar copy path; the total
-    14 rounds up to tier 16 (two zero rows); rows past the tier keep their contents."""
+    """Row sizes that are not multiples of 16 bytes take the scalar copy path, and rows above
+    16 KB are cut into column parts (40002 bytes: three parts on the scalar path; a
+    vocabulary-wide bf16 logits row: 19 parts on the vector path); the total 14 rounds up
+    to tier 16 (two zero rows); rows past the tier keep their contents."""
     print(f"[pack-edge] {elems} x {dtype}", flush=True)
     rng = np.random.default_rng(elems)
     B, gamma = 5, 4
