@@ -16,10 +16,10 @@
 // negative log-likelihood of the observed outcomes of position k over [T_lo, T_hi].  The
 // minimum is located by iterated grid refinement in u = ln T: 64 log-spaced temperatures,
 // the best one's two neighbouring cells become the next round's bracket, six rounds (final
-// spacing about 1e-8 in u).  Every round is one launch: a data-parallel pass over (sample
-// chunk, group of 8 temperatures) whose workgroups write partial sums, and a selection by
-// the last workgroup to finish that sums the partials in chunk order, so the result is
-// reproducible run to run and the bracket stays on the device (no host round trip).
+// spacing about 1e-8 in u).  Every round is two launches: a data-parallel pass over (sample
+// chunk, group of 8 temperatures) whose workgroups write partial sums, and a one-wave
+// selection that sums the partials in chunk order, so the result is reproducible run to
+// run and the bracket stays on the device (no host round trip).
 //
 // ECE: the observed (a, E) pairs are binned by a into n_bins equal bins of [0, 1]
 // (bin = min(floor(a n_bins), n_bins - 1)); per workgroup the bins live in LDS, partial bins
@@ -41,7 +41,6 @@ constexpr int kMaxEceChunks = 256;
 
 struct StsState {
   double u_lo, du, T, pad;  // bracket of the current round; the last fitted temperature
-  unsigned int done;        // workgroups of the current round that have finished
 };
 
 __device__ __forceinline__ double log_sigmoid(double x) { return fmin(x, 0.0) - log1p(exp(-fabs(x))); }
@@ -90,7 +89,6 @@ __global__ __launch_bounds__(kCalThreads) void sts_init_kernel(StsArgs a, StsLay
     st->u_lo = lo;
     st->du = (hi - lo) / (kGrid - 1);
     st->T = 1.0;
-    st->done = 0u;
   }
 }
 
@@ -99,17 +97,12 @@ __global__ __launch_bounds__(kCalThreads) void sts_init_kernel(StsArgs a, StsLay
 // observed samples).  In round 0 of a position k > 0 each thread first extends its samples'
 // log survival by position k-1 at the temperature just fitted (workgroups y = 0 store it for
 // the later rounds, in the other buffer, so no workgroup reads a value another one is
-// rewriting).  The last workgroup to finish (a device-scope counter) sums the partials in
-// chunk order with one wave, picks the best temperature (first on a tie), and narrows the
-// bracket or, after the last round, publishes T_k.
-__global__ __launch_bounds__(kCalThreads) void sts_round_kernel(StsArgs a, StsLayout l, int k, int round,
-                                                                int last) {
+// rewriting).  sts_select_kernel then picks the round's best temperature.
+__global__ __launch_bounds__(kCalThreads) void sts_round_kernel(StsArgs a, StsLayout l, int k, int round) {
   __shared__ double s_T[kGroup];
   __shared__ double red[kCalThreads / kWave];
-  __shared__ int s_last;
   char* ws = static_cast<char*>(a.ws);
-  StsState* stp = reinterpret_cast<StsState*>(ws + l.off_state);
-  const StsState st = *stp;
+  const StsState st = *reinterpret_cast<const StsState*>(ws + l.off_state);
   double* Lcur = reinterpret_cast<double*>(ws + ((k & 1) ? l.off_L1 : l.off_L0));
   const double* Lprev = reinterpret_cast<const double*>(ws + ((k & 1) ? l.off_L0 : l.off_L1));
   double* part = reinterpret_cast<double*>(ws + l.off_part);
@@ -148,19 +141,23 @@ __global__ __launch_bounds__(kCalThreads) void sts_round_kernel(StsArgs a, StsLa
   }
   const double c = block_sum_f64(cnt, red);
   if (tid == 0 && blockIdx.y == 0) my[kGrid] = c;
+}
 
-  // the last workgroup of the round selects
-  __threadfence();
-  if (tid == 0) {
-    const unsigned total = gridDim.x * gridDim.y;
-    s_last = atomicAdd(&stp->done, 1u) == total - 1;
-  }
-  __syncthreads();
-  if (!s_last || tid >= kGrid) return;
-  __threadfence();
-  const int p = tid;
+// The selection after a round (one wave, thread p = temperature p of the round): sums the
+// partials in chunk order (the loads of 16 chunks at a time are independent, so they are in
+// flight together), picks the best temperature (first on a tie), and narrows the bracket
+// or, after the last round, publishes T_k.  A launch of its own: the kernel boundary makes
+// every partial visible, where a device-scope fence in each round workgroup and a
+// last-to-finish counter cost more than the round's arithmetic.
+__global__ __launch_bounds__(kGrid) void sts_select_kernel(StsArgs a, StsLayout l, int k, int last, int chunks) {
+  const char* ws = static_cast<const char*>(a.ws);
+  StsState* stp = reinterpret_cast<StsState*>(static_cast<char*>(a.ws) + l.off_state);
+  const StsState st = *stp;
+  const double* part = reinterpret_cast<const double*>(ws + l.off_part);
+  const int p = threadIdx.x;
   double f = 0.0, n_obs = 0.0;
-  for (int ch = 0; ch < int(gridDim.x); ++ch) {
+#pragma unroll 16
+  for (int ch = 0; ch < chunks; ++ch) {
     f += part[size_t(ch) * (kGrid + 1) + p];
     n_obs += part[size_t(ch) * (kGrid + 1) + kGrid];
   }
@@ -177,7 +174,6 @@ __global__ __launch_bounds__(kCalThreads) void sts_round_kernel(StsArgs a, StsLa
   }
   if (p != 0) return;
   StsState nx = st;
-  nx.done = 0u;
   const double lo0 = log(double(a.T_lo)), hi0 = log(double(a.T_hi));
   if (n_obs == 0.0 || last) {
     const double T = n_obs == 0.0 ? 1.0 : exp(st.u_lo + bp * st.du);
@@ -312,9 +308,12 @@ hipError_t launch_sts_fit(const StsArgs& a, hipStream_t stream) {
   const StsLayout l = sts_layout(a.N);
   hipLaunchKernelGGL(sts_init_kernel, dim3(l.chunks), dim3(kCalThreads), 0, stream, a, l);
   for (int k = 0; k < a.G1; ++k)
-    for (int r = 0; r < kRounds; ++r)
+    for (int r = 0; r < kRounds; ++r) {
       hipLaunchKernelGGL(sts_round_kernel, dim3(l.chunks, kGrid / kGroup), dim3(kCalThreads), 0, stream, a,
-                         l, k, r, int(r == kRounds - 1));
+                         l, k, r);
+      hipLaunchKernelGGL(sts_select_kernel, dim3(1), dim3(kGrid), 0, stream, a, l, k, int(r == kRounds - 1),
+                         l.chunks);
+    }
   return hipGetLastError();
 }
 
