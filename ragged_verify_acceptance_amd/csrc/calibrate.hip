@@ -17,7 +17,7 @@
 // minimum is located by iterated grid refinement in u = ln T: 64 log-spaced temperatures,
 // the best one's two neighbouring cells become the next round's bracket, six rounds (final
 // spacing about 1e-8 in u).  Every round is two launches: a data-parallel pass over (sample
-// chunk, group of 8 temperatures) whose workgroups write partial sums, and a one-wave
+// chunk, pair of temperatures) whose workgroups write partial sums, and a one-wave
 // selection that sums the partials in chunk order, so the result is reproducible run to
 // run and the bracket stays on the device (no host round trip).
 //
@@ -35,7 +35,7 @@ namespace {
 constexpr int kCalThreads = 256;
 constexpr int kGrid = 64;     // temperatures per refinement round
 constexpr int kRounds = 6;
-constexpr int kGroup = 8;     // temperatures per workgroup (grid.y = kGrid / kGroup)
+constexpr int kGroup = 2;     // temperatures per workgroup (grid.y = kGrid / kGroup)
 constexpr int kMaxChunks = 512;
 constexpr int kMaxEceChunks = 256;
 
@@ -93,7 +93,7 @@ __global__ __launch_bounds__(kCalThreads) void sts_init_kernel(StsArgs a, StsLay
 }
 
 // One refinement round of position k.  Workgroup (x, y) sums the negative log-likelihood of
-// its chunk x of samples at the round's temperatures 8y .. 8y+7 (and, for y = 0, counts the
+// its chunk x of samples at the round's temperatures 2y, 2y+1 (and, for y = 0, counts the
 // observed samples).  In round 0 of a position k > 0 each thread first extends its samples'
 // log survival by position k-1 at the temperature just fitted (workgroups y = 0 store it for
 // the later rounds, in the other buffer, so no workgroup reads a value another one is
